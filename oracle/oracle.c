@@ -1,0 +1,387 @@
+/*
+ * CPU oracle for the BitNet b1.58 BitLinear W1.58A8 layer.
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library; the GPU library never
+ * links, calls or includes it, and it shares no code with the GPU library.
+ *
+ * Every function is the plain definition, written out serially.  OpenMP only
+ * splits loops whose iterations are independent (output rows, elements), so
+ * results do not depend on the thread count.  Floating point follows IEEE-754
+ * binary32 where the method computes in fp32 (built with -ffp-contract=off
+ * and without fast-math), and the absmean mean is computed exactly.
+ *
+ * Sources (the BitNet b1.58 pages):
+ *  - bako.co, "BitNet b1.58 and the 1-Bit AI Architecture Revolution",
+ *    section "The BitLinear Layer and AbsMean Quantization": gamma is the mean
+ *    absolute value of the entire weight matrix; weights are divided by
+ *    (gamma + eps), eps = 1e-5, rounded to the nearest integer and clamped to
+ *    [-1, 1]; gamma is returned with the ternary tensor.  Same section: the
+ *    product of ternary weights and activations needs only additions and
+ *    subtractions.
+ *  - deepmox.com chapter 8, section "A low-bit model is a whole-stack design":
+ *    weights take the values -1, 0, +1; activations use a per-token 8-bit path
+ *    (W1.58A8); the GPU path stores four ternary values per 8-bit unit.
+ *  - onilabs.co, "A Two-Billion Ternary Bet": activations are quantized
+ *    dynamically (per call, from the values themselves).
+ *
+ * Readings where the pages are silent (listed with reasons in the design notes):
+ *  - gamma is the exact mean of |W|, rounded once to fp32 (round to nearest,
+ *    ties to even); gamma + eps and W / (gamma + eps) are fp32 operations with
+ *    correct rounding; "round" is round-half-to-even (torch.round).
+ *  - activation scale s = 127 / max(max_k |x|, 1e-5) in fp32; q = RNE(x * s)
+ *    clamped to [-128, 127]; alpha = max_k |x| (absmax) per token.
+ *  - output y = acc * gamma * alpha / 127, evaluated in binary64 and rounded
+ *    directly to bf16 (nearest, ties to even).
+ *  - packed layout: 2-bit code c = q + 1 in {0, 1, 2}; the matrix is cut into
+ *    tiles of 16 rows x 64 columns, tiles ordered column-tile fastest, each
+ *    tile row-major with 16 bytes per row; inside a row's 16 bytes, the trit
+ *    at column offset t (0..63) sits in byte 4*(t/16) + t%4, bits
+ *    2*((t%16)/4) .. +1.  Rows are padded to a multiple of 16 with code 1.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Exact absmean.                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* |w| * 2^149 is the integer mant * 2^shift for every finite fp32 w. */
+static void abs_times_2p149(float w, uint64_t* mant, int* shift) {
+    uint32_t bits;
+    memcpy(&bits, &w, sizeof bits);
+    bits &= 0x7FFFFFFFu;
+    uint32_t biased = bits >> 23, frac = bits & 0x7FFFFFu;
+    if (biased == 0) {              /* subnormal: frac * 2^-149 */
+        *mant = frac;
+        *shift = 0;
+    } else {                        /* (2^23 + frac) * 2^(biased - 150) */
+        *mant = frac | 0x800000u;
+        *shift = (int)biased - 1;
+    }
+}
+
+/* Non-negative integer in base 2^32 (little-endian digits). 12 digits hold
+ * sum(|w|) * 2^149 for up to 2^40 finite elements (< 2^(128+149+40)) and
+ * that value times a count below 2^40. */
+#define NDIG 14
+typedef struct { uint64_t d[NDIG]; } wide;
+
+static void wide_normalize(wide* a) {
+    uint64_t carry = 0;
+    for (int i = 0; i < NDIG; ++i) {
+        uint64_t t = a->d[i] + carry;
+        a->d[i] = t & 0xFFFFFFFFu;
+        carry = t >> 32;
+    }
+}
+
+/* a += v * 2^shift, with v < 2^64 (digits may exceed 32 bits until normalized) */
+static void wide_add_shifted(wide* a, uint64_t v, int shift) {
+    int q = shift / 32, r = shift % 32;
+    unsigned __int128 x = (unsigned __int128)v << r;
+    for (int i = q; x != 0 && i < NDIG; ++i) {
+        a->d[i] += (uint64_t)(x & 0xFFFFFFFFu);
+        x >>= 32;
+    }
+}
+
+static int wide_cmp(const wide* a, const wide* b) {
+    for (int i = NDIG - 1; i >= 0; --i) {
+        if (a->d[i] != b->d[i]) return a->d[i] < b->d[i] ? -1 : 1;
+    }
+    return 0;
+}
+
+/* f * count * 2^149 as an exact integer, for finite f >= 0 */
+static wide scaled_float(float f, uint64_t count) {
+    wide r;
+    memset(&r, 0, sizeof r);
+    uint64_t mant;
+    int shift;
+    abs_times_2p149(f, &mant, &shift);
+    unsigned __int128 p = (unsigned __int128)mant * count;
+    wide_add_shifted(&r, (uint64_t)p, shift);
+    wide_add_shifted(&r, (uint64_t)(p >> 64), shift + 64);
+    wide_normalize(&r);
+    return r;
+}
+
+static wide wide_sum(const wide* a, const wide* b) {
+    wide r;
+    for (int i = 0; i < NDIG; ++i) r.d[i] = a->d[i] + b->d[i];
+    wide_normalize(&r);
+    return r;
+}
+
+/* Round X / (count * 2^149) to the nearest fp32, ties to even, by bracketing
+ * it between two neighbouring floats and comparing exactly. */
+static float round_ratio_to_f32(const wide* X, uint64_t count) {
+    double approx = 0.0;
+    for (int i = NDIG - 1; i >= 0; --i) approx = approx * 4294967296.0 + (double)X->d[i];
+    approx = ldexp(approx, -149) / (double)count;
+    float lo = (float)approx;
+    if (!(lo <= 3.4028234663852886e38f)) lo = 3.4028234663852886e38f;
+    while (lo > 0.0f) {             /* ensure lo <= exact */
+        wide s = scaled_float(lo, count);
+        if (wide_cmp(&s, X) <= 0) break;
+        lo = nextafterf(lo, 0.0f);
+    }
+    for (;;) {                      /* ensure next(lo) > exact */
+        float up = nextafterf(lo, INFINITY);
+        if (isinf(up)) return lo;
+        wide s = scaled_float(up, count);
+        if (wide_cmp(&s, X) > 0) break;
+        lo = up;
+    }
+    wide slo = scaled_float(lo, count);
+    if (wide_cmp(&slo, X) == 0) return lo;
+    float hi = nextafterf(lo, INFINITY);
+    wide shi = scaled_float(hi, count);
+    wide twice_x = wide_sum(X, X);
+    wide mid2 = wide_sum(&slo, &shi);           /* 2 * midpoint, scaled */
+    int c = wide_cmp(&twice_x, &mid2);
+    if (c < 0) return lo;
+    if (c > 0) return hi;
+    uint32_t lo_bits;
+    memcpy(&lo_bits, &lo, sizeof lo_bits);
+    return (lo_bits & 1u) ? hi : lo;            /* tie: even significand */
+}
+
+/* gamma = mean over all `count` elements of |w|, exactly, rounded once to fp32. */
+float orc_absmean(const float* w, int64_t count) {
+    if (count <= 0) return 0.0f;
+    wide total;
+    memset(&total, 0, sizeof total);
+    const int64_t chunk = (int64_t)1 << 24;     /* digits stay below 2^56 per chunk */
+    int64_t nchunks = (count + chunk - 1) / chunk;
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t c = 0; c < nchunks; ++c) {
+        wide part;
+        memset(&part, 0, sizeof part);
+        int64_t end = (c + 1) * chunk < count ? (c + 1) * chunk : count;
+        for (int64_t i = c * chunk; i < end; ++i) {
+            uint64_t mant;
+            int shift;
+            abs_times_2p149(w[i], &mant, &shift);
+            wide_add_shifted(&part, mant, shift);
+        }
+        wide_normalize(&part);
+#pragma omp critical
+        {
+            for (int i = 0; i < NDIG; ++i) total.d[i] += part.d[i];
+            wide_normalize(&total);
+        }
+    }
+    return round_ratio_to_f32(&total, (uint64_t)count);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Ternarization: q = clamp(round(w / (gamma + eps)), -1, 1).                */
+/* ------------------------------------------------------------------------ */
+
+void orc_ternarize(const float* w, int64_t count, float gamma, int8_t* q) {
+    const float eps = 1e-5f;
+    float denom = gamma + eps;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i) {
+        float scaled = w[i] / denom;
+        float r = rintf(scaled);            /* nearest, ties to even */
+        if (r > 1.0f) r = 1.0f;
+        if (r < -1.0f) r = -1.0f;
+        q[i] = (int8_t)r;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Packed layout (4 ternary values per byte).                                */
+/* ------------------------------------------------------------------------ */
+
+int64_t orc_packed_bytes(int64_t n, int64_t k) {
+    return ((n + 15) / 16) * 16 * (k / 4);
+}
+
+/* byte offset and bit offset of trit (row, col) in a matrix with k columns */
+static void trit_position(int64_t row, int64_t col, int64_t k, int64_t* byte, int* bit) {
+    int64_t tile_row = row / 16, r = row % 16;
+    int64_t tile_col = col / 64, t = col % 64;
+    int64_t tiles_per_row = k / 64;
+    int64_t tile_start = (tile_row * tiles_per_row + tile_col) * 256;
+    *byte = tile_start + r * 16 + 4 * (t / 16) + t % 4;
+    *bit = 2 * ((t % 16) / 4);
+}
+
+/* q is [n][k] with values in {-1, 0, 1}; k must be a multiple of 64.
+ * Returns 0, or -1 if k is not a multiple of 64, -2 if a value is not a trit. */
+int orc_pack(const int8_t* q, int64_t n, int64_t k, uint8_t* packed) {
+    if (k % 64 != 0 || n < 0) return -1;
+    memset(packed, 0x55, (size_t)orc_packed_bytes(n, k));   /* code 1 = trit 0 */
+    for (int64_t row = 0; row < n; ++row) {
+        for (int64_t col = 0; col < k; ++col) {
+            int8_t v = q[row * k + col];
+            if (v < -1 || v > 1) return -2;
+            int64_t byte;
+            int bit;
+            trit_position(row, col, k, &byte, &bit);
+            uint8_t code = (uint8_t)(v + 1);
+            packed[byte] = (uint8_t)((packed[byte] & ~(3u << bit)) | (code << bit));
+        }
+    }
+    return 0;
+}
+
+/* Inverse of orc_pack for the n real rows.  Returns 0, -1 on a bad k, or -3 if
+ * a code 3 (no trit) is found anywhere in the buffer, padding rows included. */
+int orc_unpack(const uint8_t* packed, int64_t n, int64_t k, int8_t* q) {
+    if (k % 64 != 0 || n < 0) return -1;
+    int64_t total = orc_packed_bytes(n, k);
+    for (int64_t b = 0; b < total; ++b) {
+        uint8_t v = packed[b];
+        for (int f = 0; f < 4; ++f)
+            if (((v >> (2 * f)) & 3u) == 3u) return -3;
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < n; ++row) {
+        for (int64_t col = 0; col < k; ++col) {
+            int64_t byte;
+            int bit;
+            trit_position(row, col, k, &byte, &bit);
+            q[row * k + col] = (int8_t)((int)((packed[byte] >> bit) & 3u) - 1);
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Per-token absmax 8-bit activation quantization.                          */
+/* ------------------------------------------------------------------------ */
+
+static float bf16_bits_to_float(uint16_t h) {
+    uint32_t bits = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return f;
+}
+
+void orc_quant_act(const uint16_t* x, int64_t m, int64_t k, int8_t* q, float* alpha) {
+#pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < m; ++row) {
+        float amax = 0.0f;
+        for (int64_t col = 0; col < k; ++col) {
+            float v = fabsf(bf16_bits_to_float(x[row * k + col]));
+            if (v > amax) amax = v;
+        }
+        float scale = 127.0f / (amax > 1e-5f ? amax : 1e-5f);
+        for (int64_t col = 0; col < k; ++col) {
+            float prod = bf16_bits_to_float(x[row * k + col]) * scale;
+            float r = rintf(prod);
+            if (r > 127.0f) r = 127.0f;
+            if (r < -128.0f) r = -128.0f;
+            q[row * k + col] = (int8_t)r;
+        }
+        alpha[row] = amax;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* The integer product, two ways.                                           */
+/* ------------------------------------------------------------------------ */
+
+/* acc[i][j] = sum_t qx[i][t] * qw[j][t].  Returns -1 if a sum leaves int32. */
+int orc_linear_mul(const int8_t* qw, const int8_t* qx, int64_t m, int64_t n, int64_t k, int32_t* acc) {
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t j = 0; j < n; ++j) {
+        for (int64_t i = 0; i < m; ++i) {
+            int64_t s = 0;
+            for (int64_t t = 0; t < k; ++t) s += (int64_t)qx[i * k + t] * (int64_t)qw[j * k + t];
+            if (s > INT32_MAX || s < INT32_MIN) bad = 1;
+            acc[i * n + j] = (int32_t)s;
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/* Addition-only form: sum of x where w = +1 minus sum of x where w = -1;
+ * w = 0 contributes nothing.  Returns -2 on a value outside {-1, 0, 1}. */
+int orc_linear_add(const int8_t* qw, const int8_t* qx, int64_t m, int64_t n, int64_t k, int32_t* acc) {
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t j = 0; j < n; ++j) {
+        for (int64_t i = 0; i < m; ++i) {
+            int64_t plus = 0, minus = 0;
+            for (int64_t t = 0; t < k; ++t) {
+                int8_t w = qw[j * k + t];
+                if (w == 1) plus += qx[i * k + t];
+                else if (w == -1) minus += qx[i * k + t];
+                else if (w != 0) bad = 1;
+            }
+            acc[i * n + j] = (int32_t)(plus - minus);
+        }
+    }
+    return bad ? -2 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Rescale to bf16.                                                          */
+/* ------------------------------------------------------------------------ */
+
+/* Nearest bf16 (ties to even) of a binary64 value, as a bit pattern. */
+uint16_t orc_bf16_from_double(double v) {
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    double a = fabs(v);
+    if (a == 0.0) return sign;
+    if (isnan(v)) return 0x7FC0u;
+    int e;
+    frexp(a, &e);                       /* a in [2^(e-1), 2^e) */
+    int ulp_exp = e - 8;                /* 8 significant bits */
+    if (ulp_exp < -133) ulp_exp = -133; /* subnormal spacing 2^-133 */
+    double r = nearbyint(ldexp(a, -ulp_exp));
+    double rounded = ldexp(r, ulp_exp);
+    if (rounded >= 0x1p128) return (uint16_t)(sign | 0x7F80u);
+    float f = (float)rounded;           /* exact */
+    uint32_t bits;
+    memcpy(&bits, &f, sizeof bits);
+    return (uint16_t)(sign | (bits >> 16));
+}
+
+/* y[i][j] = bf16(acc[i][j] * gamma * alpha[i] / 127), evaluated in binary64 */
+void orc_rescale(const int32_t* acc, int64_t m, int64_t n, float gamma, const float* alpha, uint16_t* y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j) {
+            double v = (double)acc[i * n + j] * (double)gamma * (double)alpha[i] / 127.0;
+            y[i * n + j] = orc_bf16_from_double(v);
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Whole layer from packed weights (used to time the CPU baseline).          */
+/* ------------------------------------------------------------------------ */
+
+/* y = BitLinear(x) with packed ternary weights: quantize x per token, take the
+ * integer product reading each trit from the packed buffer, rescale to bf16.
+ * xq, alpha and acc are caller-provided scratch/outputs of sizes m*k, m, m*n. */
+int orc_bitlinear_forward(const uint8_t* packed, float gamma, const uint16_t* x, int64_t m, int64_t n,
+                          int64_t k, int8_t* xq, float* alpha, int32_t* acc, uint16_t* y) {
+    if (k % 64 != 0) return -1;
+    orc_quant_act(x, m, k, xq, alpha);
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < n; ++j) {
+        for (int64_t i = 0; i < m; ++i) {
+            int64_t s = 0;
+            for (int64_t t = 0; t < k; ++t) {
+                int64_t byte;
+                int bit;
+                trit_position(j, t, k, &byte, &bit);
+                int w = (int)((packed[byte] >> bit) & 3u) - 1;
+                s += (int64_t)w * xq[i * k + t];
+            }
+            acc[i * n + j] = (int32_t)s;
+        }
+    }
+    orc_rescale(acc, m, n, gamma, alpha, y);
+    return 0;
+}

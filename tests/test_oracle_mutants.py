@@ -1,0 +1,64 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case plants one mistake in a copy of ``oracle/oracle.c`` (a dropped term,
+a wrong rounding mode, a wrong sign or index, a transposed operand), builds it
+on the CPU, and runs the oracle pin suites against that build in a
+subprocess.  The pins must fail for every mutant.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+PINS = [os.path.join(ROOT, "tests", "test_oracle_absmean.py"),
+        os.path.join(ROOT, "tests", "test_oracle_act_linear.py")]
+
+MUTANTS = {
+    "ternarize_round_half_away": ("float r = rintf(scaled);", "float r = roundf(scaled);"),
+    "ternarize_drops_eps": ("float denom = gamma + eps;", "float denom = gamma;"),
+    "ternarize_no_clamp": ("if (r > 1.0f) r = 1.0f;", ""),
+    "absmean_wrong_count": ("return round_ratio_to_f32(&total, (uint64_t)count);",
+                            "return round_ratio_to_f32(&total, (uint64_t)count + 1);"),
+    "absmean_drops_subnormal_scale": ("*shift = (int)biased - 1;", "*shift = (int)biased;"),
+    "absmean_tie_to_odd": ("return (lo_bits & 1u) ? hi : lo;", "return (lo_bits & 1u) ? lo : hi;"),
+    "pack_transposed_in_word": ("*byte = tile_start + r * 16 + 4 * (t / 16) + t % 4;\n    *bit = 2 * ((t % 16) / 4);",
+                                "*byte = tile_start + r * 16 + 4 * (t / 16) + (t % 16) / 4;\n    *bit = 2 * (t % 4);"),
+    "pack_row_major_tiles": ("int64_t tile_start = (tile_row * tiles_per_row + tile_col) * 256;",
+                             "int64_t tile_start = (tile_col * ((k + 63) / 64) + tile_row) * 256;"),
+    "quant_scale_128": ("float scale = 127.0f / (amax > 1e-5f ? amax : 1e-5f);",
+                        "float scale = 128.0f / (amax > 1e-5f ? amax : 1e-5f);"),
+    "quant_round_half_away": ("float r = rintf(prod);", "float r = roundf(prod);"),
+    "quant_no_eps_floor": ("float scale = 127.0f / (amax > 1e-5f ? amax : 1e-5f);",
+                           "float scale = 127.0f / (amax > 0.0f ? amax : 1.0f);"),
+    "linear_sign_flip": ("for (int64_t t = 0; t < k; ++t) s += (int64_t)qx[i * k + t] * (int64_t)qw[j * k + t];",
+                         "for (int64_t t = 0; t < k; ++t) s -= (int64_t)qx[i * k + t] * (int64_t)qw[j * k + t];"),
+    "linear_transposed_operand": ("for (int64_t t = 0; t < k; ++t) s += (int64_t)qx[i * k + t] * (int64_t)qw[j * k + t];",
+                                  "for (int64_t t = 0; t < k; ++t) s += (int64_t)qx[i * k + t] * (int64_t)qw[(t % n) * k + j % k];"),
+    "rescale_drops_alpha": ("(double)acc[i * n + j] * (double)gamma * (double)alpha[i] / 127.0;",
+                            "(double)acc[i * n + j] * (double)gamma / 127.0;"),
+    "rescale_128": ("(double)acc[i * n + j] * (double)gamma * (double)alpha[i] / 127.0;",
+                    "(double)acc[i * n + j] * (double)gamma * (double)alpha[i] / 128.0;"),
+    "bf16_round_half_away": ("double r = nearbyint(ldexp(a, -ulp_exp));", "double r = round(ldexp(a, -ulp_exp));"),
+    "unpack_codes_not_trits": ("q[row * k + col] = (int8_t)((int)((packed[byte] >> bit) & 3u) - 1);",
+                               "q[row * k + col] = (int8_t)((int)((packed[byte] >> bit) & 3u));"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    with open(SRC) as f:
+        src = f.read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mutant_c = tmp_path / "oracle_mutant.c"
+    mutant_c.write_text(src.replace(old, new))
+    so = tmp_path / "liboracle_mutant.so"
+    subprocess.run(["gcc", "-O2", "-std=gnu11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+                    str(mutant_c), "-o", str(so), "-lm"], check=True)
+    env = dict(os.environ, BITLINEAR_ORACLE_SO=str(so), OMP_NUM_THREADS="2")
+    res = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", *PINS],
+                         cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert res.returncode != 0, f"pins did not catch mutant {name}:\n{res.stdout[-2000:]}"
