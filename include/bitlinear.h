@@ -1,0 +1,126 @@
+/*
+ * bitlinear.h -- C ABI of the MI355X (gfx950) BitLinear W1.58A8 library.
+ *
+ * The layer is the BitNet b1.58 BitLinear: weights are absmean-ternarized to
+ * {-1, 0, +1} and stored packed at 2 bits each; activations are quantized per
+ * token to int8 by absmax; the product is accumulated in int32 and rescaled to
+ * bf16.  Sources, on the BitNet b1.58 pages:
+ *   [P1] bako.co, "BitNet b1.58 and the 1-Bit AI Architecture Revolution",
+ *        section "The BitLinear Layer and AbsMean Quantization": gamma is the
+ *        mean absolute value of the entire weight matrix; each weight is
+ *        divided by (gamma + 1e-5), rounded to the nearest integer and clamped
+ *        to [-1, 1]; with ternary weights the matrix product reduces to
+ *        integer additions and subtractions.
+ *   [P2] deepmox.com chapter 8, "A low-bit model is a whole-stack design":
+ *        weights take the three values -1, 0, +1; activations use a separate
+ *        per-token 8-bit path (W1.58A8); the GPU path packs four ternary values
+ *        per 8-bit storage unit, moves packed weights from HBM on chip,
+ *        unpacks them and computes with the 8-bit activations.
+ *   [P3] onilabs.co, "A Two-Billion Ternary Bet": activations are quantized
+ *        dynamically; scale factors are staged for mixed-precision compute.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees or synchronizes; it only enqueues work
+ *     on `stream` (a hipStream_t; NULL means the null stream) and returns.
+ *   - Tensors are dense and row-major.  W is [n][k] (n output features,
+ *     k input features), activations are [m][k] (m tokens), outputs [m][n].
+ *   - k must be a positive multiple of 64 and at most BL_MAX_K; m and n may be
+ *     0 (nothing is enqueued); n * k and m * k, m * n stay below 2^40.
+ *   - Pointers that are read or written with 128-bit accesses (w, packed, x,
+ *     xq, workspace) must be 16-byte aligned; alpha, gamma and acc 4-byte,
+ *     y 2-byte aligned.
+ *   - Validation happens on the host before anything is enqueued; a failing
+ *     check returns its code and enqueues nothing.  A failed kernel launch
+ *     returns BL_ERR_HIP.  Faults inside kernels surface at the caller's next
+ *     synchronization.  Entry points are thread-safe (no global mutable
+ *     state); calls on one stream execute in order.
+ *   - Inputs must be finite (no Inf or NaN).
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BL_MAX_K (1 << 22)
+
+typedef enum {
+    BL_OK = 0,
+    BL_ERR_NULL = 1,      /* a required pointer is NULL                          */
+    BL_ERR_SHAPE = 2,     /* m, n or k outside the supported range               */
+    BL_ERR_ALIGN = 3,     /* a pointer is not aligned as required                */
+    BL_ERR_WORKSPACE = 4, /* workspace smaller than bl_ternarize_pack_workspace_bytes */
+    BL_ERR_HIP = 5        /* the HIP runtime rejected a launch                   */
+} bl_status;
+
+/* Size in bytes of the packed ternary buffer for an [n][k] weight matrix:
+ * ceil(n/16)*16 * k/4 (four trits per byte [P2]; rows padded to 16).
+ * Returns 0 for an invalid shape. */
+size_t bl_packed_bytes(int64_t n, int64_t k);
+
+/* Device workspace needed by bl_ternarize_pack (a fixed 2 KiB: one 64-bit
+ * integer per fp32 exponent).  Returns 0 for an invalid shape. */
+size_t bl_ternarize_pack_workspace_bytes(int64_t n, int64_t k);
+
+/* Weight preparation [P1]: gamma = mean |w| over all n*k weights, computed
+ * exactly and rounded once to fp32 (nearest, ties to even); then every weight
+ * becomes q = clamp(round_half_even(w / fl32(gamma + 1e-5f)), -1, 1), the
+ * division in correctly rounded fp32; q is stored packed.
+ *   w         [n][k] fp32, read only.
+ *   packed    out, bl_packed_bytes(n, k) bytes.  Layout: 2-bit code q + 1
+ *             (0, 1, 2; 3 never occurs).  The matrix is cut into tiles of 16
+ *             rows x 64 columns; tile (i, j) starts at byte
+ *             256 * (i * (k/64) + j); inside it, row r owns bytes 16r..16r+15,
+ *             and column 64j + t of that row sits in byte 16r + (t % 16) at
+ *             bits 2*(t/16)..2*(t/16)+1.  Rows n..ceil(n/16)*16-1 hold code 1.
+ *   gamma     out, one fp32 on the device (gamma, without eps).
+ *   workspace device scratch of workspace_bytes >= the size above; its
+ *             contents on entry do not matter and are clobbered.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE (n < 1 or bad k), BL_ERR_ALIGN,
+ *         BL_ERR_WORKSPACE, BL_ERR_HIP. */
+bl_status bl_ternarize_pack(const float* w, int64_t n, int64_t k, uint8_t* packed, float* gamma,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Per-token absmax int8 activation quantization [P2, P3]: for each row i,
+ * a = max_j |x[i][j]|, s = fl32(127 / max(a, 1e-5f)),
+ * xq[i][j] = clamp(round_half_even(fl32(x[i][j] * s)), -128, 127), alpha[i] = a.
+ *   x      [m][k] bf16 (raw 16-bit patterns), read only.
+ *   xq     out [m][k] int8.
+ *   alpha  out [m] fp32 (the per-token absmax, exactly a bf16 value).
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_HIP. */
+bl_status bl_quant_act(const uint16_t* x, int64_t m, int64_t k, int8_t* xq, float* alpha, void* stream);
+
+/* Ternary x int8 product with rescale [P1, P3]:
+ *   acc[i][j] = sum_t xq[i][t] * q[j][t]          (exact, int32)
+ *   y[i][j]   = bf16(acc[i][j] * gamma * alpha[i] / 127)   (fp32 evaluation,
+ *               within one bf16 ulp of the exactly rounded value; acc = 0
+ *               gives +0)
+ *   packed/gamma as written by bl_ternarize_pack for an [n][k] matrix;
+ *   xq/alpha as written by bl_quant_act for [m][k] activations.
+ *   acc    out [m][n] int32, or NULL to skip it.
+ *   y      out [m][n] bf16 bit patterns, or NULL to skip it (not both NULL).
+ * Kernel choice depends on m only (GEMV for m <= 16, tiled GEMM above);
+ * results do not depend on it.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_HIP. */
+bl_status bl_linear(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha,
+                    int64_t m, int64_t n, int64_t k, int32_t* acc, uint16_t* y, void* stream);
+
+/* Unpack a packed buffer back to trits (test and inspection helper [P2]):
+ * q[j][t] in {-1, 0, 1} for the n real rows.  Codes 3 decode as 2 (never
+ * produced by bl_ternarize_pack).
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_HIP. */
+bl_status bl_unpack_ternary(const uint8_t* packed, int64_t n, int64_t k, int8_t* q, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* bl_status_string(bl_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITLINEAR_H */

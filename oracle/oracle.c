@@ -36,8 +36,8 @@
  *  - packed layout: 2-bit code c = q + 1 in {0, 1, 2}; the matrix is cut into
  *    tiles of 16 rows x 64 columns, tiles ordered column-tile fastest, each
  *    tile row-major with 16 bytes per row; inside a row's 16 bytes, the trit
- *    at column offset t (0..63) sits in byte 4*(t/16) + t%4, bits
- *    2*((t%16)/4) .. +1.  Rows are padded to a multiple of 16 with code 1.
+ *    at column offset t (0..63) sits in byte t % 16, bits 2*(t/16) .. +1.
+ *    Rows are padded to a multiple of 16 with code 1.
  */
 #include <math.h>
 #include <stdint.h>
@@ -209,8 +209,8 @@ static void trit_position(int64_t row, int64_t col, int64_t k, int64_t* byte, in
     int64_t tile_col = col / 64, t = col % 64;
     int64_t tiles_per_row = k / 64;
     int64_t tile_start = (tile_row * tiles_per_row + tile_col) * 256;
-    *byte = tile_start + r * 16 + 4 * (t / 16) + t % 4;
-    *bit = 2 * ((t % 16) / 4);
+    *byte = tile_start + r * 16 + t % 16;
+    *bit = 2 * (t / 16);
 }
 
 /* q is [n][k] with values in {-1, 0, 1}; k must be a multiple of 64.

@@ -223,28 +223,28 @@ def test_pack_single_trit_touches_one_two_bit_field():
     assert len(seen) == n * k
 
 
-def test_layout_words_give_codes_in_column_order():
+def test_layout_fields_give_codes_in_column_order():
     """Documented property of the tiled layout: in row r of tile (i, j), the
-    32-bit word s (bytes 4s..4s+3 of the row's 16 bytes, little-endian)
-    shifted right by 2*t and masked with 0x03030303 holds the codes (trit + 1)
-    of columns 64*j + 16*s + 4*t + 0..3, one per byte, in byte order."""
+    row's 16 bytes read as four little-endian 32-bit words v0..v3, shifted
+    right by 2*f and masked with 0x03030303, hold the codes (trit + 1) of
+    columns 64*j + 16*f + 4*w + 0..3 in word w, one per byte, in byte order;
+    so field f of the 16 bytes is the 16 consecutive columns 64*j + 16*f + 0..15."""
     rng = np.random.default_rng(11)
     n, k = 35, 256
     q = rng.integers(-1, 2, size=(n, k)).astype(np.int8)
     p = oracle.pack(q)
-    tiles = p.reshape((n + 15) // 16, k // 64, 16, 4, 4)  # [row tile][col tile][row][word][byte]
-    words = tiles.view(np.uint32).reshape((n + 15) // 16, k // 64, 16, 4)
+    words = p.view(np.uint32).reshape((n + 15) // 16, k // 64, 16, 4)  # [row tile][col tile][row][word]
     for ti in range((n + 15) // 16):
         for tj in range(k // 64):
             for r in range(16):
                 row = ti * 16 + r
-                for s in range(4):
-                    wv = int(words[ti, tj, r, s])
-                    for t in range(4):
-                        codes = ((wv >> (2 * t)) & 0x03030303).to_bytes(4, "little")
-                        cols = [64 * tj + 16 * s + 4 * t + b for b in range(4)]
-                        want = [int(q[row, c]) + 1 if row < n else 1 for c in cols]
-                        assert list(codes) == want
+                for f in range(4):
+                    codes = []
+                    for wi in range(4):
+                        codes += list(((int(words[ti, tj, r, wi]) >> (2 * f)) & 0x03030303).to_bytes(4, "little"))
+                    cols = [64 * tj + 16 * f + b for b in range(16)]
+                    want = [int(q[row, c]) + 1 if row < n else 1 for c in cols]
+                    assert codes == want
 
 
 def test_weight_path_end_to_end_small():

@@ -24,8 +24,8 @@ MUTANTS = {
                             "return round_ratio_to_f32(&total, (uint64_t)count + 1);"),
     "absmean_drops_subnormal_scale": ("*shift = (int)biased - 1;", "*shift = (int)biased;"),
     "absmean_tie_to_odd": ("return (lo_bits & 1u) ? hi : lo;", "return (lo_bits & 1u) ? lo : hi;"),
-    "pack_transposed_in_word": ("*byte = tile_start + r * 16 + 4 * (t / 16) + t % 4;\n    *bit = 2 * ((t % 16) / 4);",
-                                "*byte = tile_start + r * 16 + 4 * (t / 16) + (t % 16) / 4;\n    *bit = 2 * (t % 4);"),
+    "pack_transposed_in_row": ("*byte = tile_start + r * 16 + t % 16;\n    *bit = 2 * (t / 16);",
+                               "*byte = tile_start + r * 16 + t / 4;\n    *bit = 2 * (t % 4);"),
     "pack_row_major_tiles": ("int64_t tile_start = (tile_row * tiles_per_row + tile_col) * 256;",
                              "int64_t tile_start = (tile_col * ((k + 63) / 64) + tile_row) * 256;"),
     "quant_scale_128": ("float scale = 127.0f / (amax > 1e-5f ? amax : 1e-5f);",
