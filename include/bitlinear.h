@@ -25,13 +25,17 @@
  *     on `stream` (a hipStream_t; NULL means the null stream) and returns.
  *   - Tensors are dense and row-major.  W is [n][k] (n output features,
  *     k input features), activations are [m][k] (m tokens), outputs [m][n].
- *   - k must be a positive multiple of 64 and at most BL_MAX_K; m and n may be
- *     0 (nothing is enqueued); n * k and m * k, m * n stay below 2^40.
+ *   - k must be a positive multiple of 64 and at most BL_MAX_K (2^22);
+ *     m <= BL_MAX_M (2^24) and n <= BL_MAX_N (2^30); m and n may be 0
+ *     (nothing is enqueued) except where stated; n * k, m * k and m * n must
+ *     stay below 2^40.
  *   - Pointers that are read or written with 128-bit accesses (w, packed, x,
  *     xq, workspace) must be 16-byte aligned; alpha, gamma and acc 4-byte,
  *     y 2-byte aligned.
  *   - Validation happens on the host before anything is enqueued; a failing
- *     check returns its code and enqueues nothing.  A failed kernel launch
+ *     check returns its code and enqueues nothing.  Shapes are checked first;
+ *     an empty problem (m or n = 0) then returns BL_OK at once, so empty
+ *     tensors may pass NULL pointers.  A failed kernel launch
  *     returns BL_ERR_HIP.  Faults inside kernels surface at the caller's next
  *     synchronization.  Entry points are thread-safe (no global mutable
  *     state); calls on one stream execute in order.
@@ -48,6 +52,8 @@ extern "C" {
 #endif
 
 #define BL_MAX_K (1 << 22)
+#define BL_MAX_M (1 << 24)
+#define BL_MAX_N (1 << 30)
 
 typedef enum {
     BL_OK = 0,
@@ -111,8 +117,8 @@ bl_status bl_linear(const uint8_t* packed, const float* gamma, const int8_t* xq,
                     int64_t m, int64_t n, int64_t k, int32_t* acc, uint16_t* y, void* stream);
 
 /* Unpack a packed buffer back to trits (test and inspection helper [P2]):
- * q[j][t] in {-1, 0, 1} for the n real rows.  Codes 3 decode as 2 (never
- * produced by bl_ternarize_pack).
+ * q[j][t] in {-1, 0, 1} for the n real rows.  A code 3 (never produced by
+ * bl_ternarize_pack) decodes as 0.
  * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_HIP. */
 bl_status bl_unpack_ternary(const uint8_t* packed, int64_t n, int64_t k, int8_t* q, void* stream);
 

@@ -1,0 +1,169 @@
+"""BitLinear W1.58A8 on MI355X (gfx950): thin Python binding of ``libbitlinear.so``.
+
+The layer is the BitNet b1.58 BitLinear (bako.co, "The BitLinear Layer and
+AbsMean Quantization"; deepmox.com chapter 8, "A low-bit model is a whole-stack
+design"): absmean-ternarized weights packed at 2 bits, per-token absmax int8
+activations, int32 accumulation and a bf16 rescale.  Every step runs in the HIP
+kernels behind the C ABI (``include/bitlinear.h``); this module only marshals
+torch tensors (device memory, the current stream) into those calls.  There is
+no fallback: if the library is missing, importing raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+from ._build import LIB_PATH, INCLUDE
+
+__all__ = [
+    "BitLinearError", "bl_packed_bytes", "bl_ternarize_pack_workspace_bytes", "bl_ternarize_pack",
+    "bl_quant_act", "bl_linear", "bl_unpack_ternary", "bl_status_string", "library", "declared_symbols",
+]
+
+
+class BitLinearError(RuntimeError):
+    """A ``bl_*`` call returned a status other than BL_OK."""
+
+    def __init__(self, func: str, status: int):
+        super().__init__(f"{func}: {bl_status_string(status)} ({status})")
+        self.status = status
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libbitlinear.so is not built ({LIB_PATH}); run __graft_entry__.build()")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P, _I64, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+_lib.bl_packed_bytes.argtypes = [_I64, _I64]
+_lib.bl_packed_bytes.restype = _SZ
+_lib.bl_ternarize_pack_workspace_bytes.argtypes = [_I64, _I64]
+_lib.bl_ternarize_pack_workspace_bytes.restype = _SZ
+_lib.bl_ternarize_pack.argtypes = [_P, _I64, _I64, _P, _P, _P, _SZ, _P]
+_lib.bl_ternarize_pack.restype = ctypes.c_int
+_lib.bl_quant_act.argtypes = [_P, _I64, _I64, _P, _P, _P]
+_lib.bl_quant_act.restype = ctypes.c_int
+_lib.bl_linear.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P]
+_lib.bl_linear.restype = ctypes.c_int
+_lib.bl_unpack_ternary.argtypes = [_P, _I64, _I64, _P, _P]
+_lib.bl_unpack_ternary.restype = ctypes.c_int
+_lib.bl_status_string.argtypes = [ctypes.c_int]
+_lib.bl_status_string.restype = ctypes.c_char_p
+
+
+def library() -> ctypes.CDLL:
+    """The loaded C-ABI library (for callers that marshal pointers themselves)."""
+    return _lib
+
+
+def declared_symbols() -> list[str]:
+    """Names of the functions declared in ``include/bitlinear.h``."""
+    with open(os.path.join(INCLUDE, "bitlinear.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bl_\w+)\s*\(", text)))
+
+
+def bl_status_string(status: int) -> str:
+    return _lib.bl_status_string(int(status)).decode()
+
+
+def _check(func: str, status: int) -> None:
+    if status != 0:
+        raise BitLinearError(func, status)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape: tuple | None = None) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def bl_packed_bytes(n: int, k: int) -> int:
+    return int(_lib.bl_packed_bytes(n, k))
+
+
+def bl_ternarize_pack_workspace_bytes(n: int, k: int) -> int:
+    return int(_lib.bl_ternarize_pack_workspace_bytes(n, k))
+
+
+def bl_ternarize_pack(w: torch.Tensor, packed: torch.Tensor | None = None, gamma: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None):
+    """fp32 weights ``[n][k]`` -> (packed uint8 [bl_packed_bytes], gamma fp32 [1])."""
+    _need(w, "w", torch.float32)
+    n, k = w.shape
+    nbytes = bl_packed_bytes(n, k)
+    if packed is None:
+        packed = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=w.device)
+    if gamma is None:
+        gamma = torch.empty(1, dtype=torch.float32, device=w.device)
+    ws = bl_ternarize_pack_workspace_bytes(n, k)
+    if workspace is None:
+        workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=w.device)
+    _check("bl_ternarize_pack", _lib.bl_ternarize_pack(_ptr(w), n, k, _ptr(packed), _ptr(gamma), _ptr(workspace),
+                                                       workspace.numel(), _stream(w.device)))
+    return packed, gamma
+
+
+def bl_quant_act(x: torch.Tensor, xq: torch.Tensor | None = None, alpha: torch.Tensor | None = None):
+    """bf16 activations ``[m][k]`` -> (int8 [m][k], per-token absmax fp32 [m])."""
+    _need(x, "x", torch.bfloat16)
+    m, k = x.shape
+    if xq is None:
+        xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if alpha is None:
+        alpha = torch.empty(m, dtype=torch.float32, device=x.device)
+    _need(xq, "xq", torch.int8, (m, k))
+    _need(alpha, "alpha", torch.float32, (m,))
+    _check("bl_quant_act", _lib.bl_quant_act(_ptr(x), m, k, _ptr(xq), _ptr(alpha), _stream(x.device)))
+    return xq, alpha
+
+
+def bl_linear(packed: torch.Tensor, gamma: torch.Tensor, xq: torch.Tensor, alpha: torch.Tensor, n: int,
+              acc: torch.Tensor | None | bool = True, y: torch.Tensor | None | bool = True):
+    """Packed ternary ``[n][k]`` times int8 ``[m][k]`` -> (int32 acc [m][n] or None, bf16 y [m][n] or None).
+
+    ``acc``/``y``: a tensor to write into, True to allocate, or False/None to skip."""
+    _need(xq, "xq", torch.int8)
+    m, k = xq.shape
+    dev = xq.device
+    if acc is True:
+        acc = torch.empty((m, n), dtype=torch.int32, device=dev)
+    if y is True:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    acc = acc if isinstance(acc, torch.Tensor) else None
+    y = y if isinstance(y, torch.Tensor) else None
+    if acc is not None:
+        _need(acc, "acc", torch.int32, (m, n))
+    if y is not None:
+        _need(y, "y", torch.bfloat16, (m, n))
+    _need(packed, "packed", torch.uint8)
+    if packed.numel() < bl_packed_bytes(n, k):
+        raise ValueError("packed buffer is smaller than bl_packed_bytes(n, k)")
+    _check("bl_linear", _lib.bl_linear(_ptr(packed), _ptr(gamma), _ptr(xq), _ptr(alpha), m, n, k, _ptr(acc), _ptr(y),
+                                       _stream(dev)))
+    return acc, y
+
+
+def bl_unpack_ternary(packed: torch.Tensor, n: int, k: int, q: torch.Tensor | None = None) -> torch.Tensor:
+    """Packed buffer -> int8 trits ``[n][k]``."""
+    _need(packed, "packed", torch.uint8)
+    if q is None:
+        q = torch.empty((n, k), dtype=torch.int8, device=packed.device)
+    _check("bl_unpack_ternary", _lib.bl_unpack_ternary(_ptr(packed), n, k, _ptr(q), _stream(packed.device)))
+    return q

@@ -1,0 +1,90 @@
+// C ABI of the BitLinear W1.58A8 library: argument validation and dispatch.
+// Declarations, argument meaning, layouts and error behaviour: include/bitlinear.h.
+#include "../../include/bitlinear.h"
+#include "internal.h"
+
+namespace {
+
+constexpr int64_t kLimit40 = (int64_t)1 << 40;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool valid_k(int64_t k) { return k >= 64 && k <= BL_MAX_K && k % 64 == 0; }
+
+bool product_ok(int64_t a, int64_t b) { return a == 0 || b < kLimit40 / a; }
+
+bl_status from_hip(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t bl_packed_bytes(int64_t n, int64_t k) {
+  if (n < 0 || n > BL_MAX_N || !valid_k(k) || !product_ok(n + 16, k)) return 0;
+  return (size_t)((n + 15) / 16 * 16) * (size_t)(k / 4);
+}
+
+size_t bl_ternarize_pack_workspace_bytes(int64_t n, int64_t k) {
+  if (n < 1 || n > BL_MAX_N || !valid_k(k) || !product_ok(n + 16, k)) return 0;
+  return 256 * sizeof(unsigned long long);
+}
+
+bl_status bl_ternarize_pack(const float* w, int64_t n, int64_t k, uint8_t* packed, float* gamma, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!w || !packed || !gamma || !workspace) return BL_ERR_NULL;
+  if (n < 1 || n > BL_MAX_N || !valid_k(k) || !product_ok(n + 16, k)) return BL_ERR_SHAPE;
+  if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(gamma, 4) || !aligned(workspace, 16)) return BL_ERR_ALIGN;
+  if (workspace_bytes < bl_ternarize_pack_workspace_bytes(n, k)) return BL_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  unsigned long long* bins = (unsigned long long*)workspace;
+  hipError_t e = bl::launch_zero_bins(bins, s);
+  if (e == hipSuccess) e = bl::launch_absmean_bins(w, n * k, bins, s);
+  if (e == hipSuccess) e = bl::launch_gamma_fold(bins, n * k, gamma, s);
+  if (e == hipSuccess) e = bl::launch_ternarize_pack(w, n, k, gamma, packed, s);
+  return from_hip(e);
+}
+
+bl_status bl_quant_act(const uint16_t* x, int64_t m, int64_t k, int8_t* xq, float* alpha, void* stream) {
+  if (m < 0 || m > BL_MAX_M || !valid_k(k) || !product_ok(m, k)) return BL_ERR_SHAPE;
+  if (m == 0) return BL_OK;  // empty tensors may carry NULL pointers
+  if (!x || !xq || !alpha) return BL_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(alpha, 4)) return BL_ERR_ALIGN;
+  return from_hip(bl::launch_quant_act(x, m, k, xq, alpha, (hipStream_t)stream));
+}
+
+bl_status bl_linear(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
+                    int64_t n, int64_t k, int32_t* acc, uint16_t* y, void* stream) {
+  if (m < 0 || m > BL_MAX_M || n < 0 || n > BL_MAX_N || !valid_k(k) || !product_ok(m, k) || !product_ok(n + 16, k) ||
+      !product_ok(m, n))
+    return BL_ERR_SHAPE;
+  if (m == 0 || n == 0) return BL_OK;  // empty tensors may carry NULL pointers
+  if (!packed || !gamma || !xq || !alpha || (!acc && !y)) return BL_ERR_NULL;
+  if (!aligned(packed, 16) || !aligned(xq, 16) || !aligned(gamma, 4) || !aligned(alpha, 4) ||
+      (acc && !aligned(acc, 4)) || (y && !aligned(y, 2)))
+    return BL_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  if (m <= 16) return from_hip(bl::launch_gemv(packed, gamma, xq, alpha, m, n, k, acc, y, s));
+  return from_hip(bl::launch_gemm(packed, gamma, xq, alpha, m, n, k, acc, y, s));
+}
+
+bl_status bl_unpack_ternary(const uint8_t* packed, int64_t n, int64_t k, int8_t* q, void* stream) {
+  if (n < 0 || n > BL_MAX_N || !valid_k(k) || !product_ok(n + 16, k)) return BL_ERR_SHAPE;
+  if (n == 0) return BL_OK;
+  if (!packed || !q) return BL_ERR_NULL;
+  if (!aligned(packed, 16) || !aligned(q, 16)) return BL_ERR_ALIGN;
+  return from_hip(bl::launch_unpack(packed, n, k, q, (hipStream_t)stream));
+}
+
+const char* bl_status_string(bl_status s) {
+  switch (s) {
+    case BL_OK: return "BL_OK";
+    case BL_ERR_NULL: return "BL_ERR_NULL: a required pointer is NULL";
+    case BL_ERR_SHAPE: return "BL_ERR_SHAPE: m, n or k outside the supported range";
+    case BL_ERR_ALIGN: return "BL_ERR_ALIGN: a pointer is not aligned as required";
+    case BL_ERR_WORKSPACE: return "BL_ERR_WORKSPACE: workspace too small";
+    case BL_ERR_HIP: return "BL_ERR_HIP: the HIP runtime rejected a launch";
+  }
+  return "unknown bl_status";
+}
+
+}  // extern "C"

@@ -1,0 +1,32 @@
+// Internal declarations of the BitLinear W1.58A8 HIP library (gfx950).
+// Launchers are called only by the C ABI in abi.hip after validation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bl {
+
+// Packed layout: 16-row x 64-column tiles of 256 bytes, column tile fastest.
+constexpr int kTileRows = 16;
+constexpr int kTileCols = 64;
+constexpr int kTileBytes = 256;
+
+// Weight packer (absmean exponent bins -> exact gamma -> ternarize + pack).
+hipError_t launch_zero_bins(unsigned long long* bins, hipStream_t s);
+hipError_t launch_absmean_bins(const float* w, int64_t count, unsigned long long* bins, hipStream_t s);
+hipError_t launch_gamma_fold(const unsigned long long* bins, int64_t count, float* gamma, hipStream_t s);
+hipError_t launch_ternarize_pack(const float* w, int64_t n, int64_t k, const float* gamma, uint8_t* packed,
+                                 hipStream_t s);
+hipError_t launch_unpack(const uint8_t* packed, int64_t n, int64_t k, int8_t* q, hipStream_t s);
+
+// Per-token absmax int8 quantizer.
+hipError_t launch_quant_act(const uint16_t* x, int64_t m, int64_t k, int8_t* xq, float* alpha, hipStream_t s);
+
+// Ternary x int8 products (m <= 16: GEMV; larger m: LDS-tiled GEMM).
+hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
+                       int64_t n, int64_t k, int32_t* acc, uint16_t* y, hipStream_t s);
+hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
+                       int64_t n, int64_t k, int32_t* acc, uint16_t* y, hipStream_t s);
+
+}  // namespace bl

@@ -24,10 +24,12 @@ def _built_libraries():
 
     datagen.build()
     oracle.build()
-    try:
-        from ternary_weight_absmean_amd import _build
-    except ImportError:
-        _build = None
-    if _build is not None and not os.path.exists(_build.LIB_PATH):
-        _build.build()
+    import importlib.util
+
+    spec = importlib.util.spec_from_file_location(
+        "_bitlinear_build", os.path.join(ROOT, "ternary_weight_absmean_amd", "_build.py"))
+    build_mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(build_mod)
+    if not os.path.exists(build_mod.LIB_PATH):
+        build_mod.build()
     yield

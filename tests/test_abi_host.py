@@ -1,0 +1,110 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+The library must load, export every function that include/bitlinear.h
+declares, and reject bad arguments on the host before anything is enqueued.
+Pointers passed here are never dereferenced: every call fails validation (or
+has nothing to do) before touching the device.
+"""
+import ctypes
+
+import pytest
+import torch
+
+import ternary_weight_absmean_amd as bl
+
+BL_OK, BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_WORKSPACE, BL_ERR_HIP = range(6)
+FAKE = 0x10000  # aligned, non-null, never dereferenced
+lib = bl.library()
+
+
+def test_exports_every_declared_symbol():
+    names = bl.declared_symbols()
+    assert {"bl_ternarize_pack", "bl_quant_act", "bl_linear", "bl_unpack_ternary", "bl_packed_bytes",
+            "bl_ternarize_pack_workspace_bytes", "bl_status_string"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in range(6):
+        assert bl.bl_status_string(code).startswith("BL_")
+    assert "unknown" in bl.bl_status_string(99)
+
+
+def test_sizes():
+    assert bl.bl_packed_bytes(2560, 2560) == 2560 * 640
+    assert bl.bl_packed_bytes(17, 64) == 32 * 16
+    assert bl.bl_packed_bytes(0, 64) == 0
+    assert bl.bl_packed_bytes(16, 63) == 0
+    assert bl.bl_packed_bytes(16, 1 << 23) == 0
+    assert bl.bl_ternarize_pack_workspace_bytes(57344, 8192) == 2048
+    assert bl.bl_ternarize_pack_workspace_bytes(0, 64) == 0
+
+
+def test_ternarize_pack_validation():
+    f = lib.bl_ternarize_pack
+    assert f(None, 16, 64, FAKE, FAKE, FAKE, 2048, None) == BL_ERR_NULL
+    assert f(FAKE, 16, 64, FAKE, FAKE, None, 2048, None) == BL_ERR_NULL
+    assert f(FAKE, 0, 64, FAKE, FAKE, FAKE, 2048, None) == BL_ERR_SHAPE
+    assert f(FAKE, 16, 96, FAKE, FAKE, FAKE, 2048, None) == BL_ERR_SHAPE
+    assert f(FAKE, 16, 0, FAKE, FAKE, FAKE, 2048, None) == BL_ERR_SHAPE
+    assert f(FAKE, 1 << 31, 64, FAKE, FAKE, FAKE, 2048, None) == BL_ERR_SHAPE
+    assert f(FAKE + 4, 16, 64, FAKE, FAKE, FAKE, 2048, None) == BL_ERR_ALIGN
+    assert f(FAKE, 16, 64, FAKE + 8, FAKE, FAKE, 2048, None) == BL_ERR_ALIGN
+    assert f(FAKE, 16, 64, FAKE, FAKE, FAKE, 2047, None) == BL_ERR_WORKSPACE
+
+
+def test_quant_act_validation():
+    f = lib.bl_quant_act
+    assert f(None, 1, 64, FAKE, FAKE, None) == BL_ERR_NULL
+    assert f(None, 0, 64, None, None, None) == BL_OK  # empty: pointers may be NULL
+    assert f(FAKE, -1, 64, FAKE, FAKE, None) == BL_ERR_SHAPE
+    assert f(FAKE, 1, 100, FAKE, FAKE, None) == BL_ERR_SHAPE
+    assert f(FAKE, (1 << 24) + 1, 64, FAKE, FAKE, None) == BL_ERR_SHAPE
+    assert f(FAKE + 2, 1, 64, FAKE, FAKE, None) == BL_ERR_ALIGN
+    assert f(FAKE, 1, 64, FAKE, FAKE + 2, None) == BL_ERR_ALIGN
+    assert f(FAKE, 0, 64, FAKE, FAKE, None) == BL_OK  # empty: nothing enqueued
+
+
+def test_linear_validation():
+    f = lib.bl_linear
+    args = dict(packed=FAKE, gamma=FAKE, xq=FAKE, alpha=FAKE, m=1, n=16, k=64, acc=FAKE, y=FAKE, stream=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["packed"], a["gamma"], a["xq"], a["alpha"], a["m"], a["n"], a["k"], a["acc"], a["y"], a["stream"])
+
+    assert call(packed=None) == BL_ERR_NULL
+    assert call(alpha=None) == BL_ERR_NULL
+    assert call(acc=None, y=None) == BL_ERR_NULL
+    assert call(k=32) == BL_ERR_SHAPE
+    assert call(k=(1 << 22) + 64) == BL_ERR_SHAPE
+    assert call(n=-1) == BL_ERR_SHAPE
+    assert call(m=1 << 20, n=1 << 21) == BL_ERR_SHAPE  # m*n >= 2^40
+    assert call(xq=FAKE + 8) == BL_ERR_ALIGN
+    assert call(acc=FAKE + 2) == BL_ERR_ALIGN
+    assert call(y=FAKE + 1) == BL_ERR_ALIGN
+    assert call(m=0) == BL_OK
+    assert call(n=0) == BL_OK
+    assert call(m=0, packed=None, xq=None) == BL_OK
+
+
+def test_unpack_validation():
+    f = lib.bl_unpack_ternary
+    assert f(None, 16, 64, FAKE, None) == BL_ERR_NULL
+    assert f(FAKE, 16, 65, FAKE, None) == BL_ERR_SHAPE
+    assert f(FAKE + 1, 16, 64, FAKE, None) == BL_ERR_ALIGN
+    assert f(FAKE, 0, 64, FAKE, None) == BL_OK
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="only where no GPU is visible")
+def test_launch_failure_maps_to_hip_error_without_a_device():
+    # Valid arguments, but the HIP runtime has no device to launch on.
+    assert lib.bl_quant_act(FAKE, 1, 64, FAKE, FAKE, None) == BL_ERR_HIP
+
+
+def test_python_binding_rejects_host_tensors():
+    with pytest.raises(ValueError):
+        bl.bl_quant_act(torch.zeros((1, 64), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        bl.bl_ternarize_pack(torch.zeros((16, 64), dtype=torch.float32))

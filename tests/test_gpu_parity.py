@@ -1,0 +1,293 @@
+"""GPU parity: every C-ABI entry point against the CPU oracle on the same seeded inputs.
+
+Bar: bytes, trits, int8 activations and int32 accumulators bit-exact; gamma
+and alpha bit-exact (fp32 values the method rounds once); bf16 outputs within
+one bf16 ulp of the oracle's (relative <= 7.8e-3), with exact zeros kept.
+Shapes span several 16x64 tiles, ragged row counts and K tails that do not
+fill a 1 KiB group; the workload cases use the BitNet b1.58 2B- and 70B-shaped
+layers at full size (sampled outputs where the oracle would take minutes).
+"""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+import ternary_weight_absmean_amd as bl
+from _gpu import DEV, assert_bf16_within_one_ulp, bf16, f32, host, i8, say, u8
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - collected only where a GPU exists
+    pytest.skip("no GPU visible", allow_module_level=True)
+
+
+def valid_bytes():
+    return np.array([a | (b << 2) | (c << 4) | (d << 6) for a in range(3) for b in range(3)
+                     for c in range(3) for d in range(3)], np.uint8)
+
+
+# ---------------------------------------------------------------- quantizer
+
+
+def check_quant(x_bits):
+    m, k = x_bits.shape
+    say(f"bl_quant_act m={m} k={k}")
+    xq, alpha = bl.bl_quant_act(bf16(x_bits))
+    want_q, want_a = oracle.quant_act(x_bits)
+    np.testing.assert_array_equal(host(xq), want_q)
+    np.testing.assert_array_equal(host(alpha).view(np.uint32), want_a.view(np.uint32))
+
+
+@pytest.mark.parametrize("m,k", [(1, 64), (2, 128), (3, 192), (17, 320), (100, 2560), (5, 6912)])
+def test_quant_small_and_ragged(m, k):
+    rng = np.random.default_rng(m * 7 + k)
+    x = datagen.f32_to_bf16(rng.standard_normal((m, k)) * 10.0 ** rng.uniform(-4, 4, size=(m, 1)))
+    check_quant(x)
+
+
+def test_quant_edge_rows():
+    k = 128
+    rows = [np.zeros(k), np.full(k, -3.0), np.linspace(-127, 127, k), np.full(k, 1e-30)]
+    tie = np.zeros(k)
+    tie[:7] = [127, 2.5, -3.5, 0.5, -0.5, 1.5, -1.5]  # s = 1: ties go to even
+    rows.append(tie)
+    big = np.zeros(k)
+    big[3] = -3.0e38
+    big[4] = 1.0
+    rows.append(big)
+    check_quant(datagen.f32_to_bf16(np.array(rows)))
+
+
+@pytest.mark.parametrize("m,k", [(1, 2560), (64, 6912), (16, 8192), (1, 28672), (2048, 2560), (1024, 28672)])
+def test_quant_workload_widths(m, k):
+    n_out = 8 if k in (2560, 6912) else datagen.n_outliers_70b(k)
+    mult = 20.0 if k in (2560, 6912) else 30.0
+    wl = datagen.WORKLOAD_STACK_2B if k in (2560, 6912) else datagen.WORKLOAD_70B
+    cols = datagen.outlier_columns(wl, k, n_out)
+    check_quant(datagen.activations_bf16(datagen.stream_id(wl, 0, 0, 1) + k, m, k, cols, mult))
+
+
+# ---------------------------------------------------------------- weight packer
+
+
+def check_pack(w):
+    n, k = w.shape
+    say(f"bl_ternarize_pack n={n} k={k}")
+    packed, gamma = bl.bl_ternarize_pack(f32(w))
+    want_packed, want_gamma = oracle.ternarize_pack(w)
+    got_gamma = host(gamma)
+    assert got_gamma.view(np.uint32)[0] == np.float32(want_gamma).view(np.uint32), (got_gamma[0], want_gamma)
+    got = host(packed)
+    assert got.size == want_packed.size
+    mism = np.nonzero(got != want_packed)[0]
+    assert mism.size == 0, f"{mism.size} packed bytes differ, first at {mism[:5]}"
+    return packed
+
+
+@pytest.mark.parametrize("n,k", [(1, 64), (5, 128), (16, 64), (17, 192), (40, 320), (33, 2560)])
+def test_pack_small_and_ragged(n, k):
+    rng = np.random.default_rng(n * 31 + k)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    # weights exactly on the rounding boundaries +-0.5 * (gamma + eps) and +-1.5 * (gamma + eps)
+    g = oracle.absmean(w)
+    d = np.float32(g + np.float32(1e-5))
+    w.ravel()[1:5] = [d * np.float32(0.5), -d * np.float32(0.5), d * np.float32(1.5), np.nextafter(d * np.float32(0.5), 1)]
+    check_pack(w)
+
+
+def test_pack_gamma_exotic_values():
+    rng = np.random.default_rng(4)
+    cases = [
+        np.full((16, 64), 0.02, np.float32),                                   # constant magnitude
+        np.where(rng.random((16, 64)) < 0.5, -1.0, 1.0).astype(np.float32) * np.float32(3e-39),  # subnormal
+        np.concatenate([np.full((1, 64), 2.0 ** 25, np.float32), np.ones((15, 64), np.float32)]),
+        (rng.standard_normal((32, 128)) * 10.0 ** rng.uniform(-30, 30, size=(32, 128))).astype(np.float32),
+        np.zeros((16, 64), np.float32),
+    ]
+    for w in cases:
+        check_pack(w)
+
+
+def test_unpack_helper_matches_oracle_and_all_byte_patterns():
+    rng = np.random.default_rng(8)
+    n, k = 37, 320
+    buf = rng.choice(valid_bytes(), size=oracle.packed_bytes(n, k))
+    buf[:81] = valid_bytes()
+    say("bl_unpack_ternary")
+    q = bl.bl_unpack_ternary(u8(buf), n, k)
+    np.testing.assert_array_equal(host(q), oracle.unpack(buf, n, k))
+
+
+def test_pack_workload_2b_stack_layer0():
+    for pi, (name, k, n) in enumerate(datagen.STACK_2B_PROJ):
+        w = datagen.weights(datagen.stream_id(datagen.WORKLOAD_STACK_2B, 0, pi, datagen.TENSOR_W), n, k)
+        check_pack(w)
+
+
+def test_pack_workload_single_2560():
+    check_pack(datagen.weights(datagen.stream_id(datagen.WORKLOAD_SINGLE, 0, 0, datagen.TENSOR_W), 2560, 2560))
+
+
+@pytest.mark.parametrize("proj", [0, 1])
+def test_pack_workload_70b_layer(proj):
+    name, k, n = datagen.LAYER_70B_PROJ[proj]
+    w = datagen.weights(datagen.stream_id(datagen.WORKLOAD_70B, 0, proj, datagen.TENSOR_W), n, k)
+    check_pack(w)
+
+
+def test_pack_is_deterministic():
+    w = datagen.weights(77, 3840, 2560)
+    say("bl_ternarize_pack twice")
+    p1, g1 = bl.bl_ternarize_pack(f32(w))
+    p2, g2 = bl.bl_ternarize_pack(f32(w))
+    assert torch.equal(p1, p2) and torch.equal(g1, g2)
+
+
+# ---------------------------------------------------------------- product
+
+
+def check_linear(packed_dev, gamma_dev, qw, gamma_host, x_bits=None, xq_np=None, alpha_np=None, rows=None,
+                 toks=None):
+    """Run bl_linear on device inputs; compare acc exactly and y within 1 ulp
+    with the oracle on the (optionally sampled) token rows / output columns."""
+    n, k = qw.shape
+    if x_bits is not None:
+        xq_np, alpha_np = oracle.quant_act(x_bits)
+        xq_dev, alpha_dev = bl.bl_quant_act(bf16(x_bits))
+    else:
+        xq_dev, alpha_dev = i8(xq_np), f32(alpha_np)
+    m = xq_np.shape[0]
+    say(f"bl_linear m={m} n={n} k={k}")
+    acc, y = bl.bl_linear(packed_dev, gamma_dev, xq_dev, alpha_dev, n)
+    acc_h, y_h = host(acc), host(y)
+    toks = np.arange(m) if toks is None else toks
+    rows = np.arange(n) if rows is None else rows
+    want_acc = oracle.linear_mul(qw[rows], xq_np[toks])
+    np.testing.assert_array_equal(acc_h[np.ix_(toks, rows)], want_acc)
+    want_y = oracle.rescale(want_acc, gamma_host, alpha_np[toks])
+    assert_bf16_within_one_ulp(y_h[np.ix_(toks, rows)], want_y)
+    # the y-only and acc-only forms write the same values
+    _, y2 = bl.bl_linear(packed_dev, gamma_dev, xq_dev, alpha_dev, n, acc=False)
+    acc2, _ = bl.bl_linear(packed_dev, gamma_dev, xq_dev, alpha_dev, n, y=False)
+    assert torch.equal(y2.view(torch.int16), y.view(torch.int16)) and torch.equal(acc2, acc)
+    return acc_h, y_h
+
+
+def random_layer(rng, n, k):
+    """Random valid packed buffer (seeded test input) and its trits per the oracle."""
+    buf = rng.choice(valid_bytes(), size=oracle.packed_bytes(n, k)).astype(np.uint8)
+    return buf, oracle.unpack(buf, n, k)
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 5, 16, 17, 33, 64, 65, 100])
+@pytest.mark.parametrize("n,k", [(1, 64), (7, 128), (31, 192), (33, 320), (48, 1024), (20, 1088)])
+def test_linear_brute_force_shapes(m, n, k):
+    rng = np.random.default_rng(1000 * m + 10 * n + k)
+    buf, qw = random_layer(rng, n, k)
+    xq = rng.integers(-128, 128, size=(m, k)).astype(np.int8)
+    xq[0, : min(k, 8)] = [127, -128, -127, 0, 1, -1, 127, -128][: min(k, 8)]
+    alpha = datagen.bf16_to_f32(datagen.f32_to_bf16(rng.uniform(0.1, 50, size=m)))
+    gamma = np.float32(0.0159)
+    check_linear(u8(buf), f32(np.array([gamma])), qw, gamma, xq_np=xq, alpha_np=alpha)
+
+
+def test_linear_extremes():
+    k, n, m = 6912, 48, 4
+    qw = np.ones((n, k), np.int8)
+    qw[16:32] = -1
+    qw[32:, ::3] = 0
+    xq = np.full((m, k), 127, np.int8)
+    xq[1] = -128
+    xq[2] = 0
+    xq[3, ::2] = -127
+    packed = oracle.pack(qw)
+    alpha = np.array([127.0, 128.0, 0.0, 99.0], np.float32)
+    gamma = np.float32(0.03)
+    acc, y = check_linear(u8(packed), f32(np.array([gamma])), qw, gamma, xq_np=xq, alpha_np=alpha)
+    assert acc[0, 0] == 127 * k and acc[1, 20] == 128 * k and (acc[2] == 0).all()
+
+
+def test_linear_large_k_accumulator_range():
+    k, n, m = 1 << 20, 16, 2
+    qw = np.ones((n, k), np.int8)
+    qw[8:] = -1
+    xq = np.full((m, k), 127, np.int8)
+    xq[1] = -128
+    gamma = np.float32(1e-3)
+    alpha = np.array([1.0, 2.0], np.float32)
+    acc, _ = check_linear(u8(oracle.pack(qw)), f32(np.array([gamma])), qw, gamma, xq_np=xq, alpha_np=alpha)
+    assert acc[1, 0] == -128 * k and acc[1, 15] == 128 * k
+
+
+def test_linear_empty_is_a_noop():
+    buf = u8(np.full(oracle.packed_bytes(16, 64), 0x55, np.uint8))
+    g = f32(np.array([1.0]))
+    acc, y = bl.bl_linear(buf, g, i8(np.zeros((0, 64))), f32(np.zeros(0)), 16)
+    assert acc.shape == (0, 16) and y.shape == (0, 16)
+    acc = torch.full((2, 0), 7, dtype=torch.int32, device=DEV)
+    bl.bl_linear(buf, g, i8(np.zeros((2, 64))), f32(np.zeros(2)), 0, acc=acc, y=False)
+
+
+def workload_case(workload, proj, k, n, m, outliers, mult, layer=0, sample=None):
+    """Pack seeded weights on the GPU (gamma and bytes checked against the
+    oracle), quantize seeded activations on the GPU, and compare the product."""
+    w = datagen.weights(datagen.stream_id(workload, layer, proj, datagen.TENSOR_W), n, k)
+    packed_dev = check_pack(w)
+    gamma = oracle.absmean(w)
+    qw = oracle.ternarize(w, gamma)
+    del w
+    cols = datagen.outlier_columns(workload, k, outliers)
+    x = datagen.activations_bf16(datagen.stream_id(workload, layer, proj, datagen.TENSOR_X) + 7 * m, m, k, cols, mult)
+    rows = toks = None
+    if sample is not None:
+        rng = np.random.default_rng(m + n)
+        toks = np.sort(rng.choice(m, size=min(m, sample[0]), replace=False))
+        rows = np.sort(rng.choice(n, size=min(n, sample[1]), replace=False))
+    gamma_dev = f32(np.array([gamma]))
+    check_linear(packed_dev, gamma_dev, qw, gamma, x_bits=x, rows=rows, toks=toks)
+
+
+def test_linear_workload_single_2560_decode():
+    workload_case(datagen.WORKLOAD_SINGLE, 0, 2560, 2560, 1, 0, 1.0)
+
+
+@pytest.mark.parametrize("m", [1, 4, 16, 64])
+def test_linear_workload_2b_stack_layer0(m):
+    for pi, (name, k, n) in enumerate(datagen.STACK_2B_PROJ):
+        workload_case(datagen.WORKLOAD_STACK_2B, pi, k, n, m, datagen.STACK_2B_OUTLIERS if m == 1 else 0,
+                      datagen.STACK_2B_OUTLIER_MULT)
+
+
+def test_linear_workload_2b_stack_last_layer_decode():
+    for pi, (name, k, n) in enumerate(datagen.STACK_2B_PROJ):
+        workload_case(datagen.WORKLOAD_STACK_2B, pi, k, n, 1, datagen.STACK_2B_OUTLIERS,
+                      datagen.STACK_2B_OUTLIER_MULT, layer=datagen.STACK_2B_LAYERS - 1)
+
+
+@pytest.mark.parametrize("proj", [2, 3])
+def test_linear_workload_2b_prefill_2048(proj):
+    name, k, n = datagen.STACK_2B_PROJ[proj]
+    workload_case(datagen.WORKLOAD_STACK_2B, proj, k, n, 2048, datagen.STACK_2B_OUTLIERS,
+                  datagen.STACK_2B_OUTLIER_MULT, sample=(96, 512))
+
+
+@pytest.mark.parametrize("proj", [0, 1])
+@pytest.mark.parametrize("m", [1, 16, 1024])
+def test_linear_workload_70b(proj, m):
+    name, k, n = datagen.LAYER_70B_PROJ[proj]
+    sample = None if m == 1 else (16, 2048) if m == 16 else (48, 512)
+    workload_case(datagen.WORKLOAD_70B, proj, k, n, m, datagen.n_outliers_70b(k), datagen.LAYER_70B_OUTLIER_MULT,
+                  sample=sample)
+
+
+def test_linear_is_deterministic():
+    rng = np.random.default_rng(3)
+    buf, qw = random_layer(rng, 3840, 2560)
+    xq = i8(rng.integers(-127, 128, size=(5, 2560)))
+    a = f32(np.ones(5))
+    g = f32(np.array([0.01]))
+    say("bl_linear twice")
+    acc1, y1 = bl.bl_linear(u8(buf), g, xq, a, 3840)
+    acc2, y2 = bl.bl_linear(u8(buf), g, xq, a, 3840)
+    assert torch.equal(acc1, acc2) and torch.equal(y1.view(torch.int16), y2.view(torch.int16))
