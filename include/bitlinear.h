@@ -116,6 +116,20 @@ bl_status bl_quant_act(const uint16_t* x, int64_t m, int64_t k, int8_t* xq, floa
 bl_status bl_linear(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha,
                     int64_t m, int64_t n, int64_t k, int32_t* acc, uint16_t* y, void* stream);
 
+/* The whole layer in one call [P1, P2, P3]: per-token absmax int8
+ * quantization of x followed by the ternary product and rescale, with exactly
+ * the results of bl_quant_act followed by bl_linear.  For m <= 16 tokens whose
+ * int8 rows fit on chip (m * (k + 16) <= 33024 bytes) a single kernel does
+ * both steps (each workgroup quantizes the token block it multiplies);
+ * otherwise the two kernels run back to back on `stream`.
+ *   x      [m][k] bf16 (raw 16-bit patterns), read only.
+ *   xq     out [m][k] int8 (the quantized activations; also used as staging).
+ *   alpha  out [m] fp32 (per-token absmax).
+ *   acc, y as in bl_linear (either may be NULL, not both).
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_HIP. */
+bl_status bl_bitlinear(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t n, int64_t k,
+                       int8_t* xq, float* alpha, int32_t* acc, uint16_t* y, void* stream);
+
 /* Unpack a packed buffer back to trits (test and inspection helper [P2]):
  * q[j][t] in {-1, 0, 1} for the n real rows.  A code 3 (never produced by
  * bl_ternarize_pack) decodes as 0.

@@ -20,7 +20,7 @@ from ._build import LIB_PATH, INCLUDE
 
 __all__ = [
     "BitLinearError", "bl_packed_bytes", "bl_ternarize_pack_workspace_bytes", "bl_ternarize_pack",
-    "bl_quant_act", "bl_linear", "bl_unpack_ternary", "bl_status_string", "library", "declared_symbols",
+    "bl_quant_act", "bl_linear", "bl_bitlinear", "bl_unpack_ternary", "bl_status_string", "library", "declared_symbols",
 ]
 
 
@@ -47,6 +47,8 @@ _lib.bl_quant_act.argtypes = [_P, _I64, _I64, _P, _P, _P]
 _lib.bl_quant_act.restype = ctypes.c_int
 _lib.bl_linear.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P]
 _lib.bl_linear.restype = ctypes.c_int
+_lib.bl_bitlinear.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]
+_lib.bl_bitlinear.restype = ctypes.c_int
 _lib.bl_unpack_ternary.argtypes = [_P, _I64, _I64, _P, _P]
 _lib.bl_unpack_ternary.restype = ctypes.c_int
 _lib.bl_status_string.argtypes = [ctypes.c_int]
@@ -158,6 +160,38 @@ def bl_linear(packed: torch.Tensor, gamma: torch.Tensor, xq: torch.Tensor, alpha
     _check("bl_linear", _lib.bl_linear(_ptr(packed), _ptr(gamma), _ptr(xq), _ptr(alpha), m, n, k, _ptr(acc), _ptr(y),
                                        _stream(dev)))
     return acc, y
+
+
+def bl_bitlinear(packed: torch.Tensor, gamma: torch.Tensor, x: torch.Tensor, n: int,
+                 xq: torch.Tensor | None = None, alpha: torch.Tensor | None = None,
+                 acc: torch.Tensor | None | bool = True, y: torch.Tensor | None | bool = True):
+    """bf16 activations ``[m][k]`` through the whole layer in one call:
+    returns (acc or None, y or None, xq, alpha)."""
+    _need(x, "x", torch.bfloat16)
+    m, k = x.shape
+    dev = x.device
+    if xq is None:
+        xq = torch.empty((m, k), dtype=torch.int8, device=dev)
+    if alpha is None:
+        alpha = torch.empty(m, dtype=torch.float32, device=dev)
+    _need(xq, "xq", torch.int8, (m, k))
+    _need(alpha, "alpha", torch.float32, (m,))
+    if acc is True:
+        acc = torch.empty((m, n), dtype=torch.int32, device=dev)
+    if y is True:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    acc = acc if isinstance(acc, torch.Tensor) else None
+    y = y if isinstance(y, torch.Tensor) else None
+    if acc is not None:
+        _need(acc, "acc", torch.int32, (m, n))
+    if y is not None:
+        _need(y, "y", torch.bfloat16, (m, n))
+    _need(packed, "packed", torch.uint8)
+    if packed.numel() < bl_packed_bytes(n, k):
+        raise ValueError("packed buffer is smaller than bl_packed_bytes(n, k)")
+    _check("bl_bitlinear", _lib.bl_bitlinear(_ptr(packed), _ptr(gamma), _ptr(x), m, n, k, _ptr(xq), _ptr(alpha),
+                                             _ptr(acc), _ptr(y), _stream(dev)))
+    return acc, y, xq, alpha
 
 
 def bl_unpack_ternary(packed: torch.Tensor, n: int, k: int, q: torch.Tensor | None = None) -> torch.Tensor:

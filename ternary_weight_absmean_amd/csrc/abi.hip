@@ -67,6 +67,25 @@ bl_status bl_linear(const uint8_t* packed, const float* gamma, const int8_t* xq,
   return from_hip(bl::launch_gemm(packed, gamma, xq, alpha, m, n, k, acc, y, s));
 }
 
+bl_status bl_bitlinear(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t n, int64_t k,
+                       int8_t* xq, float* alpha, int32_t* acc, uint16_t* y, void* stream) {
+  if (m < 0 || m > BL_MAX_M || n < 0 || n > BL_MAX_N || !valid_k(k) || !product_ok(m, k) || !product_ok(n + 16, k) ||
+      !product_ok(m, n))
+    return BL_ERR_SHAPE;
+  if (m == 0) return BL_OK;  // empty tensors may carry NULL pointers
+  if (!x || !xq || !alpha || (n > 0 && (!packed || !gamma || (!acc && !y)))) return BL_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(alpha, 4) || (n > 0 && (!aligned(packed, 16) ||
+      !aligned(gamma, 4) || (acc && !aligned(acc, 4)) || (y && !aligned(y, 2)))))
+    return BL_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  if (n > 0 && m <= 16 && bl::gemv_fits_lds(m, k))
+    return from_hip(bl::launch_gemv_fused(packed, gamma, x, m, n, k, xq, alpha, acc, y, s));
+  hipError_t e = bl::launch_quant_act(x, m, k, xq, alpha, s);
+  if (e != hipSuccess || n == 0) return from_hip(e);
+  if (m <= 16) return from_hip(bl::launch_gemv(packed, gamma, xq, alpha, m, n, k, acc, y, s));
+  return from_hip(bl::launch_gemm(packed, gamma, xq, alpha, m, n, k, acc, y, s));
+}
+
 bl_status bl_unpack_ternary(const uint8_t* packed, int64_t n, int64_t k, int8_t* q, void* stream) {
   if (n < 0 || n > BL_MAX_N || !valid_k(k) || !product_ok(n + 16, k)) return BL_ERR_SHAPE;
   if (n == 0) return BL_OK;

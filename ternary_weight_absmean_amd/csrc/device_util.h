@@ -45,6 +45,23 @@ __device__ __forceinline__ v4i as_v4i(const uint4& u) {
   return r;
 }
 
+// Raw buffer resource over `bytes` bytes at `base` (stride 0).  Loads through
+// it return zero for any offset at or past `bytes` instead of touching memory,
+// so tails and absent operands need no branch (a load inside a divergent
+// branch is followed by its own wait, which serializes a batch of loads).
+// The descriptor must be wave-uniform; offsets are per lane.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t offset) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // v_mfma_i32_16x16x64_i8: D[16][16] += A[16][64] * B[64][16].  Lane l supplies
 // row l%16 of A and column l%16 of B, 16 int8 each, for the same 16 k-slots
 // (lane group l/16); D lands as rows 4*(l/16) + i, column l%16 in element i.

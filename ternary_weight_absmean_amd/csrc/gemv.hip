@@ -2,97 +2,67 @@
 //
 // deepmox.com chapter 8, "A low-bit model is a whole-stack design": decode
 // time goes to moving the weights; the GPU path keeps them packed at four
-// trits per byte, moves them on chip, unpacks and computes with the 8-bit
-// activations.  bako.co, "The BitLinear Layer and AbsMean Quantization": the
-// ternary product is integer add/subtract; here the unpacked trits feed the
-// int8 matrix cores, which perform exactly those integer sums (a trit of 0
-// contributes 0, +-1 adds or subtracts x).
+// trits per byte, moves them on chip, unpacks them and computes with the
+// 8-bit activations.  bako.co, "The BitLinear Layer and AbsMean Quantization":
+// the ternary product is integer add/subtract; here the unpacked values feed
+// the int8 matrix cores, which perform exactly those integer sums.
 //
-// The kernel is bound by HBM: every packed byte is read once, 0.25 byte per
-// weight, and nothing else is large.  Work decomposition:
-//   * one workgroup (4 waves) per 16-row tile of W and per 16-token block;
-//   * the waves split K: wave w takes 1 KiB groups w, w+4, ... (a group is
-//     four consecutive 16x64 tiles, contiguous in the packed layout), so each
+// The kernels are bound by HBM: every packed byte is read once (0.25 byte per
+// weight) and nothing else is large.  Work decomposition, shared by both:
+//   * one workgroup (4 waves) per 16-row tile of W and per block of up to 16
+//     tokens;
+//   * the waves split K: wave w takes 1 KiB groups w, w+4, ... (a group is four
+//     consecutive 16x64 tiles, contiguous in the packed layout), so each
 //     wave-wide 128-bit load reads 1 KiB of HBM with no gaps;
-//   * lane l holds row l%16 of tile (4*group + l/16): 16 bytes = 64 trits;
-//     field f of those bytes is columns 16f..16f+15 of that tile, turned into
-//     signed int8 with one v_perm per 4 trits, and multiplied with the same 16
-//     activation bytes (one 128-bit load) in v_mfma_i32_16x16x64_i8, whose
+//   * lane l holds row l%16 of tile (4*group + l/16): 16 bytes = 64 trits.
+//     Field f (bits 2f..2f+1 of each byte) is columns 16f..16f+15 of the tile,
+//     multiplied in v_mfma_i32_16x16x64_i8 with the same 16 activation bytes;
 //     B column l%16 is token l%16 of the block;
-//   * the waves' 16x16 int32 partial sums are added in LDS (integer, so the
-//     order does not matter) and wave 0 applies the epilogue
-//     y = bf16(acc * gamma * alpha / 127).
-// Loads for a batch of kGroupsPerBatch groups are issued before any of them
-// is consumed, keeping several KiB per wave in flight.
+//   * the waves' 16x16 int32 partial sums are added in LDS (integer, order-free)
+//     and wave 0 applies the epilogue y = bf16(acc * gamma * alpha / 127).
+//
+// k_bitlinear_fused (the whole layer, m_blk * (k + 16) <= 33 KiB) quantizes the
+// bf16 tokens itself (per-token absmax, identical arithmetic to bl_quant_act)
+// into LDS and feeds the MFMA with the raw codes c = q + 1, correcting with the
+// token's activation sum: sum q*x = sum c*x - sum x.  The codes need no table:
+// masking a byte with 0x03, 0x0C, 0x30 gives 1, 4 and 16 times fields 0, 1, 2,
+// and (b >> 2) & 0x30 gives 16 times field 3, so four independent accumulators
+// hold c*x scaled by 1, 4, 16, 16 and are divided exactly at the end (20 VALU
+// ops per 1 KiB group instead of 44 for a signed table lookup).
+//
+// k_gemv_direct (bl_linear: int8 activations given) reads activation bytes
+// straight from global memory and converts codes to signed trits with v_perm.
 #include "device_util.h"
 #include "internal.h"
 
 namespace bl {
 namespace {
 
-constexpr int kGemvWaves = 4;
-constexpr int kGemvThreads = kGemvWaves * 64;
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
 constexpr int kGroupsPerBatch = 4;
+constexpr int kLdsStageBytes = 33024;  // 16-token rows of up to 2 KiB, or one row of 32 KiB
+constexpr int kLdsRowPad = 16;          // row stride k + 16 bytes spreads the 16 token rows over the banks
 
-__global__ __launch_bounds__(kGemvThreads) void k_gemv(const uint4* __restrict__ packed,
-                                                       const float* __restrict__ gamma_ptr,
-                                                       const int8_t* __restrict__ xq,
-                                                       const float* __restrict__ alpha, int64_t m, int64_t n,
-                                                       int64_t k, int32_t* __restrict__ acc_out,
-                                                       uint16_t* __restrict__ y_out) {
-  __shared__ v4i partial[kGemvWaves][64];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t row_tile = blockIdx.x;
-  const int64_t tok0 = (int64_t)blockIdx.y * 16;
-  const int64_t kt_count = k / kTileCols;
-  const int64_t groups = (kt_count + 3) / 4;
-  const int sub = lane >> 4;   // tile within a group
-  const int col = lane & 15;   // A row (weight row) and B column (token)
-  const int64_t tok = tok0 + col;
-  const bool has_tok = tok < m;
-  const uint4* wbase = packed + row_tile * kt_count * (kTileBytes / 16);
-  const uint4* xrow = reinterpret_cast<const uint4*>(xq + (has_tok ? tok : 0) * k);
+__device__ __forceinline__ v4i mask4(const uint4& a, uint32_t mask, int shift) {
+  v4i r;
+  r.x = (int)((a.x >> shift) & mask);
+  r.y = (int)((a.y >> shift) & mask);
+  r.z = (int)((a.z >> shift) & mask);
+  r.w = (int)((a.w >> shift) & mask);
+  return r;
+}
 
-  v4i acc = {0, 0, 0, 0};
-  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-  for (int64_t g0 = wave; g0 < groups; g0 += (int64_t)kGemvWaves * kGroupsPerBatch) {
-    uint4 a[kGroupsPerBatch];
-    uint4 b[kGroupsPerBatch][4];
-#pragma unroll
-    for (int u = 0; u < kGroupsPerBatch; ++u) {
-      const int64_t g = g0 + (int64_t)u * kGemvWaves;
-      const int64_t kt = 4 * g + sub;
-      const bool valid = g < groups && kt < kt_count;
-      a[u] = zero;
-      if (valid) a[u] = wbase[4 * g * 16 + lane];
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        b[u][f] = zero;
-        if (valid && has_tok) b[u][f] = xrow[kt * 4 + f];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kGroupsPerBatch; ++u) {
-#pragma unroll
-      for (int f = 0; f < 4; ++f) acc = mfma_16x16x64(unpack_field(a[u], f), as_v4i(b[u][f]), acc);
-    }
-  }
-  partial[wave][lane] = acc;
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int w = 1; w < kGemvWaves; ++w) {
-    v4i p = partial[w][lane];
-    acc.x += p.x;
-    acc.y += p.y;
-    acc.z += p.z;
-    acc.w += p.w;
-  }
-  if (!has_tok) return;
-  // lane holds rows 4*(lane/16) + i of the tile for token `tok`
-  const float scale = (*gamma_ptr * alpha[tok]) / 127.0f;
-  const int64_t row0 = row_tile * kTileRows + 4 * sub;
+__device__ __forceinline__ void add4(v4i& a, const v4i& b) {
+  a.x += b.x;
+  a.y += b.y;
+  a.z += b.z;
+  a.w += b.w;
+}
+
+// Epilogue for wave 0: lane holds rows 4*(lane/16) + i of the tile, token `tok`.
+__device__ __forceinline__ void store_tile(const v4i& acc, int64_t row0, int64_t tok, int64_t n, float scale,
+                                           int32_t* __restrict__ acc_out, uint16_t* __restrict__ y_out) {
   const int vals[4] = {acc.x, acc.y, acc.z, acc.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -104,19 +74,284 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(const uint4* __restrict__
   }
 }
 
+__device__ __forceinline__ uint32_t max_abs_bf16x8(const uint4& v) {
+  uint32_t m = max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu);
+  m = max(m, max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu));
+  m = max(m, max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu));
+  return max(m, max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu));
+}
+
+// round-half-even(fl32(x * s)) clamped to int8, for the two bf16 in a dword
+__device__ __forceinline__ uint32_t quant2(uint32_t two_bf16, float s, int& sum) {
+  float lo = __uint_as_float(two_bf16 << 16);
+  float hi = __uint_as_float(two_bf16 & 0xFFFF0000u);
+  int ql = (int)fminf(fmaxf(__builtin_rintf(__fmul_rn(lo, s)), -128.0f), 127.0f);
+  int qh = (int)fminf(fmaxf(__builtin_rintf(__fmul_rn(hi, s)), -128.0f), 127.0f);
+  sum += ql + qh;
+  return ((uint32_t)ql & 0xFFu) | (((uint32_t)qh & 0xFFu) << 8);
+}
+
+// Partial reduction of `v` over the `g = min(tpr, 64)` lanes of a token row
+// group inside one wave; lanes with (tid % g) == 0 then write the group's value
+// to scratch[tid / g].  A row's value is the max/sum of its tpr/g entries.
+template <bool kMax>
+__device__ __forceinline__ void group_partial(int v, int tpr, int* scratch) {
+  const int g = tpr < 64 ? tpr : 64;
+  for (int off = g >> 1; off > 0; off >>= 1) {
+    int o = __shfl_xor(v, off, 64);
+    v = kMax ? max(v, o) : v + o;
+  }
+  if ((threadIdx.x % g) == 0) scratch[threadIdx.x / g] = v;
+}
+
+template <bool kMax>
+__device__ __forceinline__ int row_total(int row, int tpr, const int* scratch) {
+  const int g = tpr < 64 ? tpr : 64;
+  const int per_row = tpr / g;  // 1..4 entries per row
+  int r = scratch[row * per_row];
+  for (int i = 1; i < per_row; ++i) r = kMax ? max(r, scratch[row * per_row + i]) : r + scratch[row * per_row + i];
+  return r;
+}
+
+constexpr int kXRegChunks = 4;  // bf16 chunks of 8 held in registers between the two quantizer passes
+
+// Whole BitLinear for a block of up to 16 tokens: per-token absmax int8
+// quantization (same arithmetic as bl_quant_act) into LDS, then the codes x
+// int8 product with four scaled accumulators, then the bf16 rescale.
+// Latency-ordered: the weight loads and the activation loads are issued first;
+// the absmax, the activation sum and the waves' partial products each take one
+// LDS round (three barriers in all).
+__global__ __launch_bounds__(kThreads) void k_bitlinear_fused(const uint4* __restrict__ packed,
+                                                              const float* __restrict__ gamma_ptr,
+                                                              const uint4* __restrict__ x, float* __restrict__ alpha,
+                                                              int8_t* __restrict__ xq_out, int64_t m, int64_t n,
+                                                              int64_t k, int32_t* __restrict__ acc_out,
+                                                              uint16_t* __restrict__ y_out) {
+  extern __shared__ uint4 xs_raw[];  // [rows][k + kLdsRowPad] int8 activations of this token block
+  int8_t* xs = reinterpret_cast<int8_t*>(xs_raw);
+  __shared__ v4i partial[kWaves][64];
+  __shared__ int red_max[kThreads / 16];
+  __shared__ int red_sum[kThreads / 16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t row_tile = blockIdx.x;
+  const int64_t tok0 = (int64_t)blockIdx.y * 16;
+  const int rows = (int)min((int64_t)16, m - tok0);
+  const int64_t kt_count = k / kTileCols;
+  const int64_t groups = (kt_count + 3) / 4;
+  const int sub = lane >> 4;
+  const int col = lane & 15;
+  const uint4* wbase = packed + row_tile * kt_count * (kTileBytes / 16);
+  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+
+  // ---- quantize the token block into LDS.  The activation loads are issued
+  // before the weight loads: loads retire in order, so the quantizer then waits
+  // only for the activations while the weights are still in flight.
+  int rp = 1;
+  while (rp < rows) rp <<= 1;
+  const int tpr = kThreads / rp;  // threads per token row
+  const int my_row = tid / tpr;
+  const int j0 = tid % tpr;
+  const bool row_ok = my_row < rows;
+  const int64_t k8 = k / 8;
+  const int64_t ldx = k + kLdsRowPad;
+  const uint4* xb = x + (tok0 + (row_ok ? my_row : 0)) * k8;
+  const __amdgpu_buffer_rsrc_t xrsrc = buffer_rsrc(x + tok0 * k8, (uint32_t)(rows * k8 * 16));
+  const bool cached = (k8 + tpr - 1) / tpr <= kXRegChunks;
+  uint4 xr[kXRegChunks];
+  if (cached) {
+#pragma unroll
+    for (int c = 0; c < kXRegChunks; ++c) {
+      const int64_t i = j0 + (int64_t)c * tpr;
+      xr[c] = buffer_load16(xrsrc, row_ok && i < k8 ? (uint32_t)((my_row * k8 + i) * 16) : kOutOfRange);
+    }
+  }
+  // weights: the resource spans this row tile; offsets past its last 16x64
+  // tile (tail groups, groups beyond this wave's share) read as zero codes,
+  // which contribute nothing to the products
+  const __amdgpu_buffer_rsrc_t wrsrc = buffer_rsrc(wbase, (uint32_t)(kt_count * kTileBytes));
+  uint4 a_cur[kGroupsPerBatch];
+#pragma unroll
+  for (int u = 0; u < kGroupsPerBatch; ++u)
+    a_cur[u] = buffer_load16(wrsrc, (uint32_t)((wave + u * kWaves) * 1024 + lane * 16));
+  uint32_t mx = 0;
+  if (cached) {
+#pragma unroll
+    for (int c = 0; c < kXRegChunks; ++c) mx = max(mx, max_abs_bf16x8(xr[c]));
+  } else if (row_ok) {
+    for (int64_t i = j0; i < k8; i += tpr) mx = max(mx, max_abs_bf16x8(xb[i]));
+  }
+  group_partial<true>((int)mx, tpr, red_max);
+  __syncthreads();
+  const float amax = __uint_as_float((uint32_t)row_total<true>(my_row < rp ? my_row : 0, tpr, red_max) << 16);
+  const float s = 127.0f / fmaxf(amax, 1e-5f);  // IEEE division, as in bl_quant_act
+  int sum = 0;
+  if (row_ok) {
+    uint2* dst = reinterpret_cast<uint2*>(xs + (int64_t)my_row * ldx);
+    uint2* gdst = (blockIdx.x == 0 && xq_out) ? reinterpret_cast<uint2*>(xq_out + (tok0 + my_row) * k) : nullptr;
+    if (cached) {
+#pragma unroll
+      for (int c = 0; c < kXRegChunks; ++c) {
+        const int64_t i = j0 + (int64_t)c * tpr;
+        if (i < k8) {
+          const uint2 q = make_uint2(quant2(xr[c].x, s, sum) | (quant2(xr[c].y, s, sum) << 16),
+                                     quant2(xr[c].z, s, sum) | (quant2(xr[c].w, s, sum) << 16));
+          dst[i] = q;
+          if (gdst) gdst[i] = q;
+        }
+      }
+    } else {
+      for (int64_t i = j0; i < k8; i += tpr) {
+        const uint4 v = xb[i];
+        const uint2 q = make_uint2(quant2(v.x, s, sum) | (quant2(v.y, s, sum) << 16),
+                                   quant2(v.z, s, sum) | (quant2(v.w, s, sum) << 16));
+        dst[i] = q;
+        if (gdst) gdst[i] = q;
+      }
+    }
+    if (j0 == 0 && blockIdx.x == 0 && alpha) alpha[tok0 + my_row] = amax;
+  }
+  group_partial<false>(sum, tpr, red_sum);
+  __syncthreads();
+
+  // ---- K loop: codes times activations, four scaled accumulators
+  const bool has_tok = col < rows;
+  const int8_t* xrow = xs + (int64_t)(has_tok ? col : 0) * ldx;
+  v4i acc1 = {0, 0, 0, 0}, acc4 = acc1, acc16a = acc1, acc16b = acc1;
+  for (int64_t g0 = wave; g0 < groups; g0 += (int64_t)kWaves * kGroupsPerBatch) {
+    uint4 a_next[kGroupsPerBatch];
+    const int64_t gn = g0 + (int64_t)kWaves * kGroupsPerBatch;
+#pragma unroll
+    for (int u = 0; u < kGroupsPerBatch; ++u)
+      a_next[u] = buffer_load16(wrsrc, (uint32_t)((gn + u * kWaves) * 1024 + lane * 16));
+#pragma unroll
+    for (int u = 0; u < kGroupsPerBatch; ++u) {
+      const int64_t g = g0 + (int64_t)u * kWaves;
+      // tiles past the end carry zero codes, so any in-bounds activation
+      // bytes will do: clamp to the last tile
+      const int64_t kt = min(4 * g + sub, kt_count - 1);
+      uint4 b[4];
+      const uint4* xt = reinterpret_cast<const uint4*>(xrow) + kt * 4;
+#pragma unroll
+      for (int f = 0; f < 4; ++f) b[f] = xt[f];
+      acc1 = mfma_16x16x64(mask4(a_cur[u], 0x03030303u, 0), as_v4i(b[0]), acc1);
+      acc4 = mfma_16x16x64(mask4(a_cur[u], 0x0C0C0C0Cu, 0), as_v4i(b[1]), acc4);
+      acc16a = mfma_16x16x64(mask4(a_cur[u], 0x30303030u, 0), as_v4i(b[2]), acc16a);
+      acc16b = mfma_16x16x64(mask4(a_cur[u], 0x30303030u, 2), as_v4i(b[3]), acc16b);
+    }
+#pragma unroll
+    for (int u = 0; u < kGroupsPerBatch; ++u) a_cur[u] = a_next[u];
+  }
+  // exact: acc4 holds 4x, acc16a/b 16x the code sums
+  v4i part = acc1;
+  part.x += (acc4.x >> 2) + (acc16a.x >> 4) + (acc16b.x >> 4);
+  part.y += (acc4.y >> 2) + (acc16a.y >> 4) + (acc16b.y >> 4);
+  part.z += (acc4.z >> 2) + (acc16a.z >> 4) + (acc16b.z >> 4);
+  part.w += (acc4.w >> 2) + (acc16a.w >> 4) + (acc16b.w >> 4);
+  partial[wave][lane] = part;
+  __syncthreads();
+  if (wave != 0 || !has_tok) return;
+  v4i acc = partial[0][lane];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) add4(acc, partial[w][lane]);
+  const int xsum = row_total<false>(col, kThreads / rp, red_sum);  // sum q*x = sum c*x - sum x
+  acc.x -= xsum;
+  acc.y -= xsum;
+  acc.z -= xsum;
+  acc.w -= xsum;
+  const float row_amax = __uint_as_float((uint32_t)row_total<true>(col, kThreads / rp, red_max) << 16);
+  const float scale = (*gamma_ptr * row_amax) / 127.0f;
+  store_tile(acc, row_tile * kTileRows + 4 * sub, tok0 + col, n, scale, acc_out, y_out);
+}
+
+__global__ __launch_bounds__(kThreads) void k_gemv_direct(const uint4* __restrict__ packed,
+                                                          const float* __restrict__ gamma_ptr,
+                                                          const int8_t* __restrict__ xq,
+                                                          const float* __restrict__ alpha, int64_t m, int64_t n,
+                                                          int64_t k, int32_t* __restrict__ acc_out,
+                                                          uint16_t* __restrict__ y_out) {
+  __shared__ v4i partial[kWaves][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t row_tile = blockIdx.x;
+  const int64_t tok0 = (int64_t)blockIdx.y * 16;
+  const int64_t kt_count = k / kTileCols;
+  const int64_t groups = (kt_count + 3) / 4;
+  const int sub = lane >> 4;
+  const int col = lane & 15;
+  const int64_t tok = tok0 + col;
+  const bool has_tok = tok < m;
+  const uint4* wbase = packed + row_tile * kt_count * (kTileBytes / 16);
+  const int rows = (int)min((int64_t)16, m - tok0);
+  // resources over this row tile and this token block; offsets past either
+  // read as zero (tail groups, absent tokens), and a zero activation byte
+  // makes the product zero whatever the trit
+  const __amdgpu_buffer_rsrc_t wrsrc = buffer_rsrc(wbase, (uint32_t)(kt_count * kTileBytes));
+  const __amdgpu_buffer_rsrc_t xrsrc = buffer_rsrc(xq + tok0 * k, (uint32_t)(rows * k));
+
+  v4i acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+  for (int64_t g0 = wave; g0 < groups; g0 += (int64_t)kWaves * kGroupsPerBatch) {
+    uint4 a[kGroupsPerBatch];
+    uint4 b[kGroupsPerBatch][4];
+#pragma unroll
+    for (int u = 0; u < kGroupsPerBatch; ++u) {
+      const int64_t g = g0 + (int64_t)u * kWaves;
+      const int64_t kt = 4 * g + sub;
+      const bool valid = kt < kt_count && has_tok;
+      a[u] = buffer_load16(wrsrc, (uint32_t)(g * 1024 + lane * 16));
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+        b[u][f] = buffer_load16(xrsrc, valid ? (uint32_t)(col * k + kt * kTileCols + 16 * f) : kOutOfRange);
+    }
+#pragma unroll
+    for (int u = 0; u < kGroupsPerBatch; ++u) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) acc[f] = mfma_16x16x64(unpack_field(a[u], f), as_v4i(b[u][f]), acc[f]);
+    }
+  }
+  add4(acc[0], acc[1]);
+  add4(acc[2], acc[3]);
+  add4(acc[0], acc[2]);
+  partial[wave][lane] = acc[0];
+  __syncthreads();
+  if (wave != 0 || !has_tok) return;
+  v4i sum = partial[0][lane];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) add4(sum, partial[w][lane]);
+  const float scale = (*gamma_ptr * alpha[tok]) / 127.0f;
+  store_tile(sum, row_tile * kTileRows + 4 * sub, tok, n, scale, acc_out, y_out);
+}
+
+dim3 gemv_grid(int64_t m, int64_t n) {
+  return dim3((unsigned)((n + kTileRows - 1) / kTileRows), (unsigned)((m + 15) / 16));
+}
+
 }  // namespace
+
+size_t gemv_lds_bytes(int64_t m, int64_t k) { return (size_t)(m < 16 ? m : 16) * (size_t)(k + kLdsRowPad); }
+
+bool gemv_fits_lds(int64_t m, int64_t k) { return gemv_lds_bytes(m, k) <= (size_t)kLdsStageBytes; }
 
 hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
                        int64_t n, int64_t k, int32_t* acc, uint16_t* y, hipStream_t s) {
   if ((m + 15) / 16 > 65535) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((n + kTileRows - 1) / kTileRows), (unsigned)((m + 15) / 16));
-  hipLaunchKernelGGL(k_gemv, grid, dim3(kGemvThreads), 0, s, reinterpret_cast<const uint4*>(packed), gamma, xq,
-                     alpha, m, n, k, acc, y);
+  hipLaunchKernelGGL(k_gemv_direct, gemv_grid(m, n), dim3(kThreads), 0, s, reinterpret_cast<const uint4*>(packed),
+                     gamma, xq, alpha, m, n, k, acc, y);
   return hipGetLastError();
 }
 
-// Until the LDS-tiled GEMM lands, larger m runs the same kernel over
-// 16-token blocks (grid.y).
+hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t n,
+                             int64_t k, int8_t* xq, float* alpha, int32_t* acc, uint16_t* y, hipStream_t s) {
+  if (m > 16 || !gemv_fits_lds(m, k)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_bitlinear_fused, gemv_grid(m, n), dim3(kThreads), gemv_lds_bytes(m, k), s,
+                     reinterpret_cast<const uint4*>(packed), gamma, reinterpret_cast<const uint4*>(x), alpha, xq, m, n,
+                     k, acc, y);
+  return hipGetLastError();
+}
+
+// Until the LDS-tiled GEMM lands, larger m runs the GEMV over 16-token blocks.
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
                        int64_t n, int64_t k, int32_t* acc, uint16_t* y, hipStream_t s) {
   return launch_gemv(packed, gamma, xq, alpha, m, n, k, acc, y, s);

@@ -108,3 +108,19 @@ def test_python_binding_rejects_host_tensors():
         bl.bl_quant_act(torch.zeros((1, 64), dtype=torch.bfloat16))
     with pytest.raises(ValueError):
         bl.bl_ternarize_pack(torch.zeros((16, 64), dtype=torch.float32))
+
+
+def test_bitlinear_validation():
+    f = lib.bl_bitlinear
+
+    def call(packed=FAKE, gamma=FAKE, x=FAKE, m=1, n=16, k=64, xq=FAKE, alpha=FAKE, acc=FAKE, y=FAKE):
+        return f(packed, gamma, x, m, n, k, xq, alpha, acc, y, None)
+
+    assert call(x=None) == BL_ERR_NULL
+    assert call(xq=None) == BL_ERR_NULL
+    assert call(acc=None, y=None) == BL_ERR_NULL
+    assert call(k=100) == BL_ERR_SHAPE
+    assert call(m=-2) == BL_ERR_SHAPE
+    assert call(x=FAKE + 4) == BL_ERR_ALIGN
+    assert call(xq=FAKE + 1) == BL_ERR_ALIGN
+    assert call(m=0, x=None, xq=None, alpha=None) == BL_OK

@@ -291,3 +291,49 @@ def test_linear_is_deterministic():
     acc1, y1 = bl.bl_linear(u8(buf), g, xq, a, 3840)
     acc2, y2 = bl.bl_linear(u8(buf), g, xq, a, 3840)
     assert torch.equal(acc1, acc2) and torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+# ---------------------------------------------------------------- whole layer in one call
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 33, 64), (1, 2560, 2560), (1, 2560, 6912), (1, 100, 28672), (2, 17, 320),
+                                   (3, 48, 2560), (4, 3840, 2560), (5, 40, 6912), (16, 64, 1024), (16, 31, 2560),
+                                   (17, 40, 2560), (64, 100, 2560), (4, 16, 28672)])
+def test_bitlinear_matches_oracle(m, n, k):
+    """bl_bitlinear (fused quantize + product where it fits, two kernels
+    otherwise) against the oracle's quantizer, product and rescale."""
+    rng = np.random.default_rng(m * 131 + n * 7 + k)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    cols = rng.choice(k, size=min(8, k), replace=False)
+    x = datagen.activations_bf16(int(rng.integers(1 << 40)), m, k, cols, 20.0)
+    if m >= 2:
+        x[1] = 0  # an all-zero token
+    say(f"bl_bitlinear m={m} n={n} k={k}")
+    packed, gamma = bl.bl_ternarize_pack(f32(w))
+    acc, y, xq, alpha = bl.bl_bitlinear(packed, gamma, bf16(x), n)
+    want_packed, want_gamma = oracle.ternarize_pack(w)
+    want_y, want_acc, want_xq, want_alpha = oracle.bitlinear_forward(want_packed, want_gamma, x, n)
+    np.testing.assert_array_equal(host(xq), want_xq)
+    np.testing.assert_array_equal(host(alpha).view(np.uint32), want_alpha.view(np.uint32))
+    np.testing.assert_array_equal(host(acc), want_acc)
+    assert_bf16_within_one_ulp(host(y), want_y)
+    # y-only call writes the same bf16 values
+    _, y2, _, _ = bl.bl_bitlinear(packed, gamma, bf16(x), n, acc=False)
+    assert torch.equal(y2.view(torch.int16), y.view(torch.int16))
+
+
+def test_bitlinear_2b_stack_layer_decode():
+    """The benchmark's own step on one layer: seeded inputs, M = 1."""
+    wl = datagen.WORKLOAD_STACK_2B
+    for pi, (name, k, n) in enumerate(datagen.STACK_2B_PROJ):
+        w = datagen.weights(datagen.stream_id(wl, 3, pi, datagen.TENSOR_W), n, k)
+        cols = datagen.outlier_columns(wl, k, datagen.STACK_2B_OUTLIERS)
+        x = datagen.activations_bf16(datagen.stream_id(wl, 3, pi, datagen.TENSOR_X), 1, k, cols,
+                                     datagen.STACK_2B_OUTLIER_MULT)
+        say(f"bl_bitlinear 2B layer 3 {name}")
+        packed, gamma = bl.bl_ternarize_pack(f32(w))
+        acc, y, _, _ = bl.bl_bitlinear(packed, gamma, bf16(x), n)
+        want_packed, want_gamma = oracle.ternarize_pack(w)
+        want_y, want_acc, _, _ = oracle.bitlinear_forward(want_packed, want_gamma, x, n)
+        np.testing.assert_array_equal(host(acc), want_acc)
+        assert_bf16_within_one_ulp(host(y), want_y)
