@@ -1,0 +1,246 @@
+// Prefill product for BitLinear W1.58A8 (m > 16 tokens): packed ternary W x int8 x.
+//
+// deepmox.com chapter 8, "A low-bit model is a whole-stack design": the packed
+// weights move on chip, are unpacked there and multiplied with the 8-bit
+// activations; bako.co, "The BitLinear Layer and AbsMean Quantization": the
+// ternary product is integer add/subtract, here carried out by the int8
+// matrix cores (v_mfma_i32_16x16x64_i8) on the unpacked values.
+//
+// With many tokens the product is a dense contraction (2*m*n*k int8 ops over
+// n*k/4 + m*k bytes), bound by the matrix cores, not by HBM.  Tiling:
+//   * a workgroup (4 waves side by side along n) owns 256 weight rows x 64 or
+//     128 tokens; each wave owns 64 rows x all the workgroup's tokens, i.e.
+//     4 x 4 or 4 x 8 MFMA tiles of 16 x 16 (64 or 128 int32 accumulators per
+//     lane).  No two waves share weight rows, so each packed byte is unpacked
+//     once per workgroup;
+//   * K advances 256 columns per step.  The weights never pass through LDS:
+//     each wave loads its 64 rows' packed bytes straight into registers (one
+//     1 KiB load per 16 rows per step: 16 rows x 4 tiles of 64 columns) and
+//     unpacks them there -- 2-bit codes are 4x smaller than int8, so this is
+//     the cheap operand to fetch per wave;
+//   * the activation tile (tokens x 256 bytes) is shared by the four waves
+//     through LDS, double-buffered, with a 272-byte row stride so that each
+//     16-lane phase of a 128-bit read hits 16 distinct 4-bank groups;
+//   * the MFMA A operand is the raw code c = q + 1 of one 2-bit field
+//     ((p >> 2f) & 0x03030303), so the product is sum c*x; the token's sum of
+//     x, accumulated while its bytes are staged, turns it into sum q*x;
+//   * next step's global loads are issued before this step's MFMAs and
+//     written to the other LDS buffer after them: one barrier per step.
+// Tails: raw buffer resources return zero past the end of the weight row
+// tiles and token rows; column tails beyond k are masked to zero, so code 0
+// (or token 0) contributes nothing and the activation sums stay exact.
+#include "device_util.h"
+#include "internal.h"
+
+namespace bl {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kWN = 64;                 // weight rows per wave
+constexpr int kBN = kWaves * kWN;       // weight rows per workgroup
+constexpr int kStepK = 256;             // columns per step
+constexpr int kXStride = kStepK + 16;   // LDS bytes per token row
+constexpr int kRB = kWN / 16;           // 16-row MFMA blocks per wave
+constexpr int kXcds = 8;                // accelerator complex dies, each with its own L2
+
+template <int kTB>  // 16-token MFMA blocks per wave (4 or 8)
+__global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* __restrict__ packed, const float* __restrict__ gamma_ptr,
+                                                 const int8_t* __restrict__ xq, const float* __restrict__ alpha,
+                                                 int64_t m, int64_t n, int64_t k, int64_t blocks_n,
+                                                 int32_t* __restrict__ acc_out, uint16_t* __restrict__ y_out) {
+  constexpr int kBM = 16 * kTB;                       // tokens per workgroup
+  constexpr int kXLoads = kBM * kStepK / 16 / 256;    // 128-bit activation loads per thread per step
+  constexpr int kXThreadsPerTok = 256 / kBM;          // threads staging one token row
+  __shared__ uint4 xs[2][kBM * kXStride / 16];
+  __shared__ int row_sum[kBM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int sub = lane >> 4;
+  const int col = lane & 15;
+
+  // Workgroups are dealt to the XCDs round-robin (id % 8).  Give each XCD a
+  // contiguous run of tiles in token-block-major order, so the workgroups an
+  // XCD runs at once share one activation tile in that XCD's L2 while the
+  // weight blocks stream past it.
+  const int64_t tiles = (int64_t)gridDim.x;
+  const int64_t full = tiles / kXcds * kXcds;  // ids past the last full round keep their order
+  const int64_t tile = (int64_t)blockIdx.x >= full
+                           ? (int64_t)blockIdx.x
+                           : (int64_t)(blockIdx.x % kXcds) * (tiles / kXcds) + blockIdx.x / kXcds;
+  const int64_t bn = tile % blocks_n;
+  const int64_t bm = tile / blocks_n;
+  const int64_t n0 = bn * kBN;
+  const int64_t m0 = bm * kBM;
+  const int kt_count = (int)(k / kTileCols);
+  const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
+  const int steps = (kt_count + 3) / 4;
+  const int full_steps = kt_count / 4;  // steps whose four 64-column tiles all lie inside k
+  const int64_t rt0 = n0 / kTileRows;
+  const int tiles_here = (int)min((int64_t)(kBN / kTileRows), row_tiles - rt0);
+  const int tokens_here = (int)min((int64_t)kBM, m - m0);
+  const uint32_t kk = (uint32_t)k;
+
+  // Raw buffer resources over this workgroup's weight row tiles and token
+  // rows: reads past either end return zero.  All offsets fit in 32 bits.
+  const __amdgpu_buffer_rsrc_t wrsrc =
+      buffer_rsrc(packed + rt0 * kt_count * kTileBytes, (uint32_t)(tiles_here * kt_count * kTileBytes));
+  const __amdgpu_buffer_rsrc_t xrsrc = buffer_rsrc(xq + m0 * k, (uint32_t)tokens_here * kk);
+
+  // activation staging: thread t copies 16 * kXLoads bytes of one token row per step
+  const int x_tok = tid / kXThreadsPerTok;
+  const int x_chunk0 = (tid % kXThreadsPerTok) * kXLoads;
+  const uint32_t x_off0 = (uint32_t)x_tok * kk + 16u * (uint32_t)x_chunk0;
+  int x_sum = 0;
+  auto load_x = [&](int s, uint4* r) {
+    if (s < full_steps) {
+#pragma unroll
+      for (int j = 0; j < kXLoads; ++j) r[j] = buffer_load16(xrsrc, x_off0 + (uint32_t)(s * kStepK + 16 * j));
+    } else {  // partial last step: columns at or past k read as zero
+#pragma unroll
+      for (int j = 0; j < kXLoads; ++j) {
+        const uint32_t c = (uint32_t)(s * kStepK + 16 * (x_chunk0 + j));
+        r[j] = buffer_load16(xrsrc, c < kk ? x_off0 + (uint32_t)(s * kStepK + 16 * j) : kOutOfRange);
+      }
+    }
+  };
+  auto store_x = [&](int buf, const uint4* r, int j0, int j1) {
+    uint4* dst = xs[buf] + (x_tok * kXStride) / 16 + x_chunk0;
+#pragma unroll
+    for (int j = j0; j < j1; ++j) {
+      dst[j] = r[j];
+      x_sum = __builtin_amdgcn_sdot4((int)r[j].x, 0x01010101, x_sum, false);
+      x_sum = __builtin_amdgcn_sdot4((int)r[j].y, 0x01010101, x_sum, false);
+      x_sum = __builtin_amdgcn_sdot4((int)r[j].z, 0x01010101, x_sum, false);
+      x_sum = __builtin_amdgcn_sdot4((int)r[j].w, 0x01010101, x_sum, false);
+    }
+  };
+  // weights: row block rb of this wave, step s; lane = (tile sub, row col).
+  // Past-the-end tiles of a partial step are clamped to the last tile: they
+  // meet zero activations.
+  const uint32_t w_off0 = (uint32_t)(wave * kRB * kt_count) * kTileBytes + (uint32_t)col * 16u;
+  auto load_w = [&](int s, uint4* r) {
+    const uint32_t kt = (uint32_t)min(4 * s + sub, kt_count - 1);
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb)
+      r[rb] = buffer_load16(wrsrc, w_off0 + ((uint32_t)(rb * kt_count) + kt) * kTileBytes);
+  };
+
+  v4i acc[kRB][kTB];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+    for (int tb = 0; tb < kTB; ++tb) acc[rb][tb] = v4i{0, 0, 0, 0};
+
+  uint4 w_cur[kRB], w_next[kRB], x_next[kXLoads];
+  load_w(0, w_cur);
+  load_x(0, x_next);
+  store_x(0, x_next, 0, kXLoads);
+  __syncthreads();
+
+  auto compute = [&](int buf, int f0, int f1) {
+    const uint4* xt = xs[buf] + (col * kXStride + 64 * sub) / 16;
+#pragma unroll
+    for (int f = f0; f < f1; ++f) {
+      v4i b[kTB];
+#pragma unroll
+      for (int tb = 0; tb < kTB; ++tb) b[tb] = as_v4i(xt[(tb * 16 * kXStride) / 16 + f]);
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        v4i a;
+        a.x = (int)((w_cur[rb].x >> (2 * f)) & 0x03030303u);
+        a.y = (int)((w_cur[rb].y >> (2 * f)) & 0x03030303u);
+        a.z = (int)((w_cur[rb].z >> (2 * f)) & 0x03030303u);
+        a.w = (int)((w_cur[rb].w >> (2 * f)) & 0x03030303u);
+#pragma unroll
+        for (int tb = 0; tb < kTB; ++tb) acc[rb][tb] = mfma_16x16x64(a, b[tb], acc[rb][tb]);
+      }
+    }
+  };
+
+  for (int s = 0; s + 1 < steps; ++s) {
+    const int buf = s & 1;
+    load_w(s + 1, w_next);
+    load_x(s + 1, x_next);
+    // Half of this step's MFMAs run before the first consumer of next step's
+    // loads (the LDS stores and activation sums of half the tile), the other
+    // half before the rest; the scheduling barriers keep that order, so the
+    // loads stay in flight under MFMAs and the LDS stores overlap them.
+    __builtin_amdgcn_sched_barrier(0);
+    compute(buf, 0, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    store_x(buf ^ 1, x_next, 0, kXLoads / 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(buf, 2, 4);
+    __builtin_amdgcn_sched_barrier(0);
+    store_x(buf ^ 1, x_next, kXLoads / 2, kXLoads);
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) w_cur[rb] = w_next[rb];
+  }
+  compute((steps - 1) & 1, 0, 4);
+
+  // per-token activation sums: the threads of one token row hold its parts
+#pragma unroll
+  for (int off = kXThreadsPerTok / 2; off > 0; off >>= 1) x_sum += __shfl_xor(x_sum, off, 64);
+  if ((tid % kXThreadsPerTok) == 0) row_sum[x_tok] = x_sum;
+  __syncthreads();
+
+  const float gamma = *gamma_ptr;
+  // 4 consecutive outputs per lane: one 16-byte int32 / 8-byte bf16 store when
+  // every row start is aligned for it
+  const bool vec_ok = (n % 4) == 0 && ((uintptr_t)acc_out % 16) == 0 && ((uintptr_t)y_out % 8) == 0;
+#pragma unroll
+  for (int tb = 0; tb < kTB; ++tb) {
+    const int tok_local = tb * 16 + col;
+    const int64_t tok = m0 + tok_local;
+    if (tok >= m) continue;
+    const int xsum = row_sum[tok_local];
+    const float scale = (gamma * alpha[tok]) / 127.0f;
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      // this lane's four consecutive output rows row0..row0+3 for token tok
+      const int64_t row0 = n0 + wave * kWN + rb * 16 + 4 * sub;
+      const int vals[4] = {acc[rb][tb].x - xsum, acc[rb][tb].y - xsum, acc[rb][tb].z - xsum, acc[rb][tb].w - xsum};
+      if (vec_ok && row0 + 3 < n) {
+        if (acc_out) *reinterpret_cast<int4*>(acc_out + tok * n + row0) = make_int4(vals[0], vals[1], vals[2], vals[3]);
+        if (y_out) {
+          const uint32_t lo = f32_to_bf16_rne((float)vals[0] * scale) | ((uint32_t)f32_to_bf16_rne((float)vals[1] * scale) << 16);
+          const uint32_t hi = f32_to_bf16_rne((float)vals[2] * scale) | ((uint32_t)f32_to_bf16_rne((float)vals[3] * scale) << 16);
+          *reinterpret_cast<uint2*>(y_out + tok * n + row0) = make_uint2(lo, hi);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t row = row0 + i;
+          if (row < n) {
+            if (acc_out) acc_out[tok * n + row] = vals[i];
+            if (y_out) y_out[tok * n + row] = f32_to_bf16_rne((float)vals[i] * scale);
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
+                       int64_t n, int64_t k, int32_t* acc, uint16_t* y, hipStream_t s) {
+  const int64_t blocks_n = (n + kBN - 1) / kBN;
+  // 128-token tiles unless that leaves fewer than two workgroups per CU
+  const bool tall = blocks_n * ((m + 127) / 128) >= 512;
+  const int64_t bm = tall ? 128 : 64;
+  const int64_t blocks = blocks_n * ((m + bm - 1) / bm);
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (tall)
+    hipLaunchKernelGGL(k_gemm<8>, dim3((unsigned)blocks), dim3(256), 0, s, packed, gamma, xq, alpha, m, n, k, blocks_n,
+                       acc, y);
+  else
+    hipLaunchKernelGGL(k_gemm<4>, dim3((unsigned)blocks), dim3(256), 0, s, packed, gamma, xq, alpha, m, n, k, blocks_n,
+                       acc, y);
+  return hipGetLastError();
+}
+
+}  // namespace bl

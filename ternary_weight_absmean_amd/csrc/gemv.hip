@@ -351,10 +351,4 @@ hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const ui
   return hipGetLastError();
 }
 
-// Until the LDS-tiled GEMM lands, larger m runs the GEMV over 16-token blocks.
-hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
-                       int64_t n, int64_t k, int32_t* acc, uint16_t* y, hipStream_t s) {
-  return launch_gemv(packed, gamma, xq, alpha, m, n, k, acc, y, s);
-}
-
 }  // namespace bl
