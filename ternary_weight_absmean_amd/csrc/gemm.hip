@@ -19,13 +19,17 @@
 //     unpacks them there -- 2-bit codes are 4x smaller than int8, so this is
 //     the cheap operand to fetch per wave;
 //   * the activation tile (tokens x 256 bytes) is shared by the four waves
-//     through LDS, double-buffered, with a 272-byte row stride so that each
-//     16-lane phase of a 128-bit read hits 16 distinct 4-bank groups;
+//     through LDS, double-buffered, and copied there by DMA (buffer loads
+//     that write LDS directly: no registers, no LDS store instructions);
+//     16-byte chunk c of token row r is stored at chunk c ^ (r % 16) of that
+//     row, so the 16 lanes of each phase of a 128-bit read (16 tokens, one
+//     chunk) hit 16 distinct 4-bank groups;
 //   * the MFMA A operand is the raw code c = q + 1 of one 2-bit field
 //     ((p >> 2f) & 0x03030303), so the product is sum c*x; the token's sum of
-//     x, accumulated while its bytes are staged, turns it into sum q*x;
-//   * next step's global loads are issued before this step's MFMAs and
-//     written to the other LDS buffer after them: one barrier per step.
+//     x turns it into sum q*x.  The sums come from the B operands already in
+//     registers: wave w adds up field w (4 dot4 per token block and step);
+//   * next step's DMA and weight loads are issued before this step's MFMAs;
+//     one barrier per step.
 // Tails: raw buffer resources return zero past the end of the weight row
 // tiles and token rows; column tails beyond k are masked to zero, so code 0
 // (or token 0) contributes nothing and the activation sums stay exact.
@@ -39,7 +43,7 @@ constexpr int kWaves = 4;
 constexpr int kWN = 64;                 // weight rows per wave
 constexpr int kBN = kWaves * kWN;       // weight rows per workgroup
 constexpr int kStepK = 256;             // columns per step
-constexpr int kXStride = kStepK + 16;   // LDS bytes per token row
+constexpr int kXRow = kStepK / 16;     // 16-byte chunks per token row in LDS
 constexpr int kRB = kWN / 16;           // 16-row MFMA blocks per wave
 constexpr int kXcds = 8;                // accelerator complex dies, each with its own L2
 
@@ -49,14 +53,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* __restrict__ pac
                                                  int64_t m, int64_t n, int64_t k, int64_t blocks_n,
                                                  int32_t* __restrict__ acc_out, uint16_t* __restrict__ y_out) {
   constexpr int kBM = 16 * kTB;                       // tokens per workgroup
-  constexpr int kXLoads = kBM * kStepK / 16 / 256;    // 128-bit activation loads per thread per step
-  constexpr int kXThreadsPerTok = 256 / kBM;          // threads staging one token row
-  __shared__ uint4 xs[2][kBM * kXStride / 16];
+  constexpr int kXDma = kBM * kStepK / 1024 / kWaves; // 1 KiB LDS-DMA loads per wave per step
+  __shared__ uint4 xs[2][kBM * kXRow];
   __shared__ int row_sum[kBM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in a scalar register
   const int sub = lane >> 4;
   const int col = lane & 15;
 
@@ -88,32 +91,20 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* __restrict__ pac
       buffer_rsrc(packed + rt0 * kt_count * kTileBytes, (uint32_t)(tiles_here * kt_count * kTileBytes));
   const __amdgpu_buffer_rsrc_t xrsrc = buffer_rsrc(xq + m0 * k, (uint32_t)tokens_here * kk);
 
-  // activation staging: thread t copies 16 * kXLoads bytes of one token row per step
-  const int x_tok = tid / kXThreadsPerTok;
-  const int x_chunk0 = (tid % kXThreadsPerTok) * kXLoads;
-  const uint32_t x_off0 = (uint32_t)x_tok * kk + 16u * (uint32_t)x_chunk0;
-  int x_sum = 0;
-  auto load_x = [&](int s, uint4* r) {
-    if (s < full_steps) {
+  // Activation tiles go global -> LDS by DMA (buffer_load ... lds): lane i of
+  // a load writes LDS bytes 16i..16i+15 of that load's 1 KiB, i.e. token row
+  // 4*load + i/16, stored chunk i%16.  Stored chunk p of row r holds source
+  // chunk p ^ (r % 16), so the lane fetches that one.
+  const int dma_row0 = wave * kXDma * 4 + (lane >> 4);
+  auto load_x = [&](int s, int buf) {
 #pragma unroll
-      for (int j = 0; j < kXLoads; ++j) r[j] = buffer_load16(xrsrc, x_off0 + (uint32_t)(s * kStepK + 16 * j));
-    } else {  // partial last step: columns at or past k read as zero
-#pragma unroll
-      for (int j = 0; j < kXLoads; ++j) {
-        const uint32_t c = (uint32_t)(s * kStepK + 16 * (x_chunk0 + j));
-        r[j] = buffer_load16(xrsrc, c < kk ? x_off0 + (uint32_t)(s * kStepK + 16 * j) : kOutOfRange);
-      }
-    }
-  };
-  auto store_x = [&](int buf, const uint4* r, int j0, int j1) {
-    uint4* dst = xs[buf] + (x_tok * kXStride) / 16 + x_chunk0;
-#pragma unroll
-    for (int j = j0; j < j1; ++j) {
-      dst[j] = r[j];
-      x_sum = __builtin_amdgcn_sdot4((int)r[j].x, 0x01010101, x_sum, false);
-      x_sum = __builtin_amdgcn_sdot4((int)r[j].y, 0x01010101, x_sum, false);
-      x_sum = __builtin_amdgcn_sdot4((int)r[j].z, 0x01010101, x_sum, false);
-      x_sum = __builtin_amdgcn_sdot4((int)r[j].w, 0x01010101, x_sum, false);
+    for (int j = 0; j < kXDma; ++j) {
+      const int row = dma_row0 + 4 * j;
+      const int c = (lane & 15) ^ (row & 15);
+      const uint32_t col_byte = (uint32_t)(s * kStepK + 16 * c);
+      const uint32_t off = (s < full_steps || col_byte < kk) ? (uint32_t)row * kk + col_byte : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xrsrc, (__attribute__((address_space(3))) void*)(xs[buf] + (wave * kXDma + j) * 64), 16, off, 0, 0, 0);
     }
   };
   // weights: row block rb of this wave, step s; lane = (tile sub, row col).
@@ -132,20 +123,29 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* __restrict__ pac
   for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
     for (int tb = 0; tb < kTB; ++tb) acc[rb][tb] = v4i{0, 0, 0, 0};
+  // Per-token activation sums, taken from the B operands already in
+  // registers: wave w adds field w of every token block, so lane (col, sub)
+  // holds, per token block tb, the sum over columns 16w..16w+15 of column tile
+  // `sub` of every step for token tb*16 + col.
+  int x_sum[kTB];
+#pragma unroll
+  for (int tb = 0; tb < kTB; ++tb) x_sum[tb] = 0;
+  if (tid < kBM) row_sum[tid] = 0;
 
-  uint4 w_cur[kRB], w_next[kRB], x_next[kXLoads];
+  uint4 w_cur[kRB], w_next[kRB];
   load_w(0, w_cur);
-  load_x(0, x_next);
-  store_x(0, x_next, 0, kXLoads);
+  load_x(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  auto compute = [&](int buf, int f0, int f1) {
-    const uint4* xt = xs[buf] + (col * kXStride + 64 * sub) / 16;
+  auto compute = [&](int buf) {
+    // token row tb*16 + col, chunk 4*sub + f, stored at chunk (4*sub + f) ^ col
+    const uint4* xt = xs[buf] + col * kXRow;
 #pragma unroll
-    for (int f = f0; f < f1; ++f) {
+    for (int f = 0; f < 4; ++f) {
       v4i b[kTB];
 #pragma unroll
-      for (int tb = 0; tb < kTB; ++tb) b[tb] = as_v4i(xt[(tb * 16 * kXStride) / 16 + f]);
+      for (int tb = 0; tb < kTB; ++tb) b[tb] = as_v4i(xt[tb * 16 * kXRow + ((4 * sub + f) ^ col)]);
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) {
         v4i a;
@@ -156,35 +156,39 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* __restrict__ pac
 #pragma unroll
         for (int tb = 0; tb < kTB; ++tb) acc[rb][tb] = mfma_16x16x64(a, b[tb], acc[rb][tb]);
       }
+      if (f == wave) {  // wave-uniform
+#pragma unroll
+        for (int tb = 0; tb < kTB; ++tb) {
+          x_sum[tb] = __builtin_amdgcn_sdot4(b[tb].x, 0x01010101, x_sum[tb], false);
+          x_sum[tb] = __builtin_amdgcn_sdot4(b[tb].y, 0x01010101, x_sum[tb], false);
+          x_sum[tb] = __builtin_amdgcn_sdot4(b[tb].z, 0x01010101, x_sum[tb], false);
+          x_sum[tb] = __builtin_amdgcn_sdot4(b[tb].w, 0x01010101, x_sum[tb], false);
+        }
+      }
     }
   };
 
   for (int s = 0; s + 1 < steps; ++s) {
     const int buf = s & 1;
     load_w(s + 1, w_next);
-    load_x(s + 1, x_next);
-    // Half of this step's MFMAs run before the first consumer of next step's
-    // loads (the LDS stores and activation sums of half the tile), the other
-    // half before the rest; the scheduling barriers keep that order, so the
-    // loads stay in flight under MFMAs and the LDS stores overlap them.
-    __builtin_amdgcn_sched_barrier(0);
-    compute(buf, 0, 2);
-    __builtin_amdgcn_sched_barrier(0);
-    store_x(buf ^ 1, x_next, 0, kXLoads / 2);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(buf, 2, 4);
-    __builtin_amdgcn_sched_barrier(0);
-    store_x(buf ^ 1, x_next, kXLoads / 2, kXLoads);
-    __syncthreads();
+    load_x(s + 1, buf ^ 1);
+    compute(buf);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA into buf ^ 1 has landed
+    __syncthreads();                // ... and every other wave's, and nobody reads buf any more
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) w_cur[rb] = w_next[rb];
   }
-  compute((steps - 1) & 1, 0, 4);
+  compute((steps - 1) & 1);
 
-  // per-token activation sums: the threads of one token row hold its parts
+  // per-token activation sums: add the four column-tile lanes of each token,
+  // then the four waves' fields
 #pragma unroll
-  for (int off = kXThreadsPerTok / 2; off > 0; off >>= 1) x_sum += __shfl_xor(x_sum, off, 64);
-  if ((tid % kXThreadsPerTok) == 0) row_sum[x_tok] = x_sum;
+  for (int tb = 0; tb < kTB; ++tb) {
+    int v = x_sum[tb];
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    if (sub == 0) atomicAdd(&row_sum[tb * 16 + col], v);
+  }
   __syncthreads();
 
   const float gamma = *gamma_ptr;
