@@ -44,11 +44,20 @@ def parse_args():
     p.add_argument("--layers", type=int, default=30, help="layers of the 2B-shaped stack (30 = the full model)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="bound on the CPU-oracle timing sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the prefill, batched-decode and 70B-shaped measurements")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only copy a 1 GiB device buffer 3 times (counter calibration run)")
+    p.add_argument("--summarize", nargs=4, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR", "CALIB_DIR"),
+                   help="turn rocprofv3 outputs into profiles/ summaries (no GPU needed)")
+    p.add_argument("--calib-write-dir", default=None, help="WRITE_SIZE run of the calibration copy")
     return p.parse_args()
 
 
 def main() -> int:
     args = parse_args()
+    if args.summarize:
+        return summarize(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
               "(the BitLinear path runs on a single MI355X).", file=sys.stderr)
@@ -56,6 +65,15 @@ def main() -> int:
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("copied 3 x 1 GiB", flush=True)
+        return 0
 
     import datagen
     import ternary_weight_absmean_amd as bl
@@ -173,6 +191,10 @@ def main() -> int:
     avg_bytes = sum(layer_bytes) / len(layer_bytes)
     gemv_gbps = avg_bytes / (avg_us * 1e-6) / 1e9
 
+    extras = None
+    if not args.no_extras:
+        extras = measure_extras(args, linears, lib)
+
     # ------------------------------------------------------------ CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -200,14 +222,256 @@ def main() -> int:
         "wall_s_timed": round(wall, 4),
         "roofline": {"bound": "hbm", "kernel": "k_gemv_lds<fused> (bl_bitlinear)", "achieved": round(gemv_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gemv_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "avg_launch_us": round(avg_us, 3),
+                     "traffic": stored_traffic("k_bitlinear_fused", avg_bytes), "avg_launch_us": round(avg_us, 3),
                      "algorithmic_bytes_per_launch": round(avg_bytes, 1)},
         "packer": {"weights": len(linears), "fp32_GB": round(w_bytes / 1e9, 3), "ms": round(pack_ms, 3),
                    "GBps_fp32_read": round(w_bytes / (pack_ms * 1e-3) / 1e9, 1)},
         "cpu_baseline": cpu,
+        "extras": extras,
     }
     print(json.dumps(result), flush=True)
     return 0
+
+
+MFMA_I8_PEAK_TOPS = 5000.0
+CALIB_BYTES = 1 << 30
+
+
+def _read_csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(d, suffix):
+    import glob
+    hits = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    return hits[0]
+
+
+def _per_dispatch(rows, name_part, counter):
+    vals = [float(r["Counter_Value"]) for r in rows if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    return sum(vals) / len(vals) if vals else None, len(vals)
+
+
+def summarize(args):
+    """profiles/ from rocprofv3 outputs: kernel-trace stats of the benchmark,
+    FETCH_SIZE and WRITE_SIZE of its kernels, and the same counters for a
+    1 GiB device copy (calibration: bytes the counters report per byte moved)."""
+    stats_dir, fetch_dir, write_dir, calib_dir = args.summarize
+    calib_write_dir = args.calib_write_dir or calib_dir
+    stats = _read_csv(_find(stats_dir, "kernel_stats.csv"))
+    fetch = _read_csv(_find(fetch_dir, "counter_collection.csv"))
+    write = _read_csv(_find(write_dir, "counter_collection.csv"))
+    cal_f = _read_csv(_find(calib_dir, "counter_collection.csv"))
+    cal_w = _read_csv(_find(calib_write_dir, "counter_collection.csv"))
+    copy_fetch, _ = _per_dispatch(cal_f, "copy", "FETCH_SIZE")
+    copy_write, _ = _per_dispatch(cal_w, "copy", "WRITE_SIZE")
+    f_fetch = CALIB_BYTES / (copy_fetch * 1024.0)
+    f_write = CALIB_BYTES / (copy_write * 1024.0)
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    traffic = {}
+    lines = ["# Decode stack (2B-shaped, M=1): kernel durations and HBM traffic", "",
+             "Commands (run from the repository root on one MI355X):", "",
+             "```",
+             "rocprofv3 --kernel-trace --stats --output-format csv -d <STATS_DIR> -o stack -- "
+             "python bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-extras",
+             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -o f -- "
+             "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-extras",
+             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE_DIR> -o w -- "
+             "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-extras",
+             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <CALIB_DIR> -o c -- python bench.py --calibrate-copy",
+             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <CALIB_WRITE_DIR> -o c -- python bench.py --calibrate-copy",
+             "python bench.py --summarize <STATS_DIR> <FETCH_DIR> <WRITE_DIR> <CALIB_DIR> --calib-write-dir <CALIB_WRITE_DIR>",
+             "```", "",
+             f"Calibration: a 1 GiB device copy reads {copy_fetch:.0f} KiB (FETCH_SIZE) and writes "
+             f"{copy_write:.0f} KiB (WRITE_SIZE) per dispatch; scale factors {f_fetch:.4f} and {f_write:.4f}.", "",
+             "| kernel | calls | avg duration (us) | min (us) | max (us) | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | HBM bytes/launch (calibrated) |",
+             "|---|---|---|---|---|---|---|---|"]
+    for r in stats:
+        name = r["Name"]
+        short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("bl::", "").replace("void ", "")
+        fk, _ = _per_dispatch(fetch, short, "FETCH_SIZE")
+        wk, _ = _per_dispatch(write, short, "WRITE_SIZE")
+        hbm = None
+        if fk is not None and wk is not None:
+            hbm = fk * 1024.0 * f_fetch + wk * 1024.0 * f_write
+        lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | {float(r['MinNs']) / 1e3:.3f} | "
+                     f"{float(r['MaxNs']) / 1e3:.3f} | {'' if fk is None else f'{fk:.1f}'} | "
+                     f"{'' if wk is None else f'{wk:.1f}'} | {'' if hbm is None else f'{hbm:.0f}'} |")
+        base = short.split("<")[0]
+        if base in KERNEL_SOURCES and hbm is not None:
+            traffic[base] = {"bytes_per_launch": round(hbm), "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                             "calibration": {"fetch": round(f_fetch, 5), "write": round(f_write, 5)},
+                             "source_sha256_16": source_hash(base),
+                             "workload": "bitnet-b1.58-2B-shaped decode stack, M=1 (bench.py default)",
+                             "avg_duration_us": round(float(r["AverageNs"]) / 1e3, 3)}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1, sort_keys=True)
+        f.write("\n")
+    with open(os.path.join(ROOT, "profiles", "decode_stack_2b_m1.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return 0
+KERNEL_SOURCES = {"k_bitlinear_fused": "gemv.hip", "k_gemv_direct": "gemv.hip", "k_gemm": "gemm.hip"}
+
+
+def source_hash(kernel: str) -> str:
+    import hashlib
+    path = os.path.join(ROOT, "ternary_weight_absmean_amd", "csrc", KERNEL_SOURCES[kernel])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(kernel: str, algorithmic_bytes: float):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or None
+    when there is none or the kernel's source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256_16") != source_hash(kernel):
+        return None
+    return {"bytes_per_launch": rec["bytes_per_launch"],
+            "ratio_to_algorithmic": round(rec["bytes_per_launch"] / algorithmic_bytes, 3),
+            "workload": rec.get("workload")}
+
+
+def _graph_time_ms(torch, fn, reps, warm=2):
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(warm):
+        g.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def measure_extras(args, linears, lib):
+    """Other workloads of the metric, each timed as HIP-graph replays:
+    prefill (M = 2048) on the 2B stack's layer-0 gate+up and down, batched
+    decode (M = 4, 16, 64) through the whole 2B stack, and the 70B-shaped
+    layer (80 distinct copies of one layer's packed weights, looped) at M = 1,
+    16 and 1024.  Inputs are seeded synthetic activations of each shape."""
+    import numpy as np
+    import torch
+
+    import datagen
+    import ternary_weight_absmean_amd as bl
+
+    dev = torch.device("cuda", 0)
+    vp = ctypes.c_void_p
+    out = {}
+
+    def act(stream, m, k, wl, n_out, mult):
+        cols = datagen.outlier_columns(wl, k, n_out)
+        x = datagen.activations_bf16(stream, m, k, cols, mult)
+        return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def layer_fn(items, m):
+        """items: list of (packed, gamma, x, n, k, xq, alpha, y) tensors."""
+        def fn():
+            s = vp(torch.cuda.current_stream().cuda_stream)
+            for packed, gamma, x, n, k, xq, alpha, y in items:
+                rc = lib.bl_bitlinear(vp(packed.data_ptr()), vp(gamma.data_ptr()), vp(x.data_ptr()), m, n, k,
+                                      vp(xq.data_ptr()), vp(alpha.data_ptr()), None, vp(y.data_ptr()), s)
+                if rc:
+                    raise RuntimeError(bl.bl_status_string(rc))
+        return fn
+
+    def bufs(m, n, k):
+        return (torch.empty((m, k), dtype=torch.int8, device=dev), torch.empty(m, dtype=torch.float32, device=dev),
+                torch.empty((m, n), dtype=torch.bfloat16, device=dev))
+
+    # ---- prefill, 2B layer 0 gate+up and down, M = 2048 (per-token quantize + GEMM)
+    wl = datagen.WORKLOAD_STACK_2B
+    prefill = {}
+    for name in ("gate_up", "down"):
+        lin = next(l for l in linears if l["name"] == name)
+        m, n, k = 2048, lin["n"], lin["k"]
+        x = act(datagen.stream_id(wl, 0, 2 if name == "gate_up" else 3, datagen.TENSOR_X) + 2048, m, k, wl,
+                datagen.STACK_2B_OUTLIERS, datagen.STACK_2B_OUTLIER_MULT)
+        xq, alpha, y = bufs(m, n, k)
+        ms = _graph_time_ms(torch, layer_fn([(lin["packed"], lin["gamma"], x, n, k, xq, alpha, y)], m), 20)
+        # the product alone (quantized activations already in place)
+        def gemm_only():
+            s = vp(torch.cuda.current_stream().cuda_stream)
+            rc = lib.bl_linear(vp(lin["packed"].data_ptr()), vp(lin["gamma"].data_ptr()), vp(xq.data_ptr()),
+                               vp(alpha.data_ptr()), m, n, k, None, vp(y.data_ptr()), s)
+            if rc:
+                raise RuntimeError(bl.bl_status_string(rc))
+        ms_gemm = _graph_time_ms(torch, gemm_only, 20)
+        ops = 2.0 * m * n * k
+        prefill[f"{name} M={m} K={k} N={n}"] = {
+            "layer_ms": round(ms, 4), "layer_TOPS": round(ops / (ms * 1e-3) / 1e12, 1),
+            "gemm_ms": round(ms_gemm, 4), "gemm_TOPS": round(ops / (ms_gemm * 1e-3) / 1e12, 1),
+            "gemm_frac_of_int8_mfma_peak": round(ops / (ms_gemm * 1e-3) / 1e12 / MFMA_I8_PEAK_TOPS, 4)}
+    out["prefill_2b"] = prefill
+
+    # ---- batched decode through the whole 2B stack, M = 4, 16, 64
+    batched = {}
+    weight_bytes = sum(l["packed"].numel() for l in linears)
+    for m in (4, 16, 64):
+        items = []
+        for i, lin in enumerate(linears):
+            x = act(datagen.stream_id(wl, i // 4, i % 4, datagen.TENSOR_X) + 7 * m, m, lin["k"], wl, 0, 1.0)
+            items.append((lin["packed"], lin["gamma"], x, lin["n"], lin["k"], *bufs(m, lin["n"], lin["k"])))
+        ms = _graph_time_ms(torch, layer_fn(items, m), max(5, args.steps // 10))
+        batched[f"M={m}"] = {"ms_per_step": round(ms, 4), "tokens_per_s": round(m * 1000.0 / ms, 1),
+                             "weight_GBps": round(weight_bytes / (ms * 1e-3) / 1e9, 1)}
+        del items
+    out["batched_decode_2b_stack"] = batched
+
+    # ---- 70B-shaped layer: 80 distinct copies of one layer's packed weights
+    wl70 = datagen.WORKLOAD_70B
+    layer = []
+    for pi, (name, k, n) in enumerate(datagen.LAYER_70B_PROJ):
+        w = torch.from_numpy(datagen.weights(datagen.stream_id(wl70, 0, pi, datagen.TENSOR_W), n, k)).to(dev)
+        packed, gamma = bl.bl_ternarize_pack(w)
+        del w
+        layer.append((name, k, n, packed, gamma))
+    torch.cuda.synchronize()
+    n_layers = datagen.LAYER_70B_LAYERS
+    copies = [[(name, k, n, packed.clone(), gamma) for name, k, n, packed, gamma in layer] for _ in range(n_layers)]
+    torch.cuda.synchronize()
+    layer_bytes = sum(packed.numel() for _, _, _, packed, _ in layer)
+    r70 = {"packed_bytes_per_layer": layer_bytes, "layers": n_layers}
+    for m in (1, 16, 1024):
+        xs = {k: act(datagen.stream_id(wl70, 0, pi, datagen.TENSOR_X) + m, m, k, wl70, datagen.n_outliers_70b(k),
+                     datagen.LAYER_70B_OUTLIER_MULT) for pi, (_, k, _) in enumerate(datagen.LAYER_70B_PROJ)}
+        scratch = {(n, k): bufs(m, n, k) for _, k, n, _, _ in layer}
+        items = [(packed, gamma, xs[k], n, k, *scratch[(n, k)]) for c in copies for (_, k, n, packed, gamma) in c]
+        ms = _graph_time_ms(torch, layer_fn(items, m), 3 if m == 1024 else 10)
+        entry = {"ms_per_80_layers": round(ms, 3), "tokens_per_s": round(m * 1000.0 / ms, 1),
+                 "weight_GBps": round(layer_bytes * n_layers / (ms * 1e-3) / 1e9, 1)}
+        if m == 1024:
+            ops = 2.0 * m * sum(n * k for _, k, n, _, _ in layer) * n_layers
+            entry["TOPS"] = round(ops / (ms * 1e-3) / 1e12, 1)
+            entry["frac_of_int8_mfma_peak"] = round(ops / (ms * 1e-3) / 1e12 / MFMA_I8_PEAK_TOPS, 4)
+        else:
+            entry["frac_of_hbm_peak"] = round(layer_bytes * n_layers / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+        r70[f"M={m}"] = entry
+        del items, scratch
+    out["layer_70b"] = r70
+    del copies, layer
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(args, outliers):
