@@ -266,6 +266,145 @@ __global__ __launch_bounds__(kThreads) void k_bitlinear_fused(const uint4* __res
   store_tile(acc, row_tile * kTileRows + 4 * sub, tok0 + col, n, scale, acc_out, y_out);
 }
 
+constexpr int kM1MaxChunks = 14;  // bf16 chunks of 8 per lane: single-token rows up to k = 7168
+
+// Single-token BitLinear (m = 1, k <= 7168) without a barrier before the
+// products.  Every wave loads the whole bf16 row (lane l holds chunks of 8
+// elements l, l + 64, ...), reduces its absmax in registers, and quantizes
+// only the 256-column groups it multiplies (groups w, w + 4, ...) into its
+// own LDS region, which only it reads.  Each wave subtracts the activation
+// sum of its own columns from its partial products, so the waves' partials
+// add up to sum q*x; one barrier then combines them.  A workgroup handles
+// kRT consecutive 16-row tiles, reusing the quantized row; the weight loads
+// of all its tiles form one stream, prefetched a batch ahead.
+template <int kRT>
+__global__ __launch_bounds__(kThreads) void k_bitlinear_m1(const uint4* __restrict__ packed,
+                                                           const float* __restrict__ gamma_ptr,
+                                                           const uint4* __restrict__ x, float* __restrict__ alpha,
+                                                           int8_t* __restrict__ xq_out, int64_t n, int64_t k,
+                                                           int32_t* __restrict__ acc_out, uint16_t* __restrict__ y_out) {
+  extern __shared__ uint4 xw_raw[];  // [wave][groups of this wave][256 bytes]
+  __shared__ v4i partial[kRT][kWaves][64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t tile0 = (int64_t)blockIdx.x * kRT;
+  const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
+  const int tiles_here = (int)min((int64_t)kRT, row_tiles - tile0);
+  const int kt_count = (int)(k / kTileCols);
+  const int groups = (kt_count + 3) / 4;
+  const int my_groups = (groups - wave + kWaves - 1) / kWaves;
+  const int max_groups = (groups + kWaves - 1) / kWaves;
+  const int sub = lane >> 4;
+  const int col = lane & 15;
+  const int k8 = (int)(k / 8);
+
+  // activations first (loads retire in order), then the first weight batch
+  const __amdgpu_buffer_rsrc_t xrsrc = buffer_rsrc(x, (uint32_t)(k8 * 16));
+  uint4 xr[kM1MaxChunks];
+#pragma unroll
+  for (int i = 0; i < kM1MaxChunks; ++i) xr[i] = buffer_load16(xrsrc, (uint32_t)((lane + 64 * i) * 16));
+  // Weights: one resource per row tile, so that groups past k (and a whole
+  // tile past n) read as zero codes instead of the next tile's bytes.
+  const uint32_t tile_bytes = (uint32_t)(kt_count * kTileBytes);
+  auto tile_rsrc = [&](int rt) {
+    return buffer_rsrc(packed + (tile0 + rt) * kt_count * (kTileBytes / 16), rt < tiles_here ? tile_bytes : 0u);
+  };
+  // this wave's gi-th group within a row tile
+  auto w_off = [&](int gi) { return (uint32_t)((wave + gi * kWaves) * 1024 + lane * 16); };
+  uint4 a_cur[kGroupsPerBatch];
+  {
+    const __amdgpu_buffer_rsrc_t r0 = tile_rsrc(0);
+#pragma unroll
+    for (int u = 0; u < kGroupsPerBatch; ++u) a_cur[u] = buffer_load16(r0, w_off(u));
+  }
+
+  // absmax of the whole row, in this wave alone (chunks past k read as zero)
+  uint32_t mx = 0;
+#pragma unroll
+  for (int i = 0; i < kM1MaxChunks; ++i) mx = max(mx, max_abs_bf16x8(xr[i]));
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+  const float amax = __uint_as_float(mx << 16);
+  const float s = 127.0f / fmaxf(amax, 1e-5f);  // IEEE division, as in bl_quant_act
+
+  // quantize this wave's groups: chunk j belongs to group j / 32, owned by
+  // wave (j / 32) % 4; it lands at byte 8 * (j % 32) of that group's region
+  int8_t* region = reinterpret_cast<int8_t*>(xw_raw) + wave * max_groups * 256;
+  uint2* gdst = (blockIdx.x == 0 && xq_out) ? reinterpret_cast<uint2*>(xq_out) : nullptr;
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < kM1MaxChunks; ++i) {
+    const int j = lane + 64 * i;
+    const int g = j >> 5;
+    if (j < k8 && (g & (kWaves - 1)) == wave) {
+      const uint2 q = make_uint2(quant2(xr[i].x, s, sum) | (quant2(xr[i].y, s, sum) << 16),
+                                 quant2(xr[i].z, s, sum) | (quant2(xr[i].w, s, sum) << 16));
+      reinterpret_cast<uint2*>(region + (g / kWaves) * 256)[j & 31] = q;
+      if (gdst) gdst[j] = q;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+  if (blockIdx.x == 0 && wave == 0 && lane == 0 && alpha) alpha[0] = amax;
+  // this wave's own LDS writes are complete before its reads below
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    v4i acc1 = {0, 0, 0, 0}, acc4 = acc1, acc16a = acc1, acc16b = acc1;
+    const __amdgpu_buffer_rsrc_t cur_rsrc = tile_rsrc(rt);
+    const __amdgpu_buffer_rsrc_t next_rsrc = tile_rsrc(rt + 1);  // empty past the last tile
+    for (int gi = 0; gi < my_groups; gi += kGroupsPerBatch) {
+      // next batch: more groups of this tile, else the first groups of the next
+      const bool same = gi + kGroupsPerBatch < my_groups;
+      const int ngi = same ? gi + kGroupsPerBatch : 0;
+      uint4 a_next[kGroupsPerBatch];
+#pragma unroll
+      for (int u = 0; u < kGroupsPerBatch; ++u)
+        a_next[u] = buffer_load16(same ? cur_rsrc : next_rsrc, w_off(ngi + u));
+#pragma unroll
+      for (int u = 0; u < kGroupsPerBatch; ++u) {
+        // groups past this wave's share carry zero codes; any region slot will do
+        const int gl = min(gi + u, max_groups - 1);
+        const uint4* xt = reinterpret_cast<const uint4*>(region + gl * 256) + 4 * sub;
+        uint4 b[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) b[f] = xt[f];
+        acc1 = mfma_16x16x64(mask4(a_cur[u], 0x03030303u, 0), as_v4i(b[0]), acc1);
+        acc4 = mfma_16x16x64(mask4(a_cur[u], 0x0C0C0C0Cu, 0), as_v4i(b[1]), acc4);
+        acc16a = mfma_16x16x64(mask4(a_cur[u], 0x30303030u, 0), as_v4i(b[2]), acc16a);
+        acc16b = mfma_16x16x64(mask4(a_cur[u], 0x30303030u, 2), as_v4i(b[3]), acc16b);
+      }
+#pragma unroll
+      for (int u = 0; u < kGroupsPerBatch; ++u) a_cur[u] = a_next[u];
+    }
+    if (my_groups == 0 && rt + 1 < kRT) {  // keep the stream aligned: nothing was loaded for this tile
+#pragma unroll
+      for (int u = 0; u < kGroupsPerBatch; ++u) a_cur[u] = buffer_load16(next_rsrc, w_off(u));
+    }
+    // exact: acc4 holds 4x, acc16a/b 16x the code sums; minus this wave's x sum
+    v4i part = acc1;
+    part.x += (acc4.x >> 2) + (acc16a.x >> 4) + (acc16b.x >> 4) - sum;
+    part.y += (acc4.y >> 2) + (acc16a.y >> 4) + (acc16b.y >> 4) - sum;
+    part.z += (acc4.z >> 2) + (acc16a.z >> 4) + (acc16b.z >> 4) - sum;
+    part.w += (acc4.w >> 2) + (acc16a.w >> 4) + (acc16b.w >> 4) - sum;
+    partial[rt][wave][lane] = part;
+  }
+  __syncthreads();
+  // wave w finishes row tiles w, w + 4, ...; column 0 of the MFMA tile is the token
+  if (col != 0) return;
+  const float scale = (*gamma_ptr * amax) / 127.0f;
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    if (rt % kWaves != wave || rt >= tiles_here) continue;
+    v4i acc = partial[rt][0][lane];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) add4(acc, partial[rt][w][lane]);
+    store_tile(acc, (tile0 + rt) * kTileRows + 4 * sub, 0, n, scale, acc_out, y_out);
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void k_gemv_direct(const uint4* __restrict__ packed,
                                                           const float* __restrict__ gamma_ptr,
                                                           const int8_t* __restrict__ xq,
@@ -345,6 +484,23 @@ hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* 
 hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t n,
                              int64_t k, int8_t* xq, float* alpha, int32_t* acc, uint16_t* y, hipStream_t s) {
   if (m > 16 || !gemv_fits_lds(m, k)) return hipErrorInvalidValue;
+  if (m == 1 && k / 8 <= 64 * kM1MaxChunks) {
+    const int64_t groups = (k / kTileCols + 3) / 4;
+    const size_t lds = (size_t)kWaves * (size_t)((groups + kWaves - 1) / kWaves) * 256;
+    const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
+    // several row tiles per workgroup once there are more than ~2 per CU
+    const int rt = row_tiles >= 1024 ? 4 : row_tiles >= 512 ? 2 : 1;
+    const dim3 grid((unsigned)((row_tiles + rt - 1) / rt));
+    const uint4* p = reinterpret_cast<const uint4*>(packed);
+    const uint4* xv = reinterpret_cast<const uint4*>(x);
+    if (rt == 4)
+      hipLaunchKernelGGL(k_bitlinear_m1<4>, grid, dim3(kThreads), lds, s, p, gamma, xv, alpha, xq, n, k, acc, y);
+    else if (rt == 2)
+      hipLaunchKernelGGL(k_bitlinear_m1<2>, grid, dim3(kThreads), lds, s, p, gamma, xv, alpha, xq, n, k, acc, y);
+    else
+      hipLaunchKernelGGL(k_bitlinear_m1<1>, grid, dim3(kThreads), lds, s, p, gamma, xv, alpha, xq, n, k, acc, y);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_bitlinear_fused, gemv_grid(m, n), dim3(kThreads), gemv_lds_bytes(m, k), s,
                      reinterpret_cast<const uint4*>(packed), gamma, reinterpret_cast<const uint4*>(x), alpha, xq, m, n,
                      k, acc, y);

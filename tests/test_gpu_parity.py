@@ -296,7 +296,9 @@ def test_linear_is_deterministic():
 # ---------------------------------------------------------------- whole layer in one call
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 33, 64), (1, 2560, 2560), (1, 2560, 6912), (1, 100, 28672), (2, 17, 320),
+@pytest.mark.parametrize("m,n,k", [(1, 33, 64), (1, 2560, 2560), (1, 2560, 6912), (1, 100, 28672),
+                                   # single-token kernel with 2 and 4 row tiles per workgroup, ragged last workgroup
+                                   (1, 8200, 320), (1, 16400, 2560), (1, 16400, 6912), (1, 17000, 7168), (2, 17, 320),
                                    (3, 48, 2560), (4, 3840, 2560), (5, 40, 6912), (16, 64, 1024), (16, 31, 2560),
                                    (17, 40, 2560), (64, 100, 2560), (4, 16, 28672)])
 def test_bitlinear_matches_oracle(m, n, k):
