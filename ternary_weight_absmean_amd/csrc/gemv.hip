@@ -107,51 +107,56 @@ __device__ __forceinline__ void group_partial(int v, int tpr, int* scratch) {
 template <bool kMax>
 __device__ __forceinline__ int row_total(int row, int tpr, const int* scratch) {
   const int g = tpr < 64 ? tpr : 64;
-  const int per_row = tpr / g;  // 1..4 entries per row
+  const int per_row = tpr / g;  // 1..8 entries per row
   int r = scratch[row * per_row];
   for (int i = 1; i < per_row; ++i) r = kMax ? max(r, scratch[row * per_row + i]) : r + scratch[row * per_row + i];
   return r;
 }
 
-constexpr int kXRegChunks = 4;  // bf16 chunks of 8 held in registers between the two quantizer passes
 
 // Whole BitLinear for a block of up to 16 tokens: per-token absmax int8
 // quantization (same arithmetic as bl_quant_act) into LDS, then the codes x
 // int8 product with four scaled accumulators, then the bf16 rescale.
-// Latency-ordered: the weight loads and the activation loads are issued first;
-// the absmax, the activation sum and the waves' partial products each take one
-// LDS round (three barriers in all).
-__global__ __launch_bounds__(kThreads) void k_bitlinear_fused(const uint4* __restrict__ packed,
+// Latency-ordered: the activation loads and the first weight loads are issued
+// first; the absmax and the activation sum each take one LDS round.  A
+// workgroup handles kRT consecutive 16-row tiles, so the quantization is
+// amortized over them; the weight loads of all its tiles form one stream,
+// prefetched a batch ahead, with one buffer resource per tile (reads past a
+// tile, or of a tile past n, return zero codes).
+template <int kRT, int kW>
+__global__ __launch_bounds__(kW * 64) void k_bitlinear_fused(const uint4* __restrict__ packed,
                                                               const float* __restrict__ gamma_ptr,
                                                               const uint4* __restrict__ x, float* __restrict__ alpha,
                                                               int8_t* __restrict__ xq_out, int64_t m, int64_t n,
                                                               int64_t k, int32_t* __restrict__ acc_out,
                                                               uint16_t* __restrict__ y_out) {
+  constexpr int kT = kW * 64;           // threads
+  constexpr int kXC = kW >= 8 ? 8 : 4;  // bf16 chunks of 8 per thread held between the quantizer passes
   extern __shared__ uint4 xs_raw[];  // [rows][k + kLdsRowPad] int8 activations of this token block
   int8_t* xs = reinterpret_cast<int8_t*>(xs_raw);
-  __shared__ v4i partial[kWaves][64];
-  __shared__ int red_max[kThreads / 16];
-  __shared__ int red_sum[kThreads / 16];
+  __shared__ v4i partial[kRT][kW][64];
+  __shared__ int red_max[kT / 16];
+  __shared__ int red_sum[kT / 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int64_t row_tile = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t tile0 = (int64_t)blockIdx.x * kRT;
+  const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
+  const int tiles_here = (int)min((int64_t)kRT, row_tiles - tile0);
   const int64_t tok0 = (int64_t)blockIdx.y * 16;
   const int rows = (int)min((int64_t)16, m - tok0);
-  const int64_t kt_count = k / kTileCols;
-  const int64_t groups = (kt_count + 3) / 4;
+  const int kt_count = (int)(k / kTileCols);
+  const int groups = (kt_count + 3) / 4;
+  const int my_groups = (groups - wave + kW - 1) / kW;
   const int sub = lane >> 4;
   const int col = lane & 15;
-  const uint4* wbase = packed + row_tile * kt_count * (kTileBytes / 16);
-  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+  const bool first_block = blockIdx.x == 0;
 
-  // ---- quantize the token block into LDS.  The activation loads are issued
-  // before the weight loads: loads retire in order, so the quantizer then waits
-  // only for the activations while the weights are still in flight.
+  // ---- activation loads (first: loads retire in order), then the first weight batch
   int rp = 1;
   while (rp < rows) rp <<= 1;
-  const int tpr = kThreads / rp;  // threads per token row
+  const int tpr = kT / rp;  // threads per token row
   const int my_row = tid / tpr;
   const int j0 = tid % tpr;
   const bool row_ok = my_row < rows;
@@ -159,41 +164,46 @@ __global__ __launch_bounds__(kThreads) void k_bitlinear_fused(const uint4* __res
   const int64_t ldx = k + kLdsRowPad;
   const uint4* xb = x + (tok0 + (row_ok ? my_row : 0)) * k8;
   const __amdgpu_buffer_rsrc_t xrsrc = buffer_rsrc(x + tok0 * k8, (uint32_t)(rows * k8 * 16));
-  const bool cached = (k8 + tpr - 1) / tpr <= kXRegChunks;
-  uint4 xr[kXRegChunks];
+  const bool cached = (k8 + tpr - 1) / tpr <= kXC;
+  uint4 xr[kXC];
   if (cached) {
 #pragma unroll
-    for (int c = 0; c < kXRegChunks; ++c) {
+    for (int c = 0; c < kXC; ++c) {
       const int64_t i = j0 + (int64_t)c * tpr;
       xr[c] = buffer_load16(xrsrc, row_ok && i < k8 ? (uint32_t)((my_row * k8 + i) * 16) : kOutOfRange);
     }
   }
-  // weights: the resource spans this row tile; offsets past its last 16x64
-  // tile (tail groups, groups beyond this wave's share) read as zero codes,
-  // which contribute nothing to the products
-  const __amdgpu_buffer_rsrc_t wrsrc = buffer_rsrc(wbase, (uint32_t)(kt_count * kTileBytes));
+  const uint32_t tile_bytes = (uint32_t)(kt_count * kTileBytes);
+  auto tile_rsrc = [&](int rt) {
+    return buffer_rsrc(packed + (tile0 + rt) * kt_count * (kTileBytes / 16), rt < tiles_here ? tile_bytes : 0u);
+  };
+  auto w_off = [&](int gi) { return (uint32_t)((wave + gi * kW) * 1024 + lane * 16); };
   uint4 a_cur[kGroupsPerBatch];
+  {
+    const __amdgpu_buffer_rsrc_t r0 = tile_rsrc(0);
 #pragma unroll
-  for (int u = 0; u < kGroupsPerBatch; ++u)
-    a_cur[u] = buffer_load16(wrsrc, (uint32_t)((wave + u * kWaves) * 1024 + lane * 16));
+    for (int u = 0; u < kGroupsPerBatch; ++u) a_cur[u] = buffer_load16(r0, w_off(u));
+  }
+
+  // ---- quantize the token block into LDS
   uint32_t mx = 0;
   if (cached) {
 #pragma unroll
-    for (int c = 0; c < kXRegChunks; ++c) mx = max(mx, max_abs_bf16x8(xr[c]));
+    for (int c = 0; c < kXC; ++c) mx = max(mx, max_abs_bf16x8(xr[c]));
   } else if (row_ok) {
     for (int64_t i = j0; i < k8; i += tpr) mx = max(mx, max_abs_bf16x8(xb[i]));
   }
   group_partial<true>((int)mx, tpr, red_max);
   __syncthreads();
-  const float amax = __uint_as_float((uint32_t)row_total<true>(my_row < rp ? my_row : 0, tpr, red_max) << 16);
+  const float amax = __uint_as_float((uint32_t)row_total<true>(my_row, tpr, red_max) << 16);
   const float s = 127.0f / fmaxf(amax, 1e-5f);  // IEEE division, as in bl_quant_act
   int sum = 0;
   if (row_ok) {
     uint2* dst = reinterpret_cast<uint2*>(xs + (int64_t)my_row * ldx);
-    uint2* gdst = (blockIdx.x == 0 && xq_out) ? reinterpret_cast<uint2*>(xq_out + (tok0 + my_row) * k) : nullptr;
+    uint2* gdst = (first_block && xq_out) ? reinterpret_cast<uint2*>(xq_out + (tok0 + my_row) * k) : nullptr;
     if (cached) {
 #pragma unroll
-      for (int c = 0; c < kXRegChunks; ++c) {
+      for (int c = 0; c < kXC; ++c) {
         const int64_t i = j0 + (int64_t)c * tpr;
         if (i < k8) {
           const uint2 q = make_uint2(quant2(xr[c].x, s, sum) | (quant2(xr[c].y, s, sum) << 16),
@@ -211,59 +221,72 @@ __global__ __launch_bounds__(kThreads) void k_bitlinear_fused(const uint4* __res
         if (gdst) gdst[i] = q;
       }
     }
-    if (j0 == 0 && blockIdx.x == 0 && alpha) alpha[tok0 + my_row] = amax;
+    if (j0 == 0 && first_block && alpha) alpha[tok0 + my_row] = amax;
   }
   group_partial<false>(sum, tpr, red_sum);
   __syncthreads();
 
-  // ---- K loop: codes times activations, four scaled accumulators
+  // ---- weight stream: codes times activations, four scaled accumulators per tile
   const bool has_tok = col < rows;
   const int8_t* xrow = xs + (int64_t)(has_tok ? col : 0) * ldx;
-  v4i acc1 = {0, 0, 0, 0}, acc4 = acc1, acc16a = acc1, acc16b = acc1;
-  for (int64_t g0 = wave; g0 < groups; g0 += (int64_t)kWaves * kGroupsPerBatch) {
-    uint4 a_next[kGroupsPerBatch];
-    const int64_t gn = g0 + (int64_t)kWaves * kGroupsPerBatch;
 #pragma unroll
-    for (int u = 0; u < kGroupsPerBatch; ++u)
-      a_next[u] = buffer_load16(wrsrc, (uint32_t)((gn + u * kWaves) * 1024 + lane * 16));
+  for (int rt = 0; rt < kRT; ++rt) {
+    v4i acc1 = {0, 0, 0, 0}, acc4 = acc1, acc16a = acc1, acc16b = acc1;
+    const __amdgpu_buffer_rsrc_t cur_rsrc = tile_rsrc(rt);
+    const __amdgpu_buffer_rsrc_t next_rsrc = tile_rsrc(rt + 1);  // empty past the last tile
+    for (int gi = 0; gi < my_groups; gi += kGroupsPerBatch) {
+      const bool same = gi + kGroupsPerBatch < my_groups;
+      const int ngi = same ? gi + kGroupsPerBatch : 0;
+      uint4 a_next[kGroupsPerBatch];
 #pragma unroll
-    for (int u = 0; u < kGroupsPerBatch; ++u) {
-      const int64_t g = g0 + (int64_t)u * kWaves;
-      // tiles past the end carry zero codes, so any in-bounds activation
-      // bytes will do: clamp to the last tile
-      const int64_t kt = min(4 * g + sub, kt_count - 1);
-      uint4 b[4];
-      const uint4* xt = reinterpret_cast<const uint4*>(xrow) + kt * 4;
+      for (int u = 0; u < kGroupsPerBatch; ++u)
+        a_next[u] = buffer_load16(same ? cur_rsrc : next_rsrc, w_off(ngi + u));
 #pragma unroll
-      for (int f = 0; f < 4; ++f) b[f] = xt[f];
-      acc1 = mfma_16x16x64(mask4(a_cur[u], 0x03030303u, 0), as_v4i(b[0]), acc1);
-      acc4 = mfma_16x16x64(mask4(a_cur[u], 0x0C0C0C0Cu, 0), as_v4i(b[1]), acc4);
-      acc16a = mfma_16x16x64(mask4(a_cur[u], 0x30303030u, 0), as_v4i(b[2]), acc16a);
-      acc16b = mfma_16x16x64(mask4(a_cur[u], 0x30303030u, 2), as_v4i(b[3]), acc16b);
+      for (int u = 0; u < kGroupsPerBatch; ++u) {
+        // tiles past k carry zero codes, so any in-bounds activation bytes will do
+        const int kt = min(4 * (wave + (gi + u) * kW) + sub, kt_count - 1);
+        const uint4* xt = reinterpret_cast<const uint4*>(xrow) + kt * 4;
+        uint4 b[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) b[f] = xt[f];
+        acc1 = mfma_16x16x64(mask4(a_cur[u], 0x03030303u, 0), as_v4i(b[0]), acc1);
+        acc4 = mfma_16x16x64(mask4(a_cur[u], 0x0C0C0C0Cu, 0), as_v4i(b[1]), acc4);
+        acc16a = mfma_16x16x64(mask4(a_cur[u], 0x30303030u, 0), as_v4i(b[2]), acc16a);
+        acc16b = mfma_16x16x64(mask4(a_cur[u], 0x30303030u, 2), as_v4i(b[3]), acc16b);
+      }
+#pragma unroll
+      for (int u = 0; u < kGroupsPerBatch; ++u) a_cur[u] = a_next[u];
     }
+    if (my_groups == 0 && rt + 1 < kRT) {  // keep the stream aligned: nothing was loaded for this tile
 #pragma unroll
-    for (int u = 0; u < kGroupsPerBatch; ++u) a_cur[u] = a_next[u];
+      for (int u = 0; u < kGroupsPerBatch; ++u) a_cur[u] = buffer_load16(next_rsrc, w_off(u));
+    }
+    // exact: acc4 holds 4x, acc16a/b 16x the code sums
+    v4i part = acc1;
+    part.x += (acc4.x >> 2) + (acc16a.x >> 4) + (acc16b.x >> 4);
+    part.y += (acc4.y >> 2) + (acc16a.y >> 4) + (acc16b.y >> 4);
+    part.z += (acc4.z >> 2) + (acc16a.z >> 4) + (acc16b.z >> 4);
+    part.w += (acc4.w >> 2) + (acc16a.w >> 4) + (acc16b.w >> 4);
+    partial[rt][wave][lane] = part;
   }
-  // exact: acc4 holds 4x, acc16a/b 16x the code sums
-  v4i part = acc1;
-  part.x += (acc4.x >> 2) + (acc16a.x >> 4) + (acc16b.x >> 4);
-  part.y += (acc4.y >> 2) + (acc16a.y >> 4) + (acc16b.y >> 4);
-  part.z += (acc4.z >> 2) + (acc16a.z >> 4) + (acc16b.z >> 4);
-  part.w += (acc4.w >> 2) + (acc16a.w >> 4) + (acc16b.w >> 4);
-  partial[wave][lane] = part;
   __syncthreads();
-  if (wave != 0 || !has_tok) return;
-  v4i acc = partial[0][lane];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) add4(acc, partial[w][lane]);
-  const int xsum = row_total<false>(col, kThreads / rp, red_sum);  // sum q*x = sum c*x - sum x
-  acc.x -= xsum;
-  acc.y -= xsum;
-  acc.z -= xsum;
-  acc.w -= xsum;
-  const float row_amax = __uint_as_float((uint32_t)row_total<true>(col, kThreads / rp, red_max) << 16);
+  // wave w finishes row tiles w, w + 4, ... for the block's tokens
+  if (!has_tok) return;
+  const int xsum = row_total<false>(col, kT / rp, red_sum);  // sum q*x = sum c*x - sum x
+  const float row_amax = __uint_as_float((uint32_t)row_total<true>(col, kT / rp, red_max) << 16);
   const float scale = (*gamma_ptr * row_amax) / 127.0f;
-  store_tile(acc, row_tile * kTileRows + 4 * sub, tok0 + col, n, scale, acc_out, y_out);
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    if (rt % kW != wave || rt >= tiles_here) continue;
+    v4i acc = partial[rt][0][lane];
+#pragma unroll
+    for (int w = 1; w < kW; ++w) add4(acc, partial[rt][w][lane]);
+    acc.x -= xsum;
+    acc.y -= xsum;
+    acc.z -= xsum;
+    acc.w -= xsum;
+    store_tile(acc, (tile0 + rt) * kTileRows + 4 * sub, tok0 + col, n, scale, acc_out, y_out);
+  }
 }
 
 constexpr int kM1MaxChunks = 14;  // bf16 chunks of 8 per lane: single-token rows up to k = 7168
@@ -501,9 +524,23 @@ hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const ui
       hipLaunchKernelGGL(k_bitlinear_m1<1>, grid, dim3(kThreads), lds, s, p, gamma, xv, alpha, xq, n, k, acc, y);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(k_bitlinear_fused, gemv_grid(m, n), dim3(kThreads), gemv_lds_bytes(m, k), s,
-                     reinterpret_cast<const uint4*>(packed), gamma, reinterpret_cast<const uint4*>(x), alpha, xq, m, n,
-                     k, acc, y);
+  const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
+  const int rt = m == 1 ? (row_tiles >= 1024 ? 2 : 1) : (row_tiles >= 1024 ? 4 : row_tiles >= 512 ? 2 : 1);
+  const dim3 grid((unsigned)((row_tiles + rt - 1) / rt), (unsigned)((m + 15) / 16));
+  const uint4* p = reinterpret_cast<const uint4*>(packed);
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  const size_t lds = gemv_lds_bytes(m, k);
+  // long rows (>= 64 column groups): 8 waves per workgroup, one row tile each
+  if (k >= 16384) {
+    const dim3 g1((unsigned)row_tiles, (unsigned)((m + 15) / 16));
+    hipLaunchKernelGGL((k_bitlinear_fused<1, 8>), g1, dim3(512), lds, s, p, gamma, xv, alpha, xq, m, n, k, acc, y);
+  } else if (rt == 4) {
+    hipLaunchKernelGGL((k_bitlinear_fused<4, 4>), grid, dim3(256), lds, s, p, gamma, xv, alpha, xq, m, n, k, acc, y);
+  } else if (rt == 2) {
+    hipLaunchKernelGGL((k_bitlinear_fused<2, 4>), grid, dim3(256), lds, s, p, gamma, xv, alpha, xq, m, n, k, acc, y);
+  } else {
+    hipLaunchKernelGGL((k_bitlinear_fused<1, 4>), grid, dim3(256), lds, s, p, gamma, xv, alpha, xq, m, n, k, acc, y);
+  }
   return hipGetLastError();
 }
 

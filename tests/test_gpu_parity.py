@@ -298,7 +298,11 @@ def test_linear_is_deterministic():
 
 @pytest.mark.parametrize("m,n,k", [(1, 33, 64), (1, 2560, 2560), (1, 2560, 6912), (1, 100, 28672),
                                    # single-token kernel with 2 and 4 row tiles per workgroup, ragged last workgroup
-                                   (1, 8200, 320), (1, 16400, 2560), (1, 16400, 6912), (1, 17000, 7168), (2, 17, 320),
+                                   (1, 8200, 320), (1, 16400, 2560), (1, 16400, 6912), (1, 17000, 7168),
+                                   # block-quantizing kernel with 2 and 4 row tiles per workgroup
+                                   (1, 16400, 8192), (3, 8200, 2560), (16, 16400, 1024), (2, 17, 320),
+                                   # eight-wave kernel for long rows (k >= 16384)
+                                   (1, 530, 16384), (7, 70, 16448), (16, 40, 32768),
                                    (3, 48, 2560), (4, 3840, 2560), (5, 40, 6912), (16, 64, 1024), (16, 31, 2560),
                                    (17, 40, 2560), (64, 100, 2560), (4, 16, 28672)])
 def test_bitlinear_matches_oracle(m, n, k):
