@@ -62,6 +62,83 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Per-token int8 code of one finite bf16 x: round_half_even(fl32(x * s)),
+// for s = fl32(127 / max(amax, 1e-5)) and |x| <= amax.  Adding 1.5 * 2^23
+// to the fp32 product rounds it to an integer in the low mantissa bits
+// (ties to even: the sum's parity is the integer's, 1.5 * 2^23 being even),
+// so the low byte of the sum is the code in two's complement.  The product
+// is at most 127 * (1 + 2^-24) in magnitude, so every code lies in
+// [-127, 127] and the clamp to [-128, 127] never binds.
+__device__ __forceinline__ uint32_t act_code_bits(uint32_t bf16_in_high_half, float s) {
+  return __float_as_uint(__fadd_rn(__fmul_rn(__uint_as_float(bf16_in_high_half), s), 12582912.0f));
+}
+
+// Codes of the eight bf16 of a 16-byte chunk, packed in element order into
+// 8 bytes; their sum is added to `sum`.
+__device__ __forceinline__ uint2 act_codes8(const uint4& v, float s, int& sum) {
+  auto four = [&](uint32_t d0, uint32_t d1) {
+    const uint32_t a0 = act_code_bits(d0 << 16, s), a1 = act_code_bits(d0 & 0xFFFF0000u, s);
+    const uint32_t a2 = act_code_bits(d1 << 16, s), a3 = act_code_bits(d1 & 0xFFFF0000u, s);
+    // v_perm_b32: selector bytes 0-3 pick bytes of the second operand, 4-7 of the first, 0x0c gives 0
+    const uint32_t p01 = __builtin_amdgcn_perm(a1, a0, 0x0c0c0400u);
+    const uint32_t p23 = __builtin_amdgcn_perm(a3, a2, 0x0c0c0400u);
+    const uint32_t q = __builtin_amdgcn_perm(p23, p01, 0x05040100u);
+    sum = __builtin_amdgcn_sdot4((int)q, 0x01010101, sum, false);
+    return q;
+  };
+  const uint32_t lo = four(v.x, v.y);
+  const uint32_t hi = four(v.z, v.w);
+  return make_uint2(lo, hi);
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Running max of |bf16| magnitude bits over 16-byte chunks, two lanes of
+// 16 bits at a time (v_pk_max_u16); magnitude bits order like the values.
+__device__ __forceinline__ u16x2 absmax_step(u16x2 m, const uint4& v) {
+  auto mag = [](uint32_t d) { return __builtin_bit_cast(u16x2, d & 0x7FFF7FFFu); };
+  m = __builtin_elementwise_max(m, mag(v.x));
+  m = __builtin_elementwise_max(m, mag(v.y));
+  m = __builtin_elementwise_max(m, mag(v.z));
+  return __builtin_elementwise_max(m, mag(v.w));
+}
+
+// One fp32 through the vector memory path: issued where it is written and
+// waited for only where it is used (a scalar load of a kernel argument's
+// target is otherwise sunk to its use, adding a round trip there).
+__device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t offset) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, offset, 0, 0));
+}
+
+// Reduction over aligned groups of `g` lanes (g a power of two up to 64) with
+// DPP lane moves inside each 16-lane row (no LDS round trip) and, for groups
+// wider than a row, cross-lane permutes.  After each step every lane of a
+// block holds the block's reduction, so the mirrors pair blocks correctly:
+// quad_perm [1,0,3,2] and [2,3,0,1] reduce quads, row_half_mirror (lane i of
+// an 8-lane half row takes lane 7 - i) joins quad pairs, row_mirror (15 - i)
+// joins the two halves of a row.  Every lane ends with its group's value.
+template <bool kMax>
+__device__ __forceinline__ int lane_group_reduce(int v, int g) {
+  auto op = [](int a, int b) { return kMax ? max(a, b) : a + b; };
+  if (g >= 2) v = op(v, __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false));
+  if (g >= 4) v = op(v, __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false));
+  if (g >= 8) v = op(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false));
+  if (g >= 16) v = op(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false));
+  if (g >= 32) v = op(v, __shfl_xor(v, 16, 64));
+  if (g >= 64) v = op(v, __shfl_xor(v, 32, 64));
+  return v;
+}
+
+// Whole-wave reduction, wave-uniform result: DPP within rows, then the four
+// row results read as scalars.
+template <bool kMax>
+__device__ __forceinline__ int wave_reduce(int v) {
+  v = lane_group_reduce<kMax>(v, 16);
+  const int r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const int r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return kMax ? max(max(r0, r1), max(r2, r3)) : (r0 + r1) + (r2 + r3);
+}
+
 // v_mfma_i32_16x16x64_i8: D[16][16] += A[16][64] * B[64][16].  Lane l supplies
 // row l%16 of A and column l%16 of B, 16 int8 each, for the same 16 k-slots
 // (lane group l/16); D lands as rows 4*(l/16) + i, column l%16 in element i.

@@ -97,10 +97,7 @@ __device__ __forceinline__ uint32_t quant2(uint32_t two_bf16, float s, int& sum)
 template <bool kMax>
 __device__ __forceinline__ void group_partial(int v, int tpr, int* scratch) {
   const int g = tpr < 64 ? tpr : 64;
-  for (int off = g >> 1; off > 0; off >>= 1) {
-    int o = __shfl_xor(v, off, 64);
-    v = kMax ? max(v, o) : v + o;
-  }
+  v = lane_group_reduce<kMax>(v, g);
   if ((threadIdx.x % g) == 0) scratch[threadIdx.x / g] = v;
 }
 
@@ -184,6 +181,9 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_fused(const uint4* __rest
 #pragma unroll
     for (int u = 0; u < kGroupsPerBatch; ++u) a_cur[u] = buffer_load16(r0, w_off(u));
   }
+  const float gamma = buffer_load_f32(buffer_rsrc(gamma_ptr, 4), 0);
+  // keep these loads here, in flight while the activations are reduced
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- quantize the token block into LDS
   uint32_t mx = 0;
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_fused(const uint4* __rest
   if (!has_tok) return;
   const int xsum = row_total<false>(col, kT / rp, red_sum);  // sum q*x = sum c*x - sum x
   const float row_amax = __uint_as_float((uint32_t)row_total<true>(col, kT / rp, red_max) << 16);
-  const float scale = (*gamma_ptr * row_amax) / 127.0f;
+  const float scale = (gamma * row_amax) / 127.0f;
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
     if (rt % kW != wave || rt >= tiles_here) continue;
@@ -289,49 +289,67 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_fused(const uint4* __rest
   }
 }
 
-constexpr int kM1MaxChunks = 14;  // bf16 chunks of 8 per lane: single-token rows up to k = 7168
+constexpr int kM1MaxSlots = 14;  // 16-byte bf16 chunks per lane: single-token rows up to k = 7168
 
 // Single-token BitLinear (m = 1, k <= 7168) without a barrier before the
-// products.  Every wave loads the whole bf16 row (lane l holds chunks of 8
-// elements l, l + 64, ...), reduces its absmax in registers, and quantizes
-// only the 256-column groups it multiplies (groups w, w + 4, ...) into its
-// own LDS region, which only it reads.  Each wave subtracts the activation
-// sum of its own columns from its partial products, so the waves' partials
-// add up to sum q*x; one barrier then combines them.  A workgroup handles
-// kRT consecutive 16-row tiles, reusing the quantized row; the weight loads
-// of all its tiles form one stream, prefetched a batch ahead.
-template <int kRT>
+// products.  Every wave loads the whole bf16 row, reduces its absmax in
+// registers, and quantizes only the 256-column groups it multiplies (groups
+// w, w + 4, ...) into its own LDS region, which only it reads.  The row is
+// loaded in a wave-dependent order so that the wave's own groups come first
+// and fill all 64 lanes: slot i of lane l holds chunk (l % 32) of the wave's
+// group rank 2i + l / 32, own groups ranked first, then the others by index.
+// Each wave subtracts the activation sum of its own columns from its partial
+// products, so the waves' partials add up to sum q*x; one barrier then
+// combines them.  A workgroup handles kRT consecutive 16-row tiles, reusing
+// the quantized row; the weight loads of all its tiles form one stream,
+// prefetched a batch ahead.  kC = slots per lane (ceil(groups / 2)).
+template <int kRT, int kC>
 __global__ __launch_bounds__(kThreads) void k_bitlinear_m1(const uint4* __restrict__ packed,
                                                            const float* __restrict__ gamma_ptr,
                                                            const uint4* __restrict__ x, float* __restrict__ alpha,
-                                                           int8_t* __restrict__ xq_out, int64_t n, int64_t k,
+                                                           int8_t* __restrict__ xq_out, int n, int k,
                                                            int32_t* __restrict__ acc_out, uint16_t* __restrict__ y_out) {
   extern __shared__ uint4 xw_raw[];  // [wave][groups of this wave][256 bytes]
   __shared__ v4i partial[kRT][kWaves][64];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t tile0 = (int64_t)blockIdx.x * kRT;
-  const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
-  const int tiles_here = (int)min((int64_t)kRT, row_tiles - tile0);
-  const int kt_count = (int)(k / kTileCols);
+  const int tile0 = blockIdx.x * kRT;
+  const int row_tiles = (n + kTileRows - 1) / kTileRows;
+  const int tiles_here = min(kRT, row_tiles - tile0);
+  const int kt_count = k / kTileCols;
   const int groups = (kt_count + 3) / 4;
   const int my_groups = (groups - wave + kWaves - 1) / kWaves;
   const int max_groups = (groups + kWaves - 1) / kWaves;
   const int sub = lane >> 4;
   const int col = lane & 15;
-  const int k8 = (int)(k / 8);
+  const int half = lane >> 5;
+  const int r = lane & 31;
 
+  // group of rank u in this wave's order: own groups w + 4u first, then the
+  // rest ascending (the v-th group not congruent to w mod 4)
+  auto group_of_rank = [&](int u) {
+    if (u < my_groups) return wave + kWaves * u;
+    const int v = u - my_groups;
+    const int j = v % 3;
+    return (v / 3) * kWaves + j + (j >= wave ? 1 : 0);
+  };
   // activations first (loads retire in order), then the first weight batch
-  const __amdgpu_buffer_rsrc_t xrsrc = buffer_rsrc(x, (uint32_t)(k8 * 16));
-  uint4 xr[kM1MaxChunks];
+  const __amdgpu_buffer_rsrc_t xrsrc = buffer_rsrc(x, (uint32_t)(k * 2));
+  uint4 xr[kC];
 #pragma unroll
-  for (int i = 0; i < kM1MaxChunks; ++i) xr[i] = buffer_load16(xrsrc, (uint32_t)((lane + 64 * i) * 16));
+  for (int i = 0; i < kC; ++i) {
+    // wave-uniform group indices of the two ranks, then one select per lane
+    const int g0 = group_of_rank(2 * i), g1 = group_of_rank(2 * i + 1);
+    const uint32_t o0 = g0 < groups ? (uint32_t)(g0 * 512) : kOutOfRange;
+    const uint32_t o1 = g1 < groups ? (uint32_t)(g1 * 512) : kOutOfRange;
+    xr[i] = buffer_load16(xrsrc, (half ? o1 : o0) + (uint32_t)(r * 16));
+  }
   // Weights: one resource per row tile, so that groups past k (and a whole
   // tile past n) read as zero codes instead of the next tile's bytes.
   const uint32_t tile_bytes = (uint32_t)(kt_count * kTileBytes);
   auto tile_rsrc = [&](int rt) {
-    return buffer_rsrc(packed + (tile0 + rt) * kt_count * (kTileBytes / 16), rt < tiles_here ? tile_bytes : 0u);
+    return buffer_rsrc(packed + (size_t)(tile0 + rt) * kt_count * (kTileBytes / 16), rt < tiles_here ? tile_bytes : 0u);
   };
   // this wave's gi-th group within a row tile
   auto w_off = [&](int gi) { return (uint32_t)((wave + gi * kWaves) * 1024 + lane * 16); };
@@ -341,34 +359,35 @@ __global__ __launch_bounds__(kThreads) void k_bitlinear_m1(const uint4* __restri
 #pragma unroll
     for (int u = 0; u < kGroupsPerBatch; ++u) a_cur[u] = buffer_load16(r0, w_off(u));
   }
+  const float gamma = buffer_load_f32(buffer_rsrc(gamma_ptr, 4), 0);
+  // keep these loads here, in flight while the activations are reduced
+  __builtin_amdgcn_sched_barrier(0);
 
   // absmax of the whole row, in this wave alone (chunks past k read as zero)
-  uint32_t mx = 0;
+  u16x2 m2 = {0, 0};
 #pragma unroll
-  for (int i = 0; i < kM1MaxChunks; ++i) mx = max(mx, max_abs_bf16x8(xr[i]));
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
-  const float amax = __uint_as_float(mx << 16);
+  for (int i = 0; i < kC; ++i) m2 = absmax_step(m2, xr[i]);
+  const int mx = wave_reduce<true>((int)max(m2.x, m2.y));
+  const float amax = __uint_as_float((uint32_t)mx << 16);
   const float s = 127.0f / fmaxf(amax, 1e-5f);  // IEEE division, as in bl_quant_act
 
-  // quantize this wave's groups: chunk j belongs to group j / 32, owned by
-  // wave (j / 32) % 4; it lands at byte 8 * (j % 32) of that group's region
+  // quantize this wave's own groups: rank t = 2i + half lands at byte
+  // 256 t + 8 r of the wave's region
   int8_t* region = reinterpret_cast<int8_t*>(xw_raw) + wave * max_groups * 256;
   uint2* gdst = (blockIdx.x == 0 && xq_out) ? reinterpret_cast<uint2*>(xq_out) : nullptr;
   int sum = 0;
 #pragma unroll
-  for (int i = 0; i < kM1MaxChunks; ++i) {
-    const int j = lane + 64 * i;
-    const int g = j >> 5;
-    if (j < k8 && (g & (kWaves - 1)) == wave) {
-      const uint2 q = make_uint2(quant2(xr[i].x, s, sum) | (quant2(xr[i].y, s, sum) << 16),
-                                 quant2(xr[i].z, s, sum) | (quant2(xr[i].w, s, sum) << 16));
-      reinterpret_cast<uint2*>(region + (g / kWaves) * 256)[j & 31] = q;
-      if (gdst) gdst[j] = q;
+  for (int i = 0; i < kC; ++i) {
+    if (2 * i >= my_groups) break;  // wave-uniform
+    const int t = 2 * i + half;
+    if (t < my_groups) {
+      const uint2 q = act_codes8(xr[i], s, sum);
+      reinterpret_cast<uint2*>(region + t * 256)[r] = q;
+      const int chunk = (wave + kWaves * t) * 32 + r;
+      if (gdst && chunk < k / 8) gdst[chunk] = q;
     }
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+  sum = wave_reduce<false>(sum);
   if (blockIdx.x == 0 && wave == 0 && lane == 0 && alpha) alpha[0] = amax;
   // this wave's own LDS writes are complete before its reads below
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
@@ -417,14 +436,14 @@ __global__ __launch_bounds__(kThreads) void k_bitlinear_m1(const uint4* __restri
   __syncthreads();
   // wave w finishes row tiles w, w + 4, ...; column 0 of the MFMA tile is the token
   if (col != 0) return;
-  const float scale = (*gamma_ptr * amax) / 127.0f;
+  const float scale = (gamma * amax) / 127.0f;
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
     if (rt % kWaves != wave || rt >= tiles_here) continue;
     v4i acc = partial[rt][0][lane];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) add4(acc, partial[rt][w][lane]);
-    store_tile(acc, (tile0 + rt) * kTileRows + 4 * sub, 0, n, scale, acc_out, y_out);
+    store_tile(acc, (int64_t)(tile0 + rt) * kTileRows + 4 * sub, 0, n, scale, acc_out, y_out);
   }
 }
 
@@ -447,6 +466,9 @@ __global__ __launch_bounds__(kThreads) void k_gemv_direct(const uint4* __restric
   const bool has_tok = tok < m;
   const uint4* wbase = packed + row_tile * kt_count * (kTileBytes / 16);
   const int rows = (int)min((int64_t)16, m - tok0);
+  // scales read now (a load at the epilogue would add a memory round trip)
+  const float gamma = buffer_load_f32(buffer_rsrc(gamma_ptr, 4), 0);
+  const float alpha_tok = buffer_load_f32(buffer_rsrc(alpha + tok0, (uint32_t)(rows * 4)), has_tok ? col * 4 : kOutOfRange);
   // resources over this row tile and this token block; offsets past either
   // read as zero (tail groups, absent tokens), and a zero activation byte
   // makes the product zero whatever the trit
@@ -482,7 +504,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_direct(const uint4* __restric
   v4i sum = partial[0][lane];
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) add4(sum, partial[w][lane]);
-  const float scale = (*gamma_ptr * alpha[tok]) / 127.0f;
+  const float scale = (gamma * alpha_tok) / 127.0f;
   store_tile(sum, row_tile * kTileRows + 4 * sub, tok, n, scale, acc_out, y_out);
 }
 
@@ -507,7 +529,7 @@ hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* 
 hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t n,
                              int64_t k, int8_t* xq, float* alpha, int32_t* acc, uint16_t* y, hipStream_t s) {
   if (m > 16 || !gemv_fits_lds(m, k)) return hipErrorInvalidValue;
-  if (m == 1 && k / 8 <= 64 * kM1MaxChunks) {
+  if (m == 1 && k / 8 <= 64 * kM1MaxSlots) {
     const int64_t groups = (k / kTileCols + 3) / 4;
     const size_t lds = (size_t)kWaves * (size_t)((groups + kWaves - 1) / kWaves) * 256;
     const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
@@ -516,12 +538,26 @@ hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const ui
     const dim3 grid((unsigned)((row_tiles + rt - 1) / rt));
     const uint4* p = reinterpret_cast<const uint4*>(packed);
     const uint4* xv = reinterpret_cast<const uint4*>(x);
-    if (rt == 4)
-      hipLaunchKernelGGL(k_bitlinear_m1<4>, grid, dim3(kThreads), lds, s, p, gamma, xv, alpha, xq, n, k, acc, y);
-    else if (rt == 2)
-      hipLaunchKernelGGL(k_bitlinear_m1<2>, grid, dim3(kThreads), lds, s, p, gamma, xv, alpha, xq, n, k, acc, y);
-    else
-      hipLaunchKernelGGL(k_bitlinear_m1<1>, grid, dim3(kThreads), lds, s, p, gamma, xv, alpha, xq, n, k, acc, y);
+    const int ni = (int)n, ki = (int)k;
+    // slots per lane: ceil(groups / 2), 5 for rows up to 2560 columns
+    if (groups <= 10) {
+      if (rt == 4)
+        hipLaunchKernelGGL((k_bitlinear_m1<4, 5>), grid, dim3(kThreads), lds, s, p, gamma, xv, alpha, xq, ni, ki, acc, y);
+      else if (rt == 2)
+        hipLaunchKernelGGL((k_bitlinear_m1<2, 5>), grid, dim3(kThreads), lds, s, p, gamma, xv, alpha, xq, ni, ki, acc, y);
+      else
+        hipLaunchKernelGGL((k_bitlinear_m1<1, 5>), grid, dim3(kThreads), lds, s, p, gamma, xv, alpha, xq, ni, ki, acc, y);
+    } else {
+      if (rt == 4)
+        hipLaunchKernelGGL((k_bitlinear_m1<4, kM1MaxSlots>), grid, dim3(kThreads), lds, s, p, gamma, xv, alpha, xq, ni, ki,
+                           acc, y);
+      else if (rt == 2)
+        hipLaunchKernelGGL((k_bitlinear_m1<2, kM1MaxSlots>), grid, dim3(kThreads), lds, s, p, gamma, xv, alpha, xq, ni, ki,
+                           acc, y);
+      else
+        hipLaunchKernelGGL((k_bitlinear_m1<1, kM1MaxSlots>), grid, dim3(kThreads), lds, s, p, gamma, xv, alpha, xq, ni, ki,
+                           acc, y);
+    }
     return hipGetLastError();
   }
   const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
