@@ -291,10 +291,12 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_fused(const uint4* __rest
 
 constexpr int kM1MaxSlots = 14;  // 16-byte bf16 chunks per lane: single-token rows up to k = 7168
 
-// Single-token BitLinear (m = 1, k <= 7168) without a barrier before the
-// products.  Every wave loads the whole bf16 row, reduces its absmax in
-// registers, and quantizes only the 256-column groups it multiplies (groups
-// w, w + 4, ...) into its own LDS region, which only it reads.  The row is
+// Single-token BitLinear (m = 1, k <= 7168).  Wave w of kW multiplies the
+// 256-column groups w, w + kW, ... and quantizes exactly those into its own
+// LDS region, which only it reads.  The row's absmax is either reduced by
+// every wave over the whole row in registers (no barrier before the
+// products), or, with kShare, from per-wave maxima of the own groups
+// exchanged through LDS (one barrier, a quarter of the loads).  The row is
 // loaded in a wave-dependent order so that the wave's own groups come first
 // and fill all 64 lanes: slot i of lane l holds chunk (l % 32) of the wave's
 // group rank 2i + l / 32, own groups ranked first, then the others by index.
@@ -302,15 +304,17 @@ constexpr int kM1MaxSlots = 14;  // 16-byte bf16 chunks per lane: single-token r
 // products, so the waves' partials add up to sum q*x; one barrier then
 // combines them.  A workgroup handles kRT consecutive 16-row tiles, reusing
 // the quantized row; the weight loads of all its tiles form one stream,
-// prefetched a batch ahead.  kC = slots per lane (ceil(groups / 2)).
-template <int kRT, int kC>
-__global__ __launch_bounds__(kThreads) void k_bitlinear_m1(const uint4* __restrict__ packed,
+// prefetched a batch ahead.  kC = slots per lane (ceil(groups / 2), or
+// ceil(own groups / 2) with kShare).
+template <int kRT, int kC, int kW, bool kShare>
+__global__ __launch_bounds__(kW * 64) void k_bitlinear_m1(const uint4* __restrict__ packed,
                                                            const float* __restrict__ gamma_ptr,
                                                            const uint4* __restrict__ x, float* __restrict__ alpha,
                                                            int8_t* __restrict__ xq_out, int n, int k,
                                                            int32_t* __restrict__ acc_out, uint16_t* __restrict__ y_out) {
   extern __shared__ uint4 xw_raw[];  // [wave][groups of this wave][256 bytes]
-  __shared__ v4i partial[kRT][kWaves][64];
+  __shared__ v4i partial[kRT][kW][64];
+  __shared__ int wave_max[kW];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -319,20 +323,21 @@ __global__ __launch_bounds__(kThreads) void k_bitlinear_m1(const uint4* __restri
   const int tiles_here = min(kRT, row_tiles - tile0);
   const int kt_count = k / kTileCols;
   const int groups = (kt_count + 3) / 4;
-  const int my_groups = (groups - wave + kWaves - 1) / kWaves;
-  const int max_groups = (groups + kWaves - 1) / kWaves;
+  const int my_groups = (groups - wave + kW - 1) / kW;
+  const int max_groups = (groups + kW - 1) / kW;
   const int sub = lane >> 4;
   const int col = lane & 15;
   const int half = lane >> 5;
   const int r = lane & 31;
 
-  // group of rank u in this wave's order: own groups w + 4u first, then the
-  // rest ascending (the v-th group not congruent to w mod 4)
+  // group of rank u in this wave's order: own groups w + kW u first, then
+  // the rest ascending (the v-th group not congruent to w mod kW)
   auto group_of_rank = [&](int u) {
-    if (u < my_groups) return wave + kWaves * u;
+    if (u < my_groups) return wave + kW * u;
+    if (kShare) return groups;  // not loaded
     const int v = u - my_groups;
-    const int j = v % 3;
-    return (v / 3) * kWaves + j + (j >= wave ? 1 : 0);
+    const int j = v % (kW - 1);
+    return (v / (kW - 1)) * kW + j + (j >= wave ? 1 : 0);
   };
   // activations first (loads retire in order), then the first weight batch
   const __amdgpu_buffer_rsrc_t xrsrc = buffer_rsrc(x, (uint32_t)(k * 2));
@@ -352,7 +357,7 @@ __global__ __launch_bounds__(kThreads) void k_bitlinear_m1(const uint4* __restri
     return buffer_rsrc(packed + (size_t)(tile0 + rt) * kt_count * (kTileBytes / 16), rt < tiles_here ? tile_bytes : 0u);
   };
   // this wave's gi-th group within a row tile
-  auto w_off = [&](int gi) { return (uint32_t)((wave + gi * kWaves) * 1024 + lane * 16); };
+  auto w_off = [&](int gi) { return (uint32_t)((wave + gi * kW) * 1024 + lane * 16); };
   uint4 a_cur[kGroupsPerBatch];
   {
     const __amdgpu_buffer_rsrc_t r0 = tile_rsrc(0);
@@ -367,7 +372,13 @@ __global__ __launch_bounds__(kThreads) void k_bitlinear_m1(const uint4* __restri
   u16x2 m2 = {0, 0};
 #pragma unroll
   for (int i = 0; i < kC; ++i) m2 = absmax_step(m2, xr[i]);
-  const int mx = wave_reduce<true>((int)max(m2.x, m2.y));
+  int mx = wave_reduce<true>((int)max(m2.x, m2.y));
+  if (kShare) {
+    if (lane == 0) wave_max[wave] = mx;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kW; ++w) mx = max(mx, wave_max[w]);
+  }
   const float amax = __uint_as_float((uint32_t)mx << 16);
   const float s = 127.0f / fmaxf(amax, 1e-5f);  // IEEE division, as in bl_quant_act
 
@@ -383,7 +394,7 @@ __global__ __launch_bounds__(kThreads) void k_bitlinear_m1(const uint4* __restri
     if (t < my_groups) {
       const uint2 q = act_codes8(xr[i], s, sum);
       reinterpret_cast<uint2*>(region + t * 256)[r] = q;
-      const int chunk = (wave + kWaves * t) * 32 + r;
+      const int chunk = (wave + kW * t) * 32 + r;
       if (gdst && chunk < k / 8) gdst[chunk] = q;
     }
   }
@@ -434,15 +445,15 @@ __global__ __launch_bounds__(kThreads) void k_bitlinear_m1(const uint4* __restri
     partial[rt][wave][lane] = part;
   }
   __syncthreads();
-  // wave w finishes row tiles w, w + 4, ...; column 0 of the MFMA tile is the token
+  // wave w finishes row tiles w, w + kW, ...; column 0 of the MFMA tile is the token
   if (col != 0) return;
   const float scale = (gamma * amax) / 127.0f;
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
-    if (rt % kWaves != wave || rt >= tiles_here) continue;
+    if (rt % kW != wave || rt >= tiles_here) continue;
     v4i acc = partial[rt][0][lane];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) add4(acc, partial[rt][w][lane]);
+    for (int w = 1; w < kW; ++w) add4(acc, partial[rt][w][lane]);
     store_tile(acc, (int64_t)(tile0 + rt) * kTileRows + 4 * sub, 0, n, scale, acc_out, y_out);
   }
 }
@@ -526,38 +537,59 @@ hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* 
   return hipGetLastError();
 }
 
+namespace {
+
+typedef void (*M1Kernel)(const uint4*, const float*, const uint4*, float*, int8_t*, int, int, int32_t*, uint16_t*);
+struct M1Config {
+  int rt, waves;
+  M1Kernel kernel;
+};
+
+template <int kRT, int kW, bool kShare>
+M1Kernel m1_pick(int64_t groups) {
+  const int64_t own = (groups + kW - 1) / kW;
+  const int64_t slots = kShare ? (own + 1) / 2 : (groups + 1) / 2;
+  if (slots <= 2) return k_bitlinear_m1<kRT, 2, kW, kShare>;
+  if (slots <= 5) return k_bitlinear_m1<kRT, 5, kW, kShare>;
+  if (slots <= kM1MaxSlots) return k_bitlinear_m1<kRT, kM1MaxSlots, kW, kShare>;
+  return nullptr;
+}
+
+#ifndef M1_WAVES
+#define M1_WAVES 4
+#endif
+#ifndef M1_SHARE
+#define M1_SHARE true
+#endif
+
+M1Config m1_config(int64_t groups, int64_t row_tiles) {
+  // several row tiles per workgroup once there are more than ~2 per CU
+#ifdef M1_RT
+  const int rt = M1_RT;
+#else
+  const int rt = row_tiles >= 1024 ? 4 : row_tiles >= 512 ? 2 : 1;
+#endif
+  M1Config c{rt, M1_WAVES, nullptr};
+  if (rt == 4) c.kernel = m1_pick<4, M1_WAVES, M1_SHARE>(groups);
+  else if (rt == 2) c.kernel = m1_pick<2, M1_WAVES, M1_SHARE>(groups);
+  else c.kernel = m1_pick<1, M1_WAVES, M1_SHARE>(groups);
+  return c;
+}
+
+}  // namespace
+
 hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t n,
                              int64_t k, int8_t* xq, float* alpha, int32_t* acc, uint16_t* y, hipStream_t s) {
   if (m > 16 || !gemv_fits_lds(m, k)) return hipErrorInvalidValue;
   if (m == 1 && k / 8 <= 64 * kM1MaxSlots) {
     const int64_t groups = (k / kTileCols + 3) / 4;
-    const size_t lds = (size_t)kWaves * (size_t)((groups + kWaves - 1) / kWaves) * 256;
     const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
-    // several row tiles per workgroup once there are more than ~2 per CU
-    const int rt = row_tiles >= 1024 ? 4 : row_tiles >= 512 ? 2 : 1;
-    const dim3 grid((unsigned)((row_tiles + rt - 1) / rt));
-    const uint4* p = reinterpret_cast<const uint4*>(packed);
-    const uint4* xv = reinterpret_cast<const uint4*>(x);
-    const int ni = (int)n, ki = (int)k;
-    // slots per lane: ceil(groups / 2), 5 for rows up to 2560 columns
-    if (groups <= 10) {
-      if (rt == 4)
-        hipLaunchKernelGGL((k_bitlinear_m1<4, 5>), grid, dim3(kThreads), lds, s, p, gamma, xv, alpha, xq, ni, ki, acc, y);
-      else if (rt == 2)
-        hipLaunchKernelGGL((k_bitlinear_m1<2, 5>), grid, dim3(kThreads), lds, s, p, gamma, xv, alpha, xq, ni, ki, acc, y);
-      else
-        hipLaunchKernelGGL((k_bitlinear_m1<1, 5>), grid, dim3(kThreads), lds, s, p, gamma, xv, alpha, xq, ni, ki, acc, y);
-    } else {
-      if (rt == 4)
-        hipLaunchKernelGGL((k_bitlinear_m1<4, kM1MaxSlots>), grid, dim3(kThreads), lds, s, p, gamma, xv, alpha, xq, ni, ki,
-                           acc, y);
-      else if (rt == 2)
-        hipLaunchKernelGGL((k_bitlinear_m1<2, kM1MaxSlots>), grid, dim3(kThreads), lds, s, p, gamma, xv, alpha, xq, ni, ki,
-                           acc, y);
-      else
-        hipLaunchKernelGGL((k_bitlinear_m1<1, kM1MaxSlots>), grid, dim3(kThreads), lds, s, p, gamma, xv, alpha, xq, ni, ki,
-                           acc, y);
-    }
+    const M1Config c = m1_config(groups, row_tiles);
+    const size_t lds = (size_t)c.waves * (size_t)((groups + c.waves - 1) / c.waves) * 256;
+    const dim3 grid((unsigned)((row_tiles + c.rt - 1) / c.rt));
+    if (!c.kernel) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(c.kernel, grid, dim3(64 * c.waves), lds, s, reinterpret_cast<const uint4*>(packed), gamma,
+                       reinterpret_cast<const uint4*>(x), alpha, xq, (int)n, (int)k, acc, y);
     return hipGetLastError();
   }
   const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
