@@ -74,23 +74,6 @@ __device__ __forceinline__ void store_tile(const v4i& acc, int64_t row0, int64_t
   }
 }
 
-__device__ __forceinline__ uint32_t max_abs_bf16x8(const uint4& v) {
-  uint32_t m = max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu);
-  m = max(m, max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu));
-  m = max(m, max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu));
-  return max(m, max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu));
-}
-
-// round-half-even(fl32(x * s)) clamped to int8, for the two bf16 in a dword
-__device__ __forceinline__ uint32_t quant2(uint32_t two_bf16, float s, int& sum) {
-  float lo = __uint_as_float(two_bf16 << 16);
-  float hi = __uint_as_float(two_bf16 & 0xFFFF0000u);
-  int ql = (int)fminf(fmaxf(__builtin_rintf(__fmul_rn(lo, s)), -128.0f), 127.0f);
-  int qh = (int)fminf(fmaxf(__builtin_rintf(__fmul_rn(hi, s)), -128.0f), 127.0f);
-  sum += ql + qh;
-  return ((uint32_t)ql & 0xFFu) | (((uint32_t)qh & 0xFFu) << 8);
-}
-
 // Partial reduction of `v` over the `g = min(tpr, 64)` lanes of a token row
 // group inside one wave; lanes with (tid % g) == 0 then write the group's value
 // to scratch[tid / g].  A row's value is the max/sum of its tpr/g entries.
@@ -186,14 +169,14 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_fused(const uint4* __rest
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- quantize the token block into LDS
-  uint32_t mx = 0;
+  u16x2 m2 = {0, 0};
   if (cached) {
 #pragma unroll
-    for (int c = 0; c < kXC; ++c) mx = max(mx, max_abs_bf16x8(xr[c]));
+    for (int c = 0; c < kXC; ++c) m2 = absmax_step(m2, xr[c]);
   } else if (row_ok) {
-    for (int64_t i = j0; i < k8; i += tpr) mx = max(mx, max_abs_bf16x8(xb[i]));
+    for (int64_t i = j0; i < k8; i += tpr) m2 = absmax_step(m2, xb[i]);
   }
-  group_partial<true>((int)mx, tpr, red_max);
+  group_partial<true>((int)max(m2.x, m2.y), tpr, red_max);
   __syncthreads();
   const float amax = __uint_as_float((uint32_t)row_total<true>(my_row, tpr, red_max) << 16);
   const float s = 127.0f / fmaxf(amax, 1e-5f);  // IEEE division, as in bl_quant_act
@@ -206,17 +189,14 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_fused(const uint4* __rest
       for (int c = 0; c < kXC; ++c) {
         const int64_t i = j0 + (int64_t)c * tpr;
         if (i < k8) {
-          const uint2 q = make_uint2(quant2(xr[c].x, s, sum) | (quant2(xr[c].y, s, sum) << 16),
-                                     quant2(xr[c].z, s, sum) | (quant2(xr[c].w, s, sum) << 16));
+          const uint2 q = act_codes8(xr[c], s, sum);
           dst[i] = q;
           if (gdst) gdst[i] = q;
         }
       }
     } else {
       for (int64_t i = j0; i < k8; i += tpr) {
-        const uint4 v = xb[i];
-        const uint2 q = make_uint2(quant2(v.x, s, sum) | (quant2(v.y, s, sum) << 16),
-                                   quant2(v.z, s, sum) | (quant2(v.w, s, sum) << 16));
+        const uint2 q = act_codes8(xb[i], s, sum);
         dst[i] = q;
         if (gdst) gdst[i] = q;
       }
@@ -289,9 +269,9 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_fused(const uint4* __rest
   }
 }
 
-constexpr int kM1MaxSlots = 14;  // 16-byte bf16 chunks per lane: single-token rows up to k = 7168
+constexpr int kM1MaxSlots = 14;  // 16-byte bf16 chunks per lane (own groups only: rows up to k = 28672)
 
-// Single-token BitLinear (m = 1, k <= 7168).  Wave w of kW multiplies the
+// Single-token BitLinear (m = 1).  Wave w of kW multiplies the
 // 256-column groups w, w + kW, ... and quantizes exactly those into its own
 // LDS region, which only it reads.  The row's absmax is either reduced by
 // every wave over the whole row in registers (no barrier before the
@@ -541,8 +521,8 @@ namespace {
 
 typedef void (*M1Kernel)(const uint4*, const float*, const uint4*, float*, int8_t*, int, int, int32_t*, uint16_t*);
 struct M1Config {
-  int rt, waves;
-  M1Kernel kernel;
+  int rt = 0, waves = 0;
+  M1Kernel kernel = nullptr;  // none when the row needs more than kM1MaxSlots slots per lane
 };
 
 template <int kRT, int kW, bool kShare>
@@ -563,15 +543,20 @@ M1Kernel m1_pick(int64_t groups) {
 #endif
 
 M1Config m1_config(int64_t groups, int64_t row_tiles) {
-  // several row tiles per workgroup once there are more than ~2 per CU
+  // two row tiles per workgroup for short rows once there are more than ~2
+  // tiles per CU (the quantized row is reused); long rows keep one tile per
+  // workgroup, whose weight stream is already long enough to hide latency
 #ifdef M1_RT
   const int rt = M1_RT;
 #else
-  const int rt = row_tiles >= 1024 ? 4 : row_tiles >= 512 ? 2 : 1;
+  const int rt = row_tiles >= 512 && groups <= 16 ? 2 : 1;
 #endif
   M1Config c{rt, M1_WAVES, nullptr};
+#ifdef M1_RT
   if (rt == 4) c.kernel = m1_pick<4, M1_WAVES, M1_SHARE>(groups);
-  else if (rt == 2) c.kernel = m1_pick<2, M1_WAVES, M1_SHARE>(groups);
+  else
+#endif
+  if (rt == 2) c.kernel = m1_pick<2, M1_WAVES, M1_SHARE>(groups);
   else c.kernel = m1_pick<1, M1_WAVES, M1_SHARE>(groups);
   return c;
 }
@@ -581,13 +566,12 @@ M1Config m1_config(int64_t groups, int64_t row_tiles) {
 hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t n,
                              int64_t k, int8_t* xq, float* alpha, int32_t* acc, uint16_t* y, hipStream_t s) {
   if (m > 16 || !gemv_fits_lds(m, k)) return hipErrorInvalidValue;
-  if (m == 1 && k / 8 <= 64 * kM1MaxSlots) {
+  const M1Config c = m == 1 ? m1_config((k / kTileCols + 3) / 4, (n + kTileRows - 1) / kTileRows) : M1Config{};
+  if (c.kernel) {
     const int64_t groups = (k / kTileCols + 3) / 4;
     const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
-    const M1Config c = m1_config(groups, row_tiles);
     const size_t lds = (size_t)c.waves * (size_t)((groups + c.waves - 1) / c.waves) * 256;
     const dim3 grid((unsigned)((row_tiles + c.rt - 1) / c.rt));
-    if (!c.kernel) return hipErrorInvalidValue;
     hipLaunchKernelGGL(c.kernel, grid, dim3(64 * c.waves), lds, s, reinterpret_cast<const uint4*>(packed), gamma,
                        reinterpret_cast<const uint4*>(x), alpha, xq, (int)n, (int)k, acc, y);
     return hipGetLastError();

@@ -297,10 +297,10 @@ def test_linear_is_deterministic():
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 33, 64), (1, 2560, 2560), (1, 2560, 6912), (1, 100, 28672),
-                                   # single-token kernel with 2 and 4 row tiles per workgroup, ragged last workgroup
+                                   # single-token kernel with 1 and 2 row tiles per workgroup, ragged last workgroup
                                    (1, 8200, 320), (1, 16400, 2560), (1, 16400, 6912), (1, 17000, 7168),
                                    # single-token kernel: partial last column group, both slot counts
-                                   (1, 40, 192), (1, 1000, 2624), (1, 9000, 4160),
+                                   (1, 40, 192), (1, 1000, 2624), (1, 9000, 4160), (1, 8200, 28672),
                                    # block-quantizing kernel with 2 and 4 row tiles per workgroup
                                    (1, 16400, 8192), (3, 8200, 2560), (16, 16400, 1024), (2, 17, 320),
                                    # eight-wave kernel for long rows (k >= 16384)
