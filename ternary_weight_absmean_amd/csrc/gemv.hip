@@ -41,7 +41,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kGroupsPerBatch = 4;
-constexpr int kLdsStageBytes = 33024;  // 16-token rows of up to 2 KiB, or one row of 32 KiB
+constexpr int kLdsBudget = 163840;  // LDS per workgroup (and per CU) on gfx950
 constexpr int kLdsRowPad = 16;          // row stride k + 16 bytes spreads the 16 token rows over the banks
 
 __device__ __forceinline__ v4i mask4(const uint4& a, uint32_t mask, int shift) {
@@ -438,82 +438,178 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_m1(const uint4* __restric
   }
 }
 
+// Product with int8 activations given (bl_linear, and bl_bitlinear after the
+// quantizer when the fused kernels do not apply), m <= 16 tokens.  Waves
+// split K by 1 KiB groups as above; each lane loads its activation bytes
+// (16 per field) straight from global memory as MFMA B operands and reuses
+// them for the kRT row tiles of the workgroup, so activation traffic per
+// weight byte falls as 4 * tokens / (16 * kRT).  Codes become signed trits
+// with v_perm.  kB groups per wave form a batch; the next batch's loads are
+// issued before the current batch's products.
+template <int kRT, int kB>
 __global__ __launch_bounds__(kThreads) void k_gemv_direct(const uint4* __restrict__ packed,
                                                           const float* __restrict__ gamma_ptr,
                                                           const int8_t* __restrict__ xq,
                                                           const float* __restrict__ alpha, int64_t m, int64_t n,
                                                           int64_t k, int32_t* __restrict__ acc_out,
                                                           uint16_t* __restrict__ y_out) {
-  __shared__ v4i partial[kWaves][64];
+  __shared__ v4i partial[kRT][kWaves][64];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t row_tile = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t tile0 = (int64_t)blockIdx.x * kRT;
+  const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
+  const int tiles_here = (int)min((int64_t)kRT, row_tiles - tile0);
   const int64_t tok0 = (int64_t)blockIdx.y * 16;
-  const int64_t kt_count = k / kTileCols;
-  const int64_t groups = (kt_count + 3) / 4;
+  const int kt_count = (int)(k / kTileCols);
+  const int groups = (kt_count + 3) / 4;
   const int sub = lane >> 4;
   const int col = lane & 15;
   const int64_t tok = tok0 + col;
   const bool has_tok = tok < m;
-  const uint4* wbase = packed + row_tile * kt_count * (kTileBytes / 16);
   const int rows = (int)min((int64_t)16, m - tok0);
+  // resources over each row tile and over this token block; offsets past
+  // either read as zero (tail groups, absent tokens, tiles past n), and a
+  // zero activation byte makes the product zero whatever the trit
+  const uint32_t tile_bytes = (uint32_t)(kt_count * kTileBytes);
+  __amdgpu_buffer_rsrc_t wrsrc[kRT];
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt)
+    wrsrc[rt] = buffer_rsrc(packed + (tile0 + rt) * kt_count * (kTileBytes / 16), rt < tiles_here ? tile_bytes : 0u);
+  const __amdgpu_buffer_rsrc_t xrsrc = buffer_rsrc(xq + tok0 * k, (uint32_t)(rows * k));
   // scales read now (a load at the epilogue would add a memory round trip)
   const float gamma = buffer_load_f32(buffer_rsrc(gamma_ptr, 4), 0);
   const float alpha_tok = buffer_load_f32(buffer_rsrc(alpha + tok0, (uint32_t)(rows * 4)), has_tok ? col * 4 : kOutOfRange);
-  // resources over this row tile and this token block; offsets past either
-  // read as zero (tail groups, absent tokens), and a zero activation byte
-  // makes the product zero whatever the trit
-  const __amdgpu_buffer_rsrc_t wrsrc = buffer_rsrc(wbase, (uint32_t)(kt_count * kTileBytes));
-  const __amdgpu_buffer_rsrc_t xrsrc = buffer_rsrc(xq + tok0 * k, (uint32_t)(rows * k));
 
-  v4i acc[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
-  for (int64_t g0 = wave; g0 < groups; g0 += (int64_t)kWaves * kGroupsPerBatch) {
-    uint4 a[kGroupsPerBatch];
-    uint4 b[kGroupsPerBatch][4];
+  auto load_batch = [&](int g0, uint4 (&a)[kRT][kB], uint4 (&b)[kB][4]) {
 #pragma unroll
-    for (int u = 0; u < kGroupsPerBatch; ++u) {
-      const int64_t g = g0 + (int64_t)u * kWaves;
-      const int64_t kt = 4 * g + sub;
+    for (int u = 0; u < kB; ++u) {
+      const int g = g0 + u * kWaves;
+      const int kt = 4 * g + sub;
       const bool valid = kt < kt_count && has_tok;
-      a[u] = buffer_load16(wrsrc, (uint32_t)(g * 1024 + lane * 16));
 #pragma unroll
       for (int f = 0; f < 4; ++f)
         b[u][f] = buffer_load16(xrsrc, valid ? (uint32_t)(col * k + kt * kTileCols + 16 * f) : kOutOfRange);
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt)
+        a[rt][u] = buffer_load16(wrsrc[rt], g < groups ? (uint32_t)(g * 1024 + lane * 16) : kOutOfRange);
+    }
+  };
+  v4i acc[kRT][2];
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) acc[rt][0] = acc[rt][1] = v4i{0, 0, 0, 0};
+  uint4 a_cur[kRT][kB], b_cur[kB][4];
+  load_batch(wave, a_cur, b_cur);
+  for (int g0 = wave; g0 < groups; g0 += kWaves * kB) {
+    uint4 a_nxt[kRT][kB], b_nxt[kB][4];
+    load_batch(g0 + kWaves * kB, a_nxt, b_nxt);  // past the end: out of range, no memory access
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+          acc[rt][f & 1] = mfma_16x16x64(unpack_field(a_cur[rt][u], f), as_v4i(b_cur[u][f]), acc[rt][f & 1]);
+      }
     }
 #pragma unroll
-    for (int u = 0; u < kGroupsPerBatch; ++u) {
+    for (int u = 0; u < kB; ++u) {
 #pragma unroll
-      for (int f = 0; f < 4; ++f) acc[f] = mfma_16x16x64(unpack_field(a[u], f), as_v4i(b[u][f]), acc[f]);
+      for (int f = 0; f < 4; ++f) b_cur[u][f] = b_nxt[u][f];
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) a_cur[rt][u] = a_nxt[rt][u];
     }
   }
-  add4(acc[0], acc[1]);
-  add4(acc[2], acc[3]);
-  add4(acc[0], acc[2]);
-  partial[wave][lane] = acc[0];
-  __syncthreads();
-  if (wave != 0 || !has_tok) return;
-  v4i sum = partial[0][lane];
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) add4(sum, partial[w][lane]);
+  for (int rt = 0; rt < kRT; ++rt) {
+    add4(acc[rt][0], acc[rt][1]);
+    partial[rt][wave][lane] = acc[rt][0];
+  }
+  __syncthreads();
+  // wave w finishes row tiles w, w + 4, ...
+  if (!has_tok) return;
   const float scale = (gamma * alpha_tok) / 127.0f;
-  store_tile(sum, row_tile * kTileRows + 4 * sub, tok, n, scale, acc_out, y_out);
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    if (rt % kWaves != wave || rt >= tiles_here) continue;
+    v4i sum = partial[rt][0][lane];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) add4(sum, partial[rt][w][lane]);
+    store_tile(sum, (tile0 + rt) * kTileRows + 4 * sub, tok, n, scale, acc_out, y_out);
+  }
 }
 
-dim3 gemv_grid(int64_t m, int64_t n) {
-  return dim3((unsigned)((n + kTileRows - 1) / kTileRows), (unsigned)((m + 15) / 16));
-}
 
 }  // namespace
 
 size_t gemv_lds_bytes(int64_t m, int64_t k) { return (size_t)(m < 16 ? m : 16) * (size_t)(k + kLdsRowPad); }
 
-bool gemv_fits_lds(int64_t m, int64_t k) { return gemv_lds_bytes(m, k) <= (size_t)kLdsStageBytes; }
+namespace {
+
+// LDS of k_bitlinear_fused<kRT, kW> besides the token block
+constexpr size_t fused_static_lds(int rt, int w) { return (size_t)rt * w * 1024 + 2 * (size_t)(w * 4) * 4; }
+
+struct FusedPlan {
+  int rt = 0, waves = 0;
+};
+
+FusedPlan fused_plan(int64_t m, int64_t n, int64_t k) {
+  const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
+  // Several tokens: eight waves per workgroup (the block quantization is
+  // shared by more weight streams) except for short rows with many row
+  // tiles; two row tiles per workgroup once there are ~2 per CU.  A single
+  // token (rows too long for the single-token kernel): eight waves for long
+  // rows, two row tiles once there are ~4 per CU.
+#ifdef FUSED_W
+  int w = FUSED_W;
+#else
+  int w = m == 1 ? (k >= 16384 ? 8 : 4) : (row_tiles >= 512 && k <= 4096 ? 4 : 8);
+#endif
+#ifdef FUSED_RT
+  int rt = FUSED_RT;
+#else
+  int rt = m == 1 ? (row_tiles >= 1024 ? 2 : 1) : (row_tiles >= 512 ? 2 : 1);
+#endif
+  if (w == 8 && rt > 2) rt = 2;
+  const size_t dyn = gemv_lds_bytes(m, k);
+  while (rt > 1 && dyn + fused_static_lds(rt, w) > (size_t)kLdsBudget) rt /= 2;
+  if (dyn + fused_static_lds(rt, w) > (size_t)kLdsBudget) return FusedPlan{};
+  return FusedPlan{rt, w};
+}
+
+}  // namespace
+
+#ifndef FUSED_MAX_TOKEN_COLUMNS
+#define FUSED_MAX_TOKEN_COLUMNS 32767
+#endif
+
+// Every workgroup of k_bitlinear_fused quantizes its whole token block, so
+// it pays off while m * k is small (up to 8 tokens of 2560, 4 of 6912);
+// larger blocks go through the quantizer and k_gemv_direct.  One token takes
+// the single-token kernel whenever it applies.
+bool gemv_fused_applies(int64_t m, int64_t k) {
+  if (m < 1 || m > 16) return false;
+  if (m > 1 && m * k > FUSED_MAX_TOKEN_COLUMNS) return false;
+  return fused_plan(m, 1, k).rt > 0;
+}
 
 hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
                        int64_t n, int64_t k, int32_t* acc, uint16_t* y, hipStream_t s) {
   if ((m + 15) / 16 > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_gemv_direct, gemv_grid(m, n), dim3(kThreads), 0, s, reinterpret_cast<const uint4*>(packed),
-                     gamma, xq, alpha, m, n, k, acc, y);
+  const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
+#ifdef DIRECT_RT
+  const int rt = DIRECT_RT;
+#else
+  // share the activation loads among row tiles once there are tiles to spare
+  const int rt = row_tiles >= 2048 ? 4 : row_tiles >= 512 ? 2 : 1;
+#endif
+  const dim3 grid((unsigned)((row_tiles + rt - 1) / rt), (unsigned)((m + 15) / 16));
+  const uint4* p = reinterpret_cast<const uint4*>(packed);
+  if (rt == 4)
+    hipLaunchKernelGGL((k_gemv_direct<4, 2>), grid, dim3(kThreads), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
+  else if (rt == 2)
+    hipLaunchKernelGGL((k_gemv_direct<2, 2>), grid, dim3(kThreads), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
+  else
+    hipLaunchKernelGGL((k_gemv_direct<1, 4>), grid, dim3(kThreads), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
   return hipGetLastError();
 }
 
@@ -565,7 +661,7 @@ M1Config m1_config(int64_t groups, int64_t row_tiles) {
 
 hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t n,
                              int64_t k, int8_t* xq, float* alpha, int32_t* acc, uint16_t* y, hipStream_t s) {
-  if (m > 16 || !gemv_fits_lds(m, k)) return hipErrorInvalidValue;
+  if (m > 16 || !gemv_fused_applies(m, k)) return hipErrorInvalidValue;
   const M1Config c = m == 1 ? m1_config((k / kTileCols + 3) / 4, (n + kTileRows - 1) / kTileRows) : M1Config{};
   if (c.kernel) {
     const int64_t groups = (k / kTileCols + 3) / 4;
@@ -576,22 +672,25 @@ hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const ui
                        reinterpret_cast<const uint4*>(x), alpha, xq, (int)n, (int)k, acc, y);
     return hipGetLastError();
   }
+  const FusedPlan f = fused_plan(m, n, k);
   const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
-  const int rt = m == 1 ? (row_tiles >= 1024 ? 2 : 1) : (row_tiles >= 1024 ? 4 : row_tiles >= 512 ? 2 : 1);
-  const dim3 grid((unsigned)((row_tiles + rt - 1) / rt), (unsigned)((m + 15) / 16));
+  const dim3 grid((unsigned)((row_tiles + f.rt - 1) / f.rt), (unsigned)((m + 15) / 16));
   const uint4* p = reinterpret_cast<const uint4*>(packed);
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   const size_t lds = gemv_lds_bytes(m, k);
-  // long rows (>= 64 column groups): 8 waves per workgroup, one row tile each
-  if (k >= 16384) {
-    const dim3 g1((unsigned)row_tiles, (unsigned)((m + 15) / 16));
-    hipLaunchKernelGGL((k_bitlinear_fused<1, 8>), g1, dim3(512), lds, s, p, gamma, xv, alpha, xq, m, n, k, acc, y);
-  } else if (rt == 4) {
+  if (f.waves == 8) {
+    if (f.rt == 2)
+      hipLaunchKernelGGL((k_bitlinear_fused<2, 8>), grid, dim3(512), lds, s, p, gamma, xv, alpha, xq, m, n, k, acc, y);
+    else
+      hipLaunchKernelGGL((k_bitlinear_fused<1, 8>), grid, dim3(512), lds, s, p, gamma, xv, alpha, xq, m, n, k, acc, y);
+  } else if (f.rt == 4) {
     hipLaunchKernelGGL((k_bitlinear_fused<4, 4>), grid, dim3(256), lds, s, p, gamma, xv, alpha, xq, m, n, k, acc, y);
-  } else if (rt == 2) {
+  } else if (f.rt == 2) {
     hipLaunchKernelGGL((k_bitlinear_fused<2, 4>), grid, dim3(256), lds, s, p, gamma, xv, alpha, xq, m, n, k, acc, y);
-  } else {
+  } else if (f.rt == 1) {
     hipLaunchKernelGGL((k_bitlinear_fused<1, 4>), grid, dim3(256), lds, s, p, gamma, xv, alpha, xq, m, n, k, acc, y);
+  } else {
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -192,6 +192,19 @@ def test_linear_brute_force_shapes(m, n, k):
     check_linear(u8(buf), f32(np.array([gamma])), qw, gamma, xq_np=xq, alpha_np=alpha)
 
 
+@pytest.mark.parametrize("m,n,k", [(16, 16400, 1024), (5, 32800, 320), (9, 16416, 2112)])
+def test_linear_multi_tile_workgroups(m, n, k):
+    """Token blocks whose activation loads serve 2 or 4 row tiles per
+    workgroup, with a ragged last workgroup."""
+    rng = np.random.default_rng(7 * m + n + k)
+    buf, qw = random_layer(rng, n, k)
+    xq = rng.integers(-128, 128, size=(m, k)).astype(np.int8)
+    alpha = datagen.bf16_to_f32(datagen.f32_to_bf16(rng.uniform(0.1, 50, size=m)))
+    gamma = np.float32(0.0271)
+    say(f"bl_linear multi-tile m={m} n={n} k={k}")
+    check_linear(u8(buf), f32(np.array([gamma])), qw, gamma, xq_np=xq, alpha_np=alpha)
+
+
 def test_linear_extremes():
     k, n, m = 6912, 48, 4
     qw = np.ones((n, k), np.int8)
@@ -303,6 +316,10 @@ def test_linear_is_deterministic():
                                    (1, 40, 192), (1, 1000, 2624), (1, 9000, 4160), (1, 8200, 28672),
                                    # block-quantizing kernel with 2 and 4 row tiles per workgroup
                                    (1, 16400, 8192), (3, 8200, 2560), (16, 16400, 1024), (2, 17, 320),
+                                   # several tokens: quantizer + product with shared activation loads
+                                   (8, 16400, 2560), (16, 32800, 320), (5, 2000, 6912),
+                                   # block-quantizing kernel with eight waves, one and two row tiles
+                                   (4, 600, 6912), (3, 9000, 8000),
                                    # eight-wave kernel for long rows (k >= 16384)
                                    (1, 530, 16384), (7, 70, 16448), (16, 40, 32768),
                                    (3, 48, 2560), (4, 3840, 2560), (5, 40, 6912), (16, 64, 1024), (16, 31, 2560),
