@@ -48,9 +48,18 @@ def parse_args():
                    help="skip the prefill, batched-decode and 70B-shaped measurements")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only copy a 1 GiB device buffer 3 times (counter calibration run)")
-    p.add_argument("--summarize", nargs=4, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR", "CALIB_DIR"),
-                   help="turn rocprofv3 outputs into profiles/ summaries (no GPU needed)")
-    p.add_argument("--calib-write-dir", default=None, help="WRITE_SIZE run of the calibration copy")
+    p.add_argument("--profile", choices=sorted(PROFILE_CASES), default=None,
+                   help="only run one workload a few times (a short program for rocprofv3)")
+    p.add_argument("--reps", type=int, default=3, help="repetitions for --profile")
+    p.add_argument("--summarize", metavar="NAME", default=None,
+                   help="write profiles/NAME.md from rocprofv3 outputs (no GPU needed)")
+    p.add_argument("--title", default="")
+    p.add_argument("--workload", default="", help="workload the summary covers (key in profiles/traffic.json)")
+    p.add_argument("--stats", default=None, help="rocprofv3 --kernel-trace --stats output directory")
+    p.add_argument("--pmc", action="append", default=[], help="rocprofv3 --pmc output directory (repeatable)")
+    p.add_argument("--calib", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
+                   help="FETCH_SIZE and WRITE_SIZE runs of --calibrate-copy")
+    p.add_argument("--command", action="append", default=[], help="command that produced an input (repeatable)")
     return p.parse_args()
 
 
@@ -58,6 +67,11 @@ def main() -> int:
     args = parse_args()
     if args.summarize:
         return summarize(args)
+    if args.profile:
+        if args.gpus != 1:
+            print("--profile runs on one GPU", file=sys.stderr)
+            return 2
+        return PROFILE_CASES[args.profile](args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
               "(the BitLinear path runs on a single MI355X).", file=sys.stderr)
@@ -213,16 +227,18 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic (seeded N(0,0.02) weights absmean-ternarized; N(0,1) bf16 tokens, 8 outlier channels x20)",
-        "config": {"workload": "bitnet-b1.58-2B-shaped decode stack, M=1",
+        "config": {"workload": STACK_WORKLOAD,
                    "layers": args.layers, "linears_per_layer": 4,
                    "shapes_KxN": [f"{k}x{n}" for _, k, n in proj],
                    "launch": "HIP graph, one bl_bitlinear (fused quantize + product) per linear"},
         "decode_weight_GBps": round(weight_bytes_step / (ms_per_step * 1e-3) / 1e9, 1),
         "eager": {"ms_per_step": round(eager_ms, 4), "tokens_per_s": round(m * 1000.0 / eager_ms, 2)},
         "wall_s_timed": round(wall, 4),
-        "roofline": {"bound": "hbm", "kernel": "k_gemv_lds<fused> (bl_bitlinear)", "achieved": round(gemv_gbps, 1),
+        "roofline": {"bound": "hbm", "kernel": f"{STACK_KERNEL} (bl_bitlinear, all {len(linears)} launches)",
+                     "achieved": round(gemv_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gemv_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": stored_traffic("k_bitlinear_fused", avg_bytes), "avg_launch_us": round(avg_us, 3),
+                     "traffic": stored_traffic(STACK_WORKLOAD, STACK_KERNEL, avg_bytes),
+                     "avg_launch_us": round(avg_us, 3),
                      "algorithmic_bytes_per_launch": round(avg_bytes, 1)},
         "packer": {"weights": len(linears), "fp32_GB": round(w_bytes / 1e9, 3), "ms": round(pack_ms, 3),
                    "GBps_fp32_read": round(w_bytes / (pack_ms * 1e-3) / 1e9, 1)},
@@ -235,6 +251,13 @@ def main() -> int:
 
 MFMA_I8_PEAK_TOPS = 5000.0
 CALIB_BYTES = 1 << 30
+STACK_WORKLOAD = "bitnet-b1.58-2B-shaped decode stack, M=1"
+STACK_KERNEL = "k_bitlinear_m1"
+# kernel base name -> source file whose hash marks the stored counter figures as current
+KERNEL_SOURCES = {"k_bitlinear_m1": "gemv.hip", "k_bitlinear_fused": "gemv.hip", "k_gemv_direct": "gemv.hip",
+                  "k_gemm": "gemm.hip", "k_quant_act": "quant.hip"}
+CU_SIMDS = 256 * 4
+CLOCK_GHZ = 2.4
 
 
 def _read_csv(path):
@@ -251,71 +274,128 @@ def _find(d, suffix):
     return hits[0]
 
 
-def _per_dispatch(rows, name_part, counter):
-    vals = [float(r["Counter_Value"]) for r in rows if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter]
-    return sum(vals) / len(vals) if vals else None, len(vals)
+def _base_name(name: str) -> str:
+    """'bl::(anonymous namespace)::k_gemm<8>(...)' -> 'k_gemm'."""
+    short = name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0].replace("bl::", "")
+    return short.split("<")[0].strip()
+
+
+def _per_kernel(rows, counter):
+    """Average per dispatch of `counter`, and mean dispatch duration (ns), per kernel base name."""
+    import collections
+    vals, durs = collections.defaultdict(list), collections.defaultdict(list)
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        base = _base_name(r["Kernel_Name"])
+        vals[base].append(float(r["Counter_Value"]))
+        durs[base].append(float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
+    return {b: (sum(v) / len(v), sum(durs[b]) / len(durs[b]), len(v)) for b, v in vals.items()}
 
 
 def summarize(args):
-    """profiles/ from rocprofv3 outputs: kernel-trace stats of the benchmark,
-    FETCH_SIZE and WRITE_SIZE of its kernels, and the same counters for a
-    1 GiB device copy (calibration: bytes the counters report per byte moved)."""
-    stats_dir, fetch_dir, write_dir, calib_dir = args.summarize
-    calib_write_dir = args.calib_write_dir or calib_dir
-    stats = _read_csv(_find(stats_dir, "kernel_stats.csv"))
-    fetch = _read_csv(_find(fetch_dir, "counter_collection.csv"))
-    write = _read_csv(_find(write_dir, "counter_collection.csv"))
-    cal_f = _read_csv(_find(calib_dir, "counter_collection.csv"))
-    cal_w = _read_csv(_find(calib_write_dir, "counter_collection.csv"))
-    copy_fetch, _ = _per_dispatch(cal_f, "copy", "FETCH_SIZE")
-    copy_write, _ = _per_dispatch(cal_w, "copy", "WRITE_SIZE")
-    f_fetch = CALIB_BYTES / (copy_fetch * 1024.0)
-    f_write = CALIB_BYTES / (copy_write * 1024.0)
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    """profiles/NAME.md from rocprofv3 outputs: kernel durations (kernel-trace
+    stats), per-dispatch counters of each --pmc run, and, with --calib, HBM
+    bytes per launch from FETCH_SIZE + WRITE_SIZE scaled by what the same
+    counters read for a 1 GiB device copy.  MFMA utilisation, when the
+    counters are present: SQ_VALU_MFMA_BUSY_CYCLES over the dispatch's
+    duration x 1024 SIMDs x 2.4 GHz."""
+    import collections
+    name = args.summarize
+    lines = [f"# {args.title or name}", ""]
+    if args.workload:
+        lines += [f"Workload: {args.workload}", ""]
+    lines += ["Commands (run from the repository root on one MI355X; `cd /tmp && export TMPDIR=/tmp` first):", "", "```"]
+    lines += args.command + ["```", ""]
+    stats_rows = _read_csv(_find(args.stats, "kernel_stats.csv")) if args.stats else []
+    grouped = collections.OrderedDict()
+    for r in stats_rows:
+        base = _base_name(r["Name"])
+        g = grouped.setdefault(base, {"calls": 0, "total": 0.0, "min": float("inf"), "max": 0.0})
+        g["calls"] += int(r["Calls"])
+        g["total"] += float(r["TotalDurationNs"])
+        g["min"] = min(g["min"], float(r["MinNs"]))
+        g["max"] = max(g["max"], float(r["MaxNs"]))
+    if grouped:
+        lines += ["## Kernel durations (--kernel-trace --stats; template instances summed)", "",
+                  "| kernel | calls | avg (us) | min (us) | max (us) | share of GPU time |", "|---|---|---|---|---|---|"]
+        total = sum(g["total"] for g in grouped.values())
+        for base, g in grouped.items():
+            lines.append(f"| {base} | {g['calls']} | {g['total'] / g['calls'] / 1e3:.3f} | {g['min'] / 1e3:.3f} | "
+                         f"{g['max'] / 1e3:.3f} | {100 * g['total'] / total:.1f}% |")
+        lines.append("")
+    counters = collections.OrderedDict()  # counter -> {kernel: (avg value, avg duration ns, dispatches)}
+    for d in args.pmc:
+        rows = _read_csv(_find(d, "counter_collection.csv"))
+        for c in sorted({r["Counter_Name"] for r in rows}):
+            counters[c] = _per_kernel(rows, c)
+    kernels = sorted({k for per in counters.values() for k in per})
+    if counters:
+        lines += ["## Counters per dispatch (averages over the profiled dispatches)", "",
+                  "| kernel | " + " | ".join(counters) + " | avg dispatch (us) |",
+                  "|---|" + "---|" * (len(counters) + 1)]
+        for k in kernels:
+            vals = [counters[c].get(k) for c in counters]
+            dur = next((v[1] for v in vals if v), 0.0)
+            lines.append(f"| {k} | " + " | ".join("" if v is None else f"{v[0]:.1f}" for v in vals) +
+                         f" | {dur / 1e3:.3f} |")
+        lines.append("")
     traffic = {}
-    lines = ["# Decode stack (2B-shaped, M=1): kernel durations and HBM traffic", "",
-             "Commands (run from the repository root on one MI355X):", "",
-             "```",
-             "rocprofv3 --kernel-trace --stats --output-format csv -d <STATS_DIR> -o stack -- "
-             "python bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-extras",
-             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -o f -- "
-             "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-extras",
-             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE_DIR> -o w -- "
-             "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-extras",
-             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <CALIB_DIR> -o c -- python bench.py --calibrate-copy",
-             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <CALIB_WRITE_DIR> -o c -- python bench.py --calibrate-copy",
-             "python bench.py --summarize <STATS_DIR> <FETCH_DIR> <WRITE_DIR> <CALIB_DIR> --calib-write-dir <CALIB_WRITE_DIR>",
-             "```", "",
-             f"Calibration: a 1 GiB device copy reads {copy_fetch:.0f} KiB (FETCH_SIZE) and writes "
-             f"{copy_write:.0f} KiB (WRITE_SIZE) per dispatch; scale factors {f_fetch:.4f} and {f_write:.4f}.", "",
-             "| kernel | calls | avg duration (us) | min (us) | max (us) | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | HBM bytes/launch (calibrated) |",
-             "|---|---|---|---|---|---|---|---|"]
-    for r in stats:
-        name = r["Name"]
-        short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("bl::", "").replace("void ", "")
-        fk, _ = _per_dispatch(fetch, short, "FETCH_SIZE")
-        wk, _ = _per_dispatch(write, short, "WRITE_SIZE")
-        hbm = None
-        if fk is not None and wk is not None:
-            hbm = fk * 1024.0 * f_fetch + wk * 1024.0 * f_write
-        lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | {float(r['MinNs']) / 1e3:.3f} | "
-                     f"{float(r['MaxNs']) / 1e3:.3f} | {'' if fk is None else f'{fk:.1f}'} | "
-                     f"{'' if wk is None else f'{wk:.1f}'} | {'' if hbm is None else f'{hbm:.0f}'} |")
-        base = short.split("<")[0]
-        if base in KERNEL_SOURCES and hbm is not None:
-            traffic[base] = {"bytes_per_launch": round(hbm), "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
-                             "calibration": {"fetch": round(f_fetch, 5), "write": round(f_write, 5)},
-                             "source_sha256_16": source_hash(base),
-                             "workload": "bitnet-b1.58-2B-shaped decode stack, M=1 (bench.py default)",
-                             "avg_duration_us": round(float(r["AverageNs"]) / 1e3, 3)}
-    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
-        json.dump(traffic, f, indent=1, sort_keys=True)
-        f.write("\n")
-    with open(os.path.join(ROOT, "profiles", "decode_stack_2b_m1.md"), "w") as f:
+    if args.calib and "FETCH_SIZE" in counters and "WRITE_SIZE" in counters:
+        cf = _per_kernel(_read_csv(_find(args.calib[0], "counter_collection.csv")), "FETCH_SIZE")
+        cw = _per_kernel(_read_csv(_find(args.calib[1], "counter_collection.csv")), "WRITE_SIZE")
+        copy_f = next(v[0] for k, v in cf.items() if "copy" in k.lower())
+        copy_w = next(v[0] for k, v in cw.items() if "copy" in k.lower())
+        f_fetch, f_write = CALIB_BYTES / (copy_f * 1024.0), CALIB_BYTES / (copy_w * 1024.0)
+        lines += ["## HBM traffic", "",
+                  f"Calibration: a 1 GiB device copy reads {copy_f:.0f} KiB (FETCH_SIZE) and writes {copy_w:.0f} KiB "
+                  f"(WRITE_SIZE) per dispatch, so the counters are scaled by {f_fetch:.4f} and {f_write:.4f}.", "",
+                  "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per launch (calibrated) |", "|---|---|---|---|"]
+        for k in kernels:
+            fk, wk = counters["FETCH_SIZE"].get(k), counters["WRITE_SIZE"].get(k)
+            if not fk or not wk:
+                continue
+            hbm = fk[0] * 1024.0 * f_fetch + wk[0] * 1024.0 * f_write
+            lines.append(f"| {k} | {fk[0]:.1f} | {wk[0]:.1f} | {hbm:.0f} |")
+            if k in KERNEL_SOURCES:
+                traffic[k] = {"bytes_per_launch": round(hbm), "fetch_kib": round(fk[0], 1), "write_kib": round(wk[0], 1),
+                              "calibration": {"fetch": round(f_fetch, 5), "write": round(f_write, 5)},
+                              "source_sha256_16": source_hash(k), "dispatches": fk[2]}
+        lines.append("")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in counters:
+        lines += ["## MFMA utilisation", "",
+                  "busy = SQ_VALU_MFMA_BUSY_CYCLES (all SIMDs) / (dispatch duration x 2.4 GHz x 1024 SIMDs); "
+                  "ops = SQ_INSTS_MFMA x 32768 (v_mfma_i32_16x16x64_i8: 16 x 16 x 64 multiply-adds).", "",
+                  "| kernel | MFMA busy | MFMA instructions | int8 ops per dispatch | TOPS over the dispatch |",
+                  "|---|---|---|---|---|"]
+        busy = counters["SQ_VALU_MFMA_BUSY_CYCLES"]
+        insts = counters.get("SQ_INSTS_MFMA", {})
+        for k, (b, dur, _) in busy.items():
+            if b <= 0:
+                continue
+            util = b / (dur * CLOCK_GHZ * CU_SIMDS)
+            n_inst = insts.get(k, (0.0, dur, 0))[0]
+            ops = n_inst * 32768
+            lines.append(f"| {k} | {100 * util:.1f}% | {n_inst:.0f} | {ops:.4g} | "
+                         f"{ops / (insts.get(k, (0, dur, 0))[1] * 1e-9) / 1e12 if n_inst else 0:.1f} |")
+        lines.append("")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    if traffic and args.workload:
+        path = os.path.join(ROOT, "profiles", "traffic.json")
+        try:
+            with open(path) as f:
+                stored = json.load(f)
+        except (OSError, ValueError):
+            stored = {}
+        stored = {k: v for k, v in stored.items() if isinstance(v, dict) and all(isinstance(x, dict) for x in v.values())}
+        stored[args.workload] = traffic
+        with open(path, "w") as f:
+            json.dump(stored, f, indent=1, sort_keys=True)
+            f.write("\n")
+    with open(os.path.join(ROOT, "profiles", f"{name}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
     return 0
-KERNEL_SOURCES = {"k_bitlinear_fused": "gemv.hip", "k_gemv_direct": "gemv.hip", "k_gemm": "gemm.hip"}
 
 
 def source_hash(kernel: str) -> str:
@@ -325,21 +405,88 @@ def source_hash(kernel: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def stored_traffic(kernel: str, algorithmic_bytes: float):
+def stored_traffic(workload: str, kernel: str, algorithmic_bytes: float):
     """HBM bytes per launch from the committed rocprofv3 counter summary
     (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or None
     when there is none or the kernel's source changed since it was taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
-            rec = json.load(f).get(kernel)
-    except (OSError, ValueError):
+            rec = json.load(f).get(workload, {}).get(kernel)
+    except (OSError, ValueError, AttributeError):
         return None
     if not rec or rec.get("source_sha256_16") != source_hash(kernel):
         return None
     return {"bytes_per_launch": rec["bytes_per_launch"],
             "ratio_to_algorithmic": round(rec["bytes_per_launch"] / algorithmic_bytes, 3),
-            "workload": rec.get("workload")}
+            "workload": workload}
+
+
+# ---------------------------------------------------------------- short programs for rocprofv3
+
+
+def _profile_prefill_2b(args):
+    """Layer-0 gate+up and down of the 2B-shaped stack at M = 2048: bl_bitlinear
+    (quantizer + GEMM) --reps times each."""
+    import numpy as np
+    import torch
+    import datagen
+    import ternary_weight_absmean_amd as bl
+
+    dev = torch.device("cuda", 0)
+    wl = datagen.WORKLOAD_STACK_2B
+    m = 2048
+    for pi, (name, k, n) in enumerate(datagen.STACK_2B_PROJ):
+        if name not in ("gate_up", "down"):
+            continue
+        w = torch.from_numpy(datagen.weights(datagen.stream_id(wl, 0, pi, datagen.TENSOR_W), n, k)).to(dev)
+        packed, gamma = bl.bl_ternarize_pack(w)
+        del w
+        cols = datagen.outlier_columns(wl, k, datagen.STACK_2B_OUTLIERS)
+        x = datagen.activations_bf16(datagen.stream_id(wl, 0, pi, datagen.TENSOR_X) + m, m, k, cols,
+                                     datagen.STACK_2B_OUTLIER_MULT)
+        xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        for _ in range(args.reps):
+            bl.bl_bitlinear(packed, gamma, xd, n, acc=False)
+        torch.cuda.synchronize()
+        print(f"[profile] prefill_2b {name} M={m} K={k} N={n} x{args.reps}", flush=True)
+    return 0
+
+
+def _profile_70b(args, ms):
+    import numpy as np
+    import torch
+    import datagen
+    import ternary_weight_absmean_amd as bl
+
+    dev = torch.device("cuda", 0)
+    wl = datagen.WORKLOAD_70B
+    layer = []
+    for pi, (name, k, n) in enumerate(datagen.LAYER_70B_PROJ):
+        w = torch.from_numpy(datagen.weights(datagen.stream_id(wl, 0, pi, datagen.TENSOR_W), n, k)).to(dev)
+        packed, gamma = bl.bl_ternarize_pack(w)
+        del w
+        # two copies (2 x 176 MB > the 256 MB Infinity Cache): consecutive launches stream from HBM
+        layer.append((name, k, n, [packed, packed.clone()], gamma))
+    torch.cuda.synchronize()
+    for m in ms:
+        for pi, (name, k, n, copies, gamma) in enumerate(layer):
+            cols = datagen.outlier_columns(wl, k, datagen.n_outliers_70b(k))
+            x = datagen.activations_bf16(datagen.stream_id(wl, 0, pi, datagen.TENSOR_X) + m, m, k, cols,
+                                         datagen.LAYER_70B_OUTLIER_MULT)
+            xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+            for r in range(args.reps):
+                bl.bl_bitlinear(copies[r % 2], gamma, xd, n, acc=False)
+            torch.cuda.synchronize()
+            print(f"[profile] 70b {name} M={m} K={k} N={n} x{args.reps}", flush=True)
+    return 0
+
+
+PROFILE_CASES = {
+    "prefill_2b": _profile_prefill_2b,
+    "decode_70b": lambda args: _profile_70b(args, (1, 16)),
+    "prefill_70b": lambda args: _profile_70b(args, (1024,)),
+}
 
 
 def _graph_time_ms(torch, fn, reps, warm=2):
