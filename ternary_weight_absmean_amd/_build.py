@@ -21,6 +21,10 @@ FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-ffp-contract=off",
     # keep the compiler from emitting packed-fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # kernel arguments preloaded into SGPRs by the dispatcher: the first
+    # instructions need no scalar load round trip (a decode launch is a
+    # latency chain of a few microseconds)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-result",
 ]
 
