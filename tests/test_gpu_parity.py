@@ -39,7 +39,7 @@ def check_quant(x_bits):
     np.testing.assert_array_equal(host(alpha).view(np.uint32), want_a.view(np.uint32))
 
 
-@pytest.mark.parametrize("m,k", [(1, 64), (2, 128), (3, 192), (17, 320), (100, 2560), (5, 6912)])
+@pytest.mark.parametrize("m,k", [(1, 64), (2, 128), (3, 192), (17, 320), (100, 2560), (5, 6912), (3, 16384), (2, 12352)])
 def test_quant_small_and_ragged(m, k):
     rng = np.random.default_rng(m * 7 + k)
     x = datagen.f32_to_bf16(rng.standard_normal((m, k)) * 10.0 ** rng.uniform(-4, 4, size=(m, 1)))
