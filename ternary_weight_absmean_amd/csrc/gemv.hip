@@ -1,4 +1,4 @@
-// Decode product for BitLinear W1.58A8 (m <= 16 tokens): packed ternary W x int8 x.
+// Decode products for BitLinear W1.58A8 (m <= 16 tokens): packed ternary W x int8 x.
 //
 // deepmox.com chapter 8, "A low-bit model is a whole-stack design": decode
 // time goes to moving the weights; the GPU path keeps them packed at four
@@ -7,31 +7,34 @@
 // the ternary product is integer add/subtract; here the unpacked values feed
 // the int8 matrix cores, which perform exactly those integer sums.
 //
-// The kernels are bound by HBM: every packed byte is read once (0.25 byte per
-// weight) and nothing else is large.  Work decomposition, shared by both:
-//   * one workgroup (4 waves) per 16-row tile of W and per block of up to 16
+// The kernels are bound by HBM (or, for the small matrices of a 2B-shaped
+// model, by launch latency): every packed byte is read once (0.25 byte per
+// weight) and nothing else is large.  Shared decomposition:
+//   * a workgroup owns one or more 16-row tiles of W and a block of up to 16
 //     tokens;
-//   * the waves split K: wave w takes 1 KiB groups w, w+4, ... (a group is four
-//     consecutive 16x64 tiles, contiguous in the packed layout), so each
-//     wave-wide 128-bit load reads 1 KiB of HBM with no gaps;
+//   * its waves split K by 1 KiB groups (four consecutive 16x64 tiles,
+//     contiguous in the packed layout), so each wave-wide 128-bit load reads
+//     1 KiB of HBM with no gaps;
 //   * lane l holds row l%16 of tile (4*group + l/16): 16 bytes = 64 trits.
-//     Field f (bits 2f..2f+1 of each byte) is columns 16f..16f+15 of the tile,
-//     multiplied in v_mfma_i32_16x16x64_i8 with the same 16 activation bytes;
-//     B column l%16 is token l%16 of the block;
-//   * the waves' 16x16 int32 partial sums are added in LDS (integer, order-free)
-//     and wave 0 applies the epilogue y = bf16(acc * gamma * alpha / 127).
+//     Field f (bits 2f..2f+1 of each byte) is columns 16f..16f+15 of the
+//     tile, multiplied in v_mfma_i32_16x16x64_i8 with the same 16 activation
+//     bytes; B column l%16 is token l%16 of the block;
+//   * the waves' 16x16 int32 partial sums are added in LDS (integer,
+//     order-free) and the epilogue writes y = bf16(acc * gamma * alpha / 127).
 //
-// k_bitlinear_fused (the whole layer, m_blk * (k + 16) <= 33 KiB) quantizes the
-// bf16 tokens itself (per-token absmax, identical arithmetic to bl_quant_act)
-// into LDS and feeds the MFMA with the raw codes c = q + 1, correcting with the
-// token's activation sum: sum q*x = sum c*x - sum x.  The codes need no table:
-// masking a byte with 0x03, 0x0C, 0x30 gives 1, 4 and 16 times fields 0, 1, 2,
-// and (b >> 2) & 0x30 gives 16 times field 3, so four independent accumulators
-// hold c*x scaled by 1, 4, 16, 16 and are divided exactly at the end (20 VALU
-// ops per 1 KiB group instead of 44 for a signed table lookup).
-//
-// k_gemv_direct (bl_linear: int8 activations given) reads activation bytes
-// straight from global memory and converts codes to signed trits with v_perm.
+// Kernels:
+//   k_bitlinear_m1     one token, quantization fused; each wave quantizes only
+//                      the columns it multiplies (the bench step's kernel)
+//   k_bitlinear_fused  a few tokens (m * k small), block quantization fused
+//   k_gemv_lds         2..16 tokens, int8 activations given, staged in LDS
+//   k_gemv_direct      one token, int8 activations given
+// The fused kernels feed the MFMA with the raw codes c = q + 1 and correct
+// with the token's activation sum: sum q*x = sum c*x - sum x.  Masking a
+// byte with 0x03, 0x0C, 0x30 gives 1, 4 and 16 times fields 0, 1, 2, and
+// (b >> 2) & 0x30 gives 16 times field 3, so four accumulators hold c*x
+// scaled by 1, 4, 16, 16 and are divided exactly at the end (20 VALU ops per
+// 1 KiB group instead of 44 for a signed table lookup).  The others convert
+// codes to signed trits with v_perm.
 #include "device_util.h"
 #include "internal.h"
 
@@ -450,22 +453,22 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_m1(const uint4* __restric
   }
 }
 
-// Product with int8 activations given (bl_linear, and bl_bitlinear after the
-// quantizer when the fused kernels do not apply), m <= 16 tokens.  Waves
+// Product with int8 activations given for one token (bl_linear with m = 1,
+// and bl_bitlinear's fallback for rows longer than the fused kernels take).  Waves
 // split K by 1 KiB groups as above; each lane loads its activation bytes
 // (16 per field) straight from global memory as MFMA B operands and reuses
 // them for the kRT row tiles of the workgroup, so activation traffic per
 // weight byte falls as 4 * tokens / (16 * kRT).  Codes become signed trits
 // with v_perm.  kB groups per wave form a batch; the next batch's loads are
 // issued before the current batch's products.
-template <int kRT, int kB>
-__global__ __launch_bounds__(kThreads) void k_gemv_direct(const uint4* __restrict__ packed,
+template <int kRT, int kB, int kW>
+__global__ __launch_bounds__(kW * 64) void k_gemv_direct(const uint4* __restrict__ packed,
                                                           const float* __restrict__ gamma_ptr,
                                                           const int8_t* __restrict__ xq,
                                                           const float* __restrict__ alpha, int64_t m, int64_t n,
                                                           int64_t k, int32_t* __restrict__ acc_out,
                                                           uint16_t* __restrict__ y_out) {
-  __shared__ v4i partial[kRT][kWaves][64];
+  __shared__ v4i partial[kRT][kW][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t tile0 = (int64_t)blockIdx.x * kRT;
@@ -495,7 +498,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_direct(const uint4* __restric
   auto load_batch = [&](int g0, uint4 (&a)[kRT][kB], uint4 (&b)[kB][4]) {
 #pragma unroll
     for (int u = 0; u < kB; ++u) {
-      const int g = g0 + u * kWaves;
+      const int g = g0 + u * kW;
       const int kt = 4 * g + sub;
       const bool valid = kt < kt_count && has_tok;
 #pragma unroll
@@ -511,9 +514,9 @@ __global__ __launch_bounds__(kThreads) void k_gemv_direct(const uint4* __restric
   for (int rt = 0; rt < kRT; ++rt) acc[rt][0] = acc[rt][1] = v4i{0, 0, 0, 0};
   uint4 a_cur[kRT][kB], b_cur[kB][4];
   load_batch(wave, a_cur, b_cur);
-  for (int g0 = wave; g0 < groups; g0 += kWaves * kB) {
+  for (int g0 = wave; g0 < groups; g0 += kW * kB) {
     uint4 a_nxt[kRT][kB], b_nxt[kB][4];
-    load_batch(g0 + kWaves * kB, a_nxt, b_nxt);  // past the end: out of range, no memory access
+    load_batch(g0 + kW * kB, a_nxt, b_nxt);  // past the end: out of range, no memory access
 #pragma unroll
     for (int u = 0; u < kB; ++u) {
 #pragma unroll
@@ -537,19 +540,156 @@ __global__ __launch_bounds__(kThreads) void k_gemv_direct(const uint4* __restric
     partial[rt][wave][lane] = acc[rt][0];
   }
   __syncthreads();
-  // wave w finishes row tiles w, w + 4, ...
+  // wave w finishes row tiles w, w + kW, ...
   if (!has_tok) return;
   const float scale = (gamma * alpha_tok) / 127.0f;
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
-    if (rt % kWaves != wave || rt >= tiles_here) continue;
+    if (rt % kW != wave || rt >= tiles_here) continue;
     v4i sum = partial[rt][0][lane];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) add4(sum, partial[rt][w][lane]);
+    for (int w = 1; w < kW; ++w) add4(sum, partial[rt][w][lane]);
     store_tile(sum, (tile0 + rt) * kTileRows + 4 * sub, tok, n, scale, acc_out, y_out);
   }
 }
 
+
+// Product with int8 activations given, 2 <= m <= 16 tokens, activations
+// staged through LDS.  Loaded straight from global memory as MFMA B operands
+// (k_gemv_direct), a wave's activation load touches 32 cache lines (16
+// token rows x 2 lines) for 1 KiB, so the L1 line rate bounds the kernel
+// near 2.5 TB/s of weights at 16 tokens.  Here the workgroup copies the
+// token block in column chunks of kC = kW * kGW * 256 bytes per token, with
+// loads that read each token row contiguously, into LDS (row stride kC + 16
+// bytes: the 16 rows of a B operand read fall in distinct banks); the waves
+// then read their B operands from LDS.  Per chunk, wave w multiplies groups
+// w, w + kW, ... of the chunk (kGW of them) for the kRT row tiles of the
+// workgroup.  The next chunk's activations and weights are loaded into
+// registers while the current chunk is multiplied; two barriers per chunk
+// guard the single LDS buffer.  Codes become signed trits with v_perm.
+template <int kRT, int kW, int kGW>
+__global__ __launch_bounds__(kW * 64) void k_gemv_lds(const uint4* __restrict__ packed,
+                                                       const float* __restrict__ gamma_ptr,
+                                                       const int8_t* __restrict__ xq,
+                                                       const float* __restrict__ alpha, int64_t m, int64_t n,
+                                                       int64_t k, int32_t* __restrict__ acc_out,
+                                                       uint16_t* __restrict__ y_out) {
+  constexpr int kT = kW * 64;
+  constexpr int kC = kW * kGW * 256;          // columns per chunk
+  constexpr int kLd = kC + 16;                // LDS row stride
+  constexpr int kPieces = 16 * kC / 16;       // 16-byte pieces per chunk (16 token rows)
+  constexpr int kXLoads = kPieces / kT;       // per thread
+  static_assert(kPieces % kT == 0, "chunk must split evenly over the threads");
+  __shared__ uint4 xs_raw[16 * kLd / 16];
+  __shared__ v4i partial[kRT][kW][64];
+  int8_t* xs = reinterpret_cast<int8_t*>(xs_raw);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t tile0 = (int64_t)blockIdx.x * kRT;
+  const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
+  const int tiles_here = (int)min((int64_t)kRT, row_tiles - tile0);
+  const int64_t tok0 = (int64_t)blockIdx.y * 16;
+  const int rows = (int)min((int64_t)16, m - tok0);
+  const int kt_count = (int)(k / kTileCols);
+  const int groups = (kt_count + 3) / 4;
+  const int chunks = (int)((k + kC - 1) / kC);
+  const int sub = lane >> 4;
+  const int col = lane & 15;
+  const bool has_tok = col < rows;
+
+  const uint32_t tile_bytes = (uint32_t)(kt_count * kTileBytes);
+  __amdgpu_buffer_rsrc_t wrsrc[kRT];
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt)
+    wrsrc[rt] = buffer_rsrc(packed + (tile0 + rt) * kt_count * (kTileBytes / 16), rt < tiles_here ? tile_bytes : 0u);
+  const __amdgpu_buffer_rsrc_t xrsrc = buffer_rsrc(xq + tok0 * k, (uint32_t)(rows * k));
+  const float gamma = buffer_load_f32(buffer_rsrc(gamma_ptr, 4), 0);
+  const float alpha_tok = buffer_load_f32(buffer_rsrc(alpha + tok0, (uint32_t)(rows * 4)), has_tok ? col * 4 : kOutOfRange);
+
+  // piece p of a chunk: token row p / (kC / 16), 16 bytes at column 16 * (p % (kC / 16))
+  auto load_x = [&](int c, uint4 (&v)[kXLoads]) {
+#pragma unroll
+    for (int i = 0; i < kXLoads; ++i) {
+      const int p = tid + i * kT;
+      const int r = p / (kC / 16);
+      const int64_t colx = (int64_t)c * kC + 16 * (p % (kC / 16));
+      v[i] = buffer_load16(xrsrc, colx < k ? (uint32_t)(r * k + colx) : kOutOfRange);
+    }
+  };
+  // this wave's u-th group of chunk c (global group index)
+  auto group_of = [&](int c, int u) { return c * (kW * kGW) + wave + u * kW; };
+  auto load_w = [&](int c, uint4 (&a)[kRT][kGW]) {
+#pragma unroll
+    for (int u = 0; u < kGW; ++u) {
+      const int g = group_of(c, u);
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt)
+        a[rt][u] = buffer_load16(wrsrc[rt], g < groups ? (uint32_t)(g * 1024 + lane * 16) : kOutOfRange);
+    }
+  };
+
+  v4i acc[kRT][2];
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) acc[rt][0] = acc[rt][1] = v4i{0, 0, 0, 0};
+  uint4 xv[kXLoads];
+  uint4 a_cur[kRT][kGW];
+  load_x(0, xv);
+  load_w(0, a_cur);
+  for (int c = 0; c < chunks; ++c) {
+    __syncthreads();  // the previous chunk's B operands have been read
+#pragma unroll
+    for (int i = 0; i < kXLoads; ++i) {
+      const int p = tid + i * kT;
+      *reinterpret_cast<uint4*>(xs + (p / (kC / 16)) * kLd + 16 * (p % (kC / 16))) = xv[i];
+    }
+    __syncthreads();
+    uint4 a_nxt[kRT][kGW];
+    if (c + 1 < chunks) {
+      load_x(c + 1, xv);
+      load_w(c + 1, a_nxt);
+    }
+#pragma unroll
+    for (int u = 0; u < kGW; ++u) {
+      // local tile 4 * (wave + u * kW) + sub of this chunk, field f
+      const int8_t* xt = xs + col * kLd + (4 * (wave + u * kW) + sub) * kTileCols;
+      uint4 b[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) b[f] = *reinterpret_cast<const uint4*>(xt + 16 * f);
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+          acc[rt][f & 1] = mfma_16x16x64(unpack_field(a_cur[rt][u], f), as_v4i(b[f]), acc[rt][f & 1]);
+      }
+    }
+    if (c + 1 < chunks) {
+#pragma unroll
+      for (int u = 0; u < kGW; ++u) {
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) a_cur[rt][u] = a_nxt[rt][u];
+      }
+    }
+  }
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    add4(acc[rt][0], acc[rt][1]);
+    partial[rt][wave][lane] = acc[rt][0];
+  }
+  __syncthreads();
+  // wave w finishes row tiles w, w + kW, ...
+  if (!has_tok) return;
+  const float scale = (gamma * alpha_tok) / 127.0f;
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    if (rt % kW != wave || rt >= tiles_here) continue;
+    v4i sum = partial[rt][0][lane];
+#pragma unroll
+    for (int w = 1; w < kW; ++w) add4(sum, partial[rt][w][lane]);
+    store_tile(sum, (tile0 + rt) * kTileRows + 4 * sub, tok0 + col, n, scale, acc_out, y_out);
+  }
+}
 
 }  // namespace
 
@@ -608,20 +748,26 @@ hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* 
                        int64_t n, int64_t k, int32_t* acc, uint16_t* y, hipStream_t s) {
   if ((m + 15) / 16 > 65535) return hipErrorInvalidValue;
   const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
-#ifdef DIRECT_RT
-  const int rt = DIRECT_RT;
-#else
-  // share the activation loads among row tiles once there are tiles to spare
-  const int rt = row_tiles >= 2048 ? 4 : row_tiles >= 512 ? 2 : 1;
-#endif
-  const dim3 grid((unsigned)((row_tiles + rt - 1) / rt), (unsigned)((m + 15) / 16));
   const uint4* p = reinterpret_cast<const uint4*>(packed);
+  if (m >= 2) {
+    // two row tiles per workgroup once there are ~2 per CU
+    const int rt = row_tiles >= 512 ? 2 : 1;
+    const dim3 grid((unsigned)((row_tiles + rt - 1) / rt), (unsigned)((m + 15) / 16));
+    if (rt == 2)
+      hipLaunchKernelGGL((k_gemv_lds<2, 4, 4>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
+    else
+      hipLaunchKernelGGL((k_gemv_lds<1, 4, 4>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
+    return hipGetLastError();
+  }
+  // one token: its activation bytes are few, so each lane loads its own
+  const int rt = row_tiles >= 2048 ? 4 : row_tiles >= 512 ? 2 : 1;
+  const dim3 grid((unsigned)((row_tiles + rt - 1) / rt), (unsigned)((m + 15) / 16));
   if (rt == 4)
-    hipLaunchKernelGGL((k_gemv_direct<4, 2>), grid, dim3(kThreads), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
+    hipLaunchKernelGGL((k_gemv_direct<4, 2, 4>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
   else if (rt == 2)
-    hipLaunchKernelGGL((k_gemv_direct<2, 2>), grid, dim3(kThreads), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
+    hipLaunchKernelGGL((k_gemv_direct<2, 2, 4>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
   else
-    hipLaunchKernelGGL((k_gemv_direct<1, 4>), grid, dim3(kThreads), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
+    hipLaunchKernelGGL((k_gemv_direct<1, 4, 4>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
   return hipGetLastError();
 }
 
