@@ -8,11 +8,12 @@
 //
 // With many tokens the product is a dense contraction (2*m*n*k int8 ops over
 // n*k/4 + m*k bytes), bound by the matrix cores, not by HBM.  Tiling:
-//   * a workgroup (4 waves side by side along n) owns 256 weight rows x 64 or
-//     128 tokens; each wave owns 64 rows x all the workgroup's tokens, i.e.
-//     4 x 4 or 4 x 8 MFMA tiles of 16 x 16 (64 or 128 int32 accumulators per
-//     lane).  No two waves share weight rows, so each packed byte is unpacked
-//     once per workgroup;
+//   * a workgroup (4 waves side by side along n) owns 256 weight rows x 128
+//     or 64 tokens, or 128 rows x 64 tokens (the largest tile that leaves
+//     enough workgroups); each wave owns 64 or 32 rows x all the workgroup's
+//     tokens, i.e. 4 x 8, 4 x 4 or 2 x 4 MFMA tiles of 16 x 16.  No two
+//     waves share weight rows, so each packed byte is unpacked once per
+//     workgroup;
 //   * K advances 256 columns per step.  The weights never pass through LDS:
 //     each wave loads its 64 rows' packed bytes straight into registers (one
 //     1 KiB load per 16 rows per step: 16 rows x 4 tiles of 64 columns) and
@@ -40,19 +41,18 @@ namespace bl {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kWN = 64;                 // weight rows per wave
-constexpr int kBN = kWaves * kWN;       // weight rows per workgroup
 constexpr int kStepK = 256;             // columns per step
 constexpr int kXRow = kStepK / 16;     // 16-byte chunks per token row in LDS
-constexpr int kRB = kWN / 16;           // 16-row MFMA blocks per wave
 constexpr int kXcds = 8;                // accelerator complex dies, each with its own L2
 
-template <int kTB>  // 16-token MFMA blocks per wave (4 or 8)
+template <int kTB, int kRB>  // 16-token (4 or 8) and 16-row (2 or 4) MFMA blocks per wave
 __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* __restrict__ packed, const float* __restrict__ gamma_ptr,
                                                  const int8_t* __restrict__ xq, const float* __restrict__ alpha,
                                                  int64_t m, int64_t n, int64_t k, int64_t blocks_n,
                                                  int32_t* __restrict__ acc_out, uint16_t* __restrict__ y_out) {
   constexpr int kBM = 16 * kTB;                       // tokens per workgroup
+  constexpr int kWN = 16 * kRB;                       // weight rows per wave
+  constexpr int kBN = kWaves * kWN;                   // weight rows per workgroup
   constexpr int kXDma = kBM * kStepK / 1024 / kWaves; // 1 KiB LDS-DMA loads per wave per step
   __shared__ uint4 xs[2][kBM * kXRow];
   __shared__ int row_sum[kBM];
@@ -232,18 +232,26 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* __restrict__ pac
 
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
                        int64_t n, int64_t k, int32_t* acc, uint16_t* y, hipStream_t s) {
-  const int64_t blocks_n = (n + kBN - 1) / kBN;
-  // 128-token tiles unless that leaves fewer than two workgroups per CU
-  const bool tall = blocks_n * ((m + 127) / 128) >= 512;
-  const int64_t bm = tall ? 128 : 64;
-  const int64_t blocks = blocks_n * ((m + bm - 1) / bm);
-  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (tall)
-    hipLaunchKernelGGL(k_gemm<8>, dim3((unsigned)blocks), dim3(256), 0, s, packed, gamma, xq, alpha, m, n, k, blocks_n,
+  // Largest tile that still gives the chip enough workgroups: 256 rows x 128
+  // tokens with >= 4 per CU, else 256 x 64 with >= 2 per CU, else 128 x 64.
+  auto count = [&](int64_t rows, int64_t toks) { return ((n + rows - 1) / rows) * ((m + toks - 1) / toks); };
+  const uint8_t* p = packed;
+  if (count(256, 128) >= 1024) {
+    const int64_t blocks_n = (n + 255) / 256, blocks = count(256, 128);
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_gemm<8, 4>), dim3((unsigned)blocks), dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, blocks_n,
                        acc, y);
-  else
-    hipLaunchKernelGGL(k_gemm<4>, dim3((unsigned)blocks), dim3(256), 0, s, packed, gamma, xq, alpha, m, n, k, blocks_n,
+  } else if (count(256, 64) >= 512) {
+    const int64_t blocks_n = (n + 255) / 256, blocks = count(256, 64);
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_gemm<4, 4>), dim3((unsigned)blocks), dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, blocks_n,
                        acc, y);
+  } else {
+    const int64_t blocks_n = (n + 127) / 128, blocks = count(128, 64);
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_gemm<4, 2>), dim3((unsigned)blocks), dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, blocks_n,
+                       acc, y);
+  }
   return hipGetLastError();
 }
 
