@@ -87,7 +87,8 @@ size_t bl_ternarize_pack_workspace_bytes(int64_t n, int64_t k);
  *   gamma     out, one fp32 on the device (gamma, without eps).
  *   workspace device scratch of workspace_bytes >= the size above; its
  *             contents on entry do not matter and are clobbered.
- * Errors: BL_ERR_NULL, BL_ERR_SHAPE (n < 1 or bad k), BL_ERR_ALIGN,
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE (n < 1, bad k, or n*k > 2^39, beyond
+ *         which the exact integer sum could overflow), BL_ERR_ALIGN,
  *         BL_ERR_WORKSPACE, BL_ERR_HIP. */
 bl_status bl_ternarize_pack(const float* w, int64_t n, int64_t k, uint8_t* packed, float* gamma,
                             void* workspace, size_t workspace_bytes, void* stream);

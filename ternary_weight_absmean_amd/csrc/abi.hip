@@ -32,7 +32,7 @@ size_t bl_ternarize_pack_workspace_bytes(int64_t n, int64_t k) {
 bl_status bl_ternarize_pack(const float* w, int64_t n, int64_t k, uint8_t* packed, float* gamma, void* workspace,
                             size_t workspace_bytes, void* stream) {
   if (!w || !packed || !gamma || !workspace) return BL_ERR_NULL;
-  if (n < 1 || n > BL_MAX_N || !valid_k(k) || !product_ok(n + 16, k)) return BL_ERR_SHAPE;
+  if (n < 1 || n > BL_MAX_N || !valid_k(k) || !product_ok(n + 16, k) || n * k > (1LL << 39)) return BL_ERR_SHAPE;
   if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(gamma, 4) || !aligned(workspace, 16)) return BL_ERR_ALIGN;
   if (workspace_bytes < bl_ternarize_pack_workspace_bytes(n, k)) return BL_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;

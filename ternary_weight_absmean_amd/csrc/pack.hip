@@ -31,37 +31,86 @@ namespace bl {
 namespace {
 
 constexpr int kBins = 256;
+
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
 constexpr int kBinThreads = 256;
-constexpr int kBinWaves = kBinThreads / 64;
+constexpr int kBinLoads = 4;   // float4 loads per thread per iteration (in flight together)
+constexpr int kWindow = 16;    // exponents accumulated in registers
 
 __global__ void k_zero_bins(unsigned long long* bins) { bins[threadIdx.x] = 0ull; }
 
-__device__ __forceinline__ void bin_abs(unsigned long long* lbins, float v) {
-  uint32_t b = __float_as_uint(v) & 0x7FFFFFFFu;
-  uint32_t e = b >> 23;
-  uint32_t sig = (b & 0x7FFFFFu) | (e ? 0x800000u : 0u);
-  atomicAdd(&lbins[e], (unsigned long long)sig);
-}
-
+// Exact sum of |w| by exponent.  |w| = sig * 2^(e-150) with e the biased
+// exponent and sig the significand (hidden bit included for e > 0); the
+// bins hold sum sig per exponent, so that sum |w| = sum_e bins[e] *
+// 2^(max(e, 1) - 150).  Most values of a weight matrix fall within a few
+// binades of its largest, so each lane adds sig << (e - e0) into one 64-bit
+// register for e in the wave's window [e0, e0 + 16), e0 taken from the
+// wave's first values; that register equals sum sig * 2^(e - e0), i.e. the
+// bin e0 contribution of the window, and is split into its low and high 32
+// bits for bins e0 and e0 + 32.  Values outside the window (and subnormals)
+// go to LDS bins by atomic add.  All additions are of integers, so the
+// result does not depend on the grid or the order.  Per lane at most 2^20
+// values (count <= 2^39 over 2^19 threads) of at most 2^39 each, and no bin
+// exceeds count * 2^24 + 2^51 < 2^64: no overflow.
 __global__ __launch_bounds__(kBinThreads) void k_absmean_bins(const float4* __restrict__ w4, int64_t n4,
                                                                unsigned long long* __restrict__ bins) {
-  __shared__ unsigned long long lbins[kBinWaves][kBins];
+  __shared__ unsigned long long lbins[kBins];
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  for (int i = tid; i < kBinWaves * kBins; i += kBinThreads) (&lbins[0][0])[i] = 0ull;
+  lbins[tid] = 0ull;
   __syncthreads();
-  const int64_t stride = (int64_t)gridDim.x * kBinThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kBinThreads + tid; i < n4; i += stride) {
-    float4 v = w4[i];
-    bin_abs(lbins[wave], v.x);
-    bin_abs(lbins[wave], v.y);
-    bin_abs(lbins[wave], v.z);
-    bin_abs(lbins[wave], v.w);
+  const int64_t stride = (int64_t)gridDim.x * kBinThreads * kBinLoads;
+  int e0 = -1;  // window base, chosen from the first batch
+  unsigned long long acc = 0ull;
+  auto add = [&](float v) {
+    const uint32_t b = __float_as_uint(v) & 0x7FFFFFFFu;
+    const int e = (int)(b >> 23);
+    const uint32_t sig = (b & 0x7FFFFFu) | (e ? 0x800000u : 0u);
+    const uint32_t d = (uint32_t)(e - e0);
+    if (d < (uint32_t)kWindow) {
+      acc += (unsigned long long)sig << d;
+    } else if (sig) {
+      atomicAdd(&lbins[e], (unsigned long long)sig);
+    }
+  };
+  for (int64_t base = (int64_t)blockIdx.x * kBinThreads * kBinLoads; base < n4; base += stride) {
+    float4 v[kBinLoads];
+#pragma unroll
+    for (int j = 0; j < kBinLoads; ++j) {
+      const int64_t i = base + j * kBinThreads + tid;
+      v[j] = w4[i < n4 ? i : n4 - 1];
+      if (i >= n4) v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (e0 < 0) {
+      uint32_t mx = 0;
+#pragma unroll
+      for (int j = 0; j < kBinLoads; ++j)
+        mx = max(mx, max(max(__float_as_uint(v[j].x) & 0x7FFFFFFFu, __float_as_uint(v[j].y) & 0x7FFFFFFFu),
+                         max(__float_as_uint(v[j].z) & 0x7FFFFFFFu, __float_as_uint(v[j].w) & 0x7FFFFFFFu)));
+      const int emax = wave_reduce<true>((int)(mx >> 23));
+      e0 = min(max(emax - (kWindow - 4), 1), kBins - 2 - 32);  // e0 >= 1, e0 + 32 <= 253
+    }
+#pragma unroll
+    for (int j = 0; j < kBinLoads; ++j) {
+      add(v[j].x);
+      add(v[j].y);
+      add(v[j].z);
+      add(v[j].w);
+    }
+  }
+  if (e0 >= 0) {  // wave-uniform: the wave saw at least one batch
+    const unsigned long long lo = wave_sum_u64(acc & 0xFFFFFFFFull);
+    const unsigned long long hi = wave_sum_u64(acc >> 32);
+    if ((tid & 63) == 0) {
+      if (lo) atomicAdd(&lbins[e0], lo);
+      if (hi) atomicAdd(&lbins[e0 + 32], hi);
+    }
   }
   __syncthreads();
-  unsigned long long s = 0;
-#pragma unroll
-  for (int wv = 0; wv < kBinWaves; ++wv) s += lbins[wv][tid];
+  const unsigned long long s = lbins[tid];
   if (s) atomicAdd(&bins[tid], s);
 }
 
@@ -74,20 +123,44 @@ __device__ __forceinline__ uint32_t limb_bit(const uint32_t* q, int pos) {
   return (q[pos >> 4] >> (pos & 15)) & 1u;
 }
 
-__global__ void k_gamma_fold(const unsigned long long* __restrict__ bins, unsigned long long count,
-                             float* __restrict__ gamma) {
+// floor(cur / d) and cur mod d for cur < 2^56, 0 < d < 2^40: a double
+// estimate (relative error below 2^-52, so within one of the quotient), then
+// integer correction.
+__device__ __forceinline__ uint32_t div_step(unsigned long long cur, unsigned long long d, unsigned long long& rem) {
+  long long q = (long long)((double)cur / (double)d);
+  long long r = (long long)cur - q * (long long)d;
+  while (r < 0) {
+    --q;
+    r += (long long)d;
+  }
+  while (r >= (long long)d) {
+    ++q;
+    r -= (long long)d;
+  }
+  rem = (unsigned long long)r;
+  return (uint32_t)q;
+}
+
+// One workgroup: the 256 bins are read in parallel into LDS; one thread then
+// forms X = sum bins[e] * 2^(max(e,1) - 1) = sum |w| * 2^149 in 16-bit limbs,
+// divides by the element count (long division by limbs), and rounds the
+// quotient once to fp32, nearest with ties to even.
+__global__ __launch_bounds__(kBins) void k_gamma_fold(const unsigned long long* __restrict__ bins,
+                                                       unsigned long long count, float* __restrict__ gamma) {
+  __shared__ unsigned long long lb[kBins];
+  lb[threadIdx.x] = bins[threadIdx.x];
+  __syncthreads();
   if (threadIdx.x != 0) return;
-  // X = sum_e bins[e] * 2^(max(e,1) - 1) = sum |w| * 2^149, as 16-bit limbs
   uint32_t x[kLimbs];
 #pragma unroll
   for (int i = 0; i < kLimbs; ++i) x[i] = 0;
   for (int e = 0; e < kBins - 1; ++e) {
-    unsigned long long v = bins[e];
+    const unsigned long long v = lb[e];
     if (v == 0) continue;
-    int sh = e ? e - 1 : 0;
-    int q = sh >> 4, r = sh & 15;
-    unsigned long long lo = v << r;
-    unsigned long long hi = r ? (v >> (64 - r)) : 0ull;
+    const int sh = e ? e - 1 : 0;
+    const int q = sh >> 4, r = sh & 15;
+    const unsigned long long lo = v << r;
+    const unsigned long long hi = r ? (v >> (64 - r)) : 0ull;
     x[q + 0] += (uint32_t)(lo & 0xFFFFu);
     x[q + 1] += (uint32_t)((lo >> 16) & 0xFFFFu);
     x[q + 2] += (uint32_t)((lo >> 32) & 0xFFFFu);
@@ -96,18 +169,14 @@ __global__ void k_gamma_fold(const unsigned long long* __restrict__ bins, unsign
   }
   uint32_t carry = 0;
   for (int i = 0; i < kLimbs; ++i) {
-    uint32_t t = x[i] + carry;
+    const uint32_t t = x[i] + carry;
     x[i] = t & 0xFFFFu;
     carry = t >> 16;
   }
   // Q = floor(X / count), R = X mod count (count < 2^40, so rem << 16 < 2^56)
   uint32_t qv[kLimbs];
   unsigned long long rem = 0;
-  for (int i = kLimbs - 1; i >= 0; --i) {
-    unsigned long long cur = (rem << 16) | x[i];
-    qv[i] = (uint32_t)(cur / count);
-    rem = cur % count;
-  }
+  for (int i = kLimbs - 1; i >= 0; --i) qv[i] = div_step((rem << 16) | x[i], count, rem);
   int nb = 0;  // bit length of Q
   for (int i = kLimbs - 1; i >= 0; --i) {
     if (qv[i]) {
@@ -116,22 +185,25 @@ __global__ void k_gamma_fold(const unsigned long long* __restrict__ bins, unsign
     }
   }
   // keep 24 significant bits; mean = mant * 2^(shift - 149)
-  int shift = nb > 24 ? nb - 24 : 0;
+  const int shift = nb > 24 ? nb - 24 : 0;
   uint32_t mant = 0;
   for (int b = 23; b >= 0; --b) mant = (mant << 1) | (shift + b < kLimbs * 16 ? limb_bit(qv, shift + b) : 0u);
   bool up;
   if (shift == 0) {
-    unsigned long long twice = rem << 1;  // rem < 2^40
+    const unsigned long long twice = rem << 1;  // rem < 2^40
     up = twice > count || (twice == count && (mant & 1u));
   } else {
-    bool round_bit = limb_bit(qv, shift - 1);
+    const bool round_bit = limb_bit(qv, shift - 1);
+    // sticky: the remainder, or any quotient bit below the round bit
     bool sticky = rem != 0;
-    for (int b = 0; b < shift - 1 && !sticky; ++b) sticky = limb_bit(qv, b);
+    const int below = shift - 1;  // bits 0 .. below-1
+    for (int i = 0; i < (below >> 4) && !sticky; ++i) sticky = qv[i] != 0;
+    if (!sticky && (below & 15)) sticky = (qv[below >> 4] & ((1u << (below & 15)) - 1u)) != 0;
     up = round_bit && (sticky || (mant & 1u));
   }
   // fp32 encoding of mant * 2^(shift-149): (shift << 23) + mant, also across
   // the carry when rounding reaches 2^24 and for subnormals (shift = 0).
-  uint32_t bits = ((uint32_t)shift << 23) + mant + (up ? 1u : 0u);
+  const uint32_t bits = ((uint32_t)shift << 23) + mant + (up ? 1u : 0u);
   *gamma = __uint_as_float(bits);
 }
 
@@ -139,42 +211,43 @@ __global__ void k_gamma_fold(const unsigned long long* __restrict__ bins, unsign
 
 constexpr int kPackThreads = 256;
 
-// Thread per (row, 64-column tile): reads the 64 fp32 weights of that row
-// segment (256 contiguous bytes) and writes its 16 packed bytes.  Column
-// 16*f + b of the segment goes to byte b, bits 2f..2f+1, as code q + 1.
-__global__ __launch_bounds__(kPackThreads) void k_ternarize_pack(const float* __restrict__ w, int64_t n, int64_t k,
+// Lane per 4 consecutive weights (one float4): 16 lanes cover one row of a
+// 64-column tile and a wave covers 4 consecutive tiles of one row, so each
+// wave-wide load reads 1 KiB contiguously.  Column c of the tile goes to byte
+// c % 16, bits 2*(c/16): lane j (columns 4j..4j+3) fills field j / 4 of bytes
+// 4*(j%4) .. 4*(j%4)+3, i.e. dword j % 4 of the row's 16 packed bytes.  The
+// four lanes j = d, d+4, d+8, d+12 of dword d are OR-combined with DPP row
+// rotations, and lanes 0..3 of each 16 store the dwords.  Rows past n get
+// code 1 (trit 0).  Code = q + 1, q = clamp(round_half_even(w / (gamma +
+// 1e-5)), -1, 1) with IEEE fp32 division.
+__global__ __launch_bounds__(kPackThreads) void k_ternarize_pack(const float4* __restrict__ w4, int64_t n, int64_t k,
                                                                   const float* __restrict__ gamma_ptr,
-                                                                  uint4* __restrict__ packed) {
-  const int64_t kt_count = k / kTileCols;
+                                                                  uint32_t* __restrict__ packed) {
+  const int64_t k4 = k / 4;
   const int64_t n_pad = (n + kTileRows - 1) / kTileRows * kTileRows;
-  const int64_t idx = (int64_t)blockIdx.x * kPackThreads + threadIdx.x;
-  if (idx >= n_pad * kt_count) return;
-  const int64_t row = idx / kt_count;
-  const int64_t kt = idx % kt_count;
-  uint4* dst = packed + ((row / kTileRows) * kt_count + kt) * (kTileBytes / 16) + (row % kTileRows);
-  if (row >= n) {
-    *dst = make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
-    return;
-  }
+  const int64_t idx = (int64_t)blockIdx.x * kPackThreads + threadIdx.x;  // float4 index in the padded matrix
+  if (idx >= n_pad * k4) return;  // whole 16-lane groups leave together (k4 is a multiple of 16)
+  const int64_t row = idx / k4;
+  const int64_t c4 = idx % k4;  // float4 within the row
+  const int j = (int)(c4 & 15);  // lane within the tile row
+  const int64_t kt = c4 >> 4;
   const float denom = *gamma_ptr + 1e-5f;
-  const float4* src = reinterpret_cast<const float4*>(w + row * k + kt * kTileCols);
-  uint32_t word[4] = {0u, 0u, 0u, 0u};
+  uint32_t part = 0;
+  if (row < n) {
+    const float4 v = w4[idx];
+    const float c[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-#pragma unroll
-    for (int b4 = 0; b4 < 4; ++b4) {
-      float4 v = src[f * 4 + b4];
-      float c[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float r = __builtin_rintf(c[j] / denom);  // IEEE division, then round half to even
-        r = fminf(fmaxf(r, -1.0f), 1.0f);
-        uint32_t code = (uint32_t)((int)r + 1);
-        word[b4] |= code << (8 * j + 2 * f);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const float r = fminf(fmaxf(__builtin_rintf(c[i] / denom), -1.0f), 1.0f);  // IEEE division, then RNE
+      part |= (uint32_t)((int)r + 1) << (8 * i + 2 * (j >> 2));
     }
+  } else {
+    part = 0x01010101u << (2 * (j >> 2));
   }
-  *dst = make_uint4(word[0], word[1], word[2], word[3]);
+  // OR over the four lanes of the same dword (lane offsets 4 and 8 within the 16-lane row)
+  part |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)part, 0x124, 0xF, 0xF, false);  // row_ror:4
+  part |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)part, 0x128, 0xF, 0xF, false);  // row_ror:8
+  if (j < 4) packed[(((row / kTileRows) * (k / kTileCols) + kt) * kTileRows + (row % kTileRows)) * 4 + j] = part;
 }
 
 __global__ __launch_bounds__(kPackThreads) void k_unpack(const uint4* __restrict__ packed, int64_t n, int64_t k,
@@ -202,8 +275,8 @@ hipError_t launch_zero_bins(unsigned long long* bins, hipStream_t s) {
 
 hipError_t launch_absmean_bins(const float* w, int64_t count, unsigned long long* bins, hipStream_t s) {
   const int64_t n4 = count / 4;
-  int64_t blocks = (n4 + kBinThreads - 1) / kBinThreads;
-  if (blocks > 4096) blocks = 4096;
+  int64_t blocks = (n4 + kBinThreads * kBinLoads - 1) / (kBinThreads * kBinLoads);
+  if (blocks > 2048) blocks = 2048;  // 2^19 threads: at most 2^20 values per lane for count <= 2^39
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(k_absmean_bins, dim3((unsigned)blocks), dim3(kBinThreads), 0, s,
                      reinterpret_cast<const float4*>(w), n4, bins);
@@ -211,17 +284,18 @@ hipError_t launch_absmean_bins(const float* w, int64_t count, unsigned long long
 }
 
 hipError_t launch_gamma_fold(const unsigned long long* bins, int64_t count, float* gamma, hipStream_t s) {
-  hipLaunchKernelGGL(k_gamma_fold, dim3(1), dim3(64), 0, s, bins, (unsigned long long)count, gamma);
+  hipLaunchKernelGGL(k_gamma_fold, dim3(1), dim3(kBins), 0, s, bins, (unsigned long long)count, gamma);
   return hipGetLastError();
 }
 
 hipError_t launch_ternarize_pack(const float* w, int64_t n, int64_t k, const float* gamma, uint8_t* packed,
                                  hipStream_t s) {
   const int64_t n_pad = (n + kTileRows - 1) / kTileRows * kTileRows;
-  const int64_t threads = n_pad * (k / kTileCols);
+  const int64_t threads = n_pad * (k / 4);
   const int64_t blocks = (threads + kPackThreads - 1) / kPackThreads;
-  hipLaunchKernelGGL(k_ternarize_pack, dim3((unsigned)blocks), dim3(kPackThreads), 0, s, w, n, k, gamma,
-                     reinterpret_cast<uint4*>(packed));
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_ternarize_pack, dim3((unsigned)blocks), dim3(kPackThreads), 0, s,
+                     reinterpret_cast<const float4*>(w), n, k, gamma, reinterpret_cast<uint32_t*>(packed));
   return hipGetLastError();
 }
 

@@ -49,6 +49,8 @@ def test_ternarize_pack_validation():
     assert f(FAKE, 16, 96, FAKE, FAKE, FAKE, 2048, None) == BL_ERR_SHAPE
     assert f(FAKE, 16, 0, FAKE, FAKE, FAKE, 2048, None) == BL_ERR_SHAPE
     assert f(FAKE, 1 << 31, 64, FAKE, FAKE, FAKE, 2048, None) == BL_ERR_SHAPE
+    # more than 2^39 weights: the exact integer sum of |w| could overflow
+    assert f(FAKE, (1 << 17) + 16, 1 << 22, FAKE, FAKE, FAKE, 2048, None) == BL_ERR_SHAPE
     assert f(FAKE + 4, 16, 64, FAKE, FAKE, FAKE, 2048, None) == BL_ERR_ALIGN
     assert f(FAKE, 16, 64, FAKE + 8, FAKE, FAKE, 2048, None) == BL_ERR_ALIGN
     assert f(FAKE, 16, 64, FAKE, FAKE, FAKE, 2047, None) == BL_ERR_WORKSPACE

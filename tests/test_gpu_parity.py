@@ -105,6 +105,14 @@ def test_pack_gamma_exotic_values():
         (rng.standard_normal((32, 128)) * 10.0 ** rng.uniform(-30, 30, size=(32, 128))).astype(np.float32),
         np.zeros((16, 64), np.float32),
     ]
+    # many workgroups whose register windows differ: mostly N(0, 0.02), with
+    # entries 1e6 and 1e-8 times larger and exact zeros scattered through
+    w = (rng.standard_normal((600, 2560)) * 0.02).astype(np.float32)
+    pick = rng.random(w.shape)
+    w[pick < 0.01] *= np.float32(1e6)
+    w[(pick >= 0.01) & (pick < 0.02)] *= np.float32(1e-8)
+    w[(pick >= 0.02) & (pick < 0.03)] = 0.0
+    cases.append(w)
     for w in cases:
         check_pack(w)
 
@@ -181,7 +189,7 @@ def random_layer(rng, n, k):
 
 
 @pytest.mark.parametrize("m", [1, 2, 3, 5, 16, 17, 33, 64, 65, 100])
-@pytest.mark.parametrize("n,k", [(1, 64), (7, 128), (31, 192), (33, 320), (48, 1024), (20, 1088)])
+@pytest.mark.parametrize("n,k", [(1, 64), (7, 128), (31, 192), (33, 320), (48, 1024), (20, 1088), (264, 320)])
 def test_linear_brute_force_shapes(m, n, k):
     rng = np.random.default_rng(1000 * m + 10 * n + k)
     buf, qw = random_layer(rng, n, k)
