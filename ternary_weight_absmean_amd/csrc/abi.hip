@@ -26,7 +26,7 @@ size_t bl_packed_bytes(int64_t n, int64_t k) {
 
 size_t bl_ternarize_pack_workspace_bytes(int64_t n, int64_t k) {
   if (n < 1 || n > BL_MAX_N || !valid_k(k) || !product_ok(n + 16, k)) return 0;
-  return 256 * sizeof(unsigned long long);
+  return bl::kPackWorkspaceBytes;
 }
 
 bl_status bl_ternarize_pack(const float* w, int64_t n, int64_t k, uint8_t* packed, float* gamma, void* workspace,
@@ -37,8 +37,7 @@ bl_status bl_ternarize_pack(const float* w, int64_t n, int64_t k, uint8_t* packe
   if (workspace_bytes < bl_ternarize_pack_workspace_bytes(n, k)) return BL_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   unsigned long long* bins = (unsigned long long*)workspace;
-  hipError_t e = bl::launch_zero_bins(bins, s);
-  if (e == hipSuccess) e = bl::launch_absmean_bins(w, n * k, bins, s);
+  hipError_t e = bl::launch_absmean_bins(w, n * k, bins, s);
   if (e == hipSuccess) e = bl::launch_gamma_fold(bins, n * k, gamma, s);
   if (e == hipSuccess) e = bl::launch_ternarize_pack(w, n, k, gamma, packed, s);
   return from_hip(e);

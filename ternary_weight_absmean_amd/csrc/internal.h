@@ -13,9 +13,11 @@ constexpr int kTileCols = 64;
 constexpr int kTileBytes = 256;
 
 // Weight packer (absmean exponent bins -> exact gamma -> ternarize + pack).
-hipError_t launch_zero_bins(unsigned long long* bins, hipStream_t s);
-hipError_t launch_absmean_bins(const float* w, int64_t count, unsigned long long* bins, hipStream_t s);
-hipError_t launch_gamma_fold(const unsigned long long* bins, int64_t count, float* gamma, hipStream_t s);
+// The workspace holds 256 exponent bins (u64) per absmean workgroup.
+constexpr int kAbsmeanMaxBlocks = 256;
+constexpr size_t kPackWorkspaceBytes = (size_t)kAbsmeanMaxBlocks * 256 * sizeof(unsigned long long);
+hipError_t launch_absmean_bins(const float* w, int64_t count, unsigned long long* ws, hipStream_t s);
+hipError_t launch_gamma_fold(const unsigned long long* ws, int64_t count, float* gamma, hipStream_t s);
 hipError_t launch_ternarize_pack(const float* w, int64_t n, int64_t k, const float* gamma, uint8_t* packed,
                                  hipStream_t s);
 hipError_t launch_unpack(const uint8_t* packed, int64_t n, int64_t k, int8_t* q, hipStream_t s);

@@ -16,13 +16,13 @@
 // sum_e bins[e] * 2^(e-150) / (n*k) exactly in multi-word integer arithmetic
 // and rounds it once to fp32 (nearest, ties to even).
 //
-// Kernels (all HBM-bound streaming passes except the one-thread fold):
-//   k_zero_bins        256 x u64 <- 0
-//   k_absmean_bins     read w once; per-wave LDS bins; one global atomic per
-//                      non-empty bin per workgroup
-//   k_gamma_fold       exact mean -> gamma (device memory; no host readback)
-//   k_ternarize_pack   read w again; one thread per 16-byte row chunk of a
-//                      16x64 tile; IEEE fp32 divide, round-half-even, clamp
+// Kernels (all HBM-bound streaming passes except the fold):
+//   k_absmean_bins     read w once; exponent bins per workgroup (registers
+//                      and LDS), written to the workspace (no global atomics)
+//   k_gamma_fold       sum the workgroups' bins, exact mean -> gamma (device
+//                      memory; no host readback)
+//   k_ternarize_pack   read w again; lane per float4, 16 lanes per 64-column
+//                      row segment; IEEE fp32 divide, round-half-even, clamp
 //   k_unpack           packed -> int8 trits (inspection helper)
 #include "device_util.h"
 #include "internal.h"
@@ -31,17 +31,15 @@ namespace bl {
 namespace {
 
 constexpr int kBins = 256;
+constexpr int kBinThreads = 512;
+constexpr int kBinLoads = 8;    // float4 loads per thread per iteration (in flight together)
+constexpr int kWindow = 16;     // exponents accumulated in registers
 
 __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
 }
-constexpr int kBinThreads = 256;
-constexpr int kBinLoads = 4;   // float4 loads per thread per iteration (in flight together)
-constexpr int kWindow = 16;    // exponents accumulated in registers
-
-__global__ void k_zero_bins(unsigned long long* bins) { bins[threadIdx.x] = 0ull; }
 
 // Exact sum of |w| by exponent.  |w| = sig * 2^(e-150) with e the biased
 // exponent and sig the significand (hidden bit included for e > 0); the
@@ -52,15 +50,16 @@ __global__ void k_zero_bins(unsigned long long* bins) { bins[threadIdx.x] = 0ull
 // wave's first values; that register equals sum sig * 2^(e - e0), i.e. the
 // bin e0 contribution of the window, and is split into its low and high 32
 // bits for bins e0 and e0 + 32.  Values outside the window (and subnormals)
-// go to LDS bins by atomic add.  All additions are of integers, so the
-// result does not depend on the grid or the order.  Per lane at most 2^20
-// values (count <= 2^39 over 2^19 threads) of at most 2^39 each, and no bin
-// exceeds count * 2^24 + 2^51 < 2^64: no overflow.
+// go to LDS bins by atomic add.  Each workgroup writes its 256 bins to its
+// row of the workspace; the fold adds the rows.  All additions are of
+// integers, so the result does not depend on the grid or the order.  At
+// most 2^17 threads and count <= 2^39: at most 2^22 values per lane of at
+// most 2^39 each, and no bin total exceeds count * 2^24 + 2^49 < 2^64.
 __global__ __launch_bounds__(kBinThreads) void k_absmean_bins(const float4* __restrict__ w4, int64_t n4,
-                                                               unsigned long long* __restrict__ bins) {
+                                                               unsigned long long* __restrict__ ws) {
   __shared__ unsigned long long lbins[kBins];
   const int tid = threadIdx.x;
-  lbins[tid] = 0ull;
+  if (tid < kBins) lbins[tid] = 0ull;
   __syncthreads();
   const int64_t stride = (int64_t)gridDim.x * kBinThreads * kBinLoads;
   int e0 = -1;  // window base, chosen from the first batch
@@ -110,8 +109,7 @@ __global__ __launch_bounds__(kBinThreads) void k_absmean_bins(const float4* __re
     }
   }
   __syncthreads();
-  const unsigned long long s = lbins[tid];
-  if (s) atomicAdd(&bins[tid], s);
+  if (tid < kBins) ws[(int64_t)blockIdx.x * kBins + tid] = lbins[tid];
 }
 
 // ---------------------------------------------------------------- exact fold
@@ -141,32 +139,54 @@ __device__ __forceinline__ uint32_t div_step(unsigned long long cur, unsigned lo
   return (uint32_t)q;
 }
 
-// One workgroup: the 256 bins are read in parallel into LDS; one thread then
-// forms X = sum bins[e] * 2^(max(e,1) - 1) = sum |w| * 2^149 in 16-bit limbs,
-// divides by the element count (long division by limbs), and rounds the
-// quotient once to fp32, nearest with ties to even.
-__global__ __launch_bounds__(kBins) void k_gamma_fold(const unsigned long long* __restrict__ bins,
-                                                       unsigned long long count, float* __restrict__ gamma) {
-  __shared__ unsigned long long lb[kBins];
-  lb[threadIdx.x] = bins[threadIdx.x];
-  __syncthreads();
-  if (threadIdx.x != 0) return;
-  uint32_t x[kLimbs];
+// One workgroup: four threads per exponent e add its bins over the absmean
+// workgroups, and thread e adds the value bins[e] * 2^(max(e,1) - 1) into 16-bit limbs
+// of X = sum |w| * 2^149 (LDS atomics; each limb sum stays below 2^25); one
+// thread then propagates the carries, divides by the element count (long
+// division by limbs) and rounds the quotient once to fp32, nearest with
+// ties to even.
+constexpr int kFoldThreads = 1024;  // four threads per exponent share the workgroup rows
+
+__global__ __launch_bounds__(kFoldThreads) void k_gamma_fold(const unsigned long long* __restrict__ ws, int blocks,
+                                                              unsigned long long count, float* __restrict__ gamma) {
+  __shared__ uint32_t xl[kLimbs];
+  __shared__ unsigned long long part[kFoldThreads / kBins][kBins];
+  const int e = threadIdx.x % kBins;
+  const int p = threadIdx.x / kBins;
+  constexpr int kParts = kFoldThreads / kBins;
+  if (threadIdx.x < kLimbs) xl[threadIdx.x] = 0;
+  unsigned long long v = 0;
+  {
+    int b = p;
+    for (; b + 15 * kParts < blocks; b += 16 * kParts) {  // 16 loads in flight
+      unsigned long long t[16];
 #pragma unroll
-  for (int i = 0; i < kLimbs; ++i) x[i] = 0;
-  for (int e = 0; e < kBins - 1; ++e) {
-    const unsigned long long v = lb[e];
-    if (v == 0) continue;
+      for (int j = 0; j < 16; ++j) t[j] = ws[(int64_t)(b + j * kParts) * kBins + e];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v += t[j];
+    }
+    for (; b < blocks; b += kParts) v += ws[(int64_t)b * kBins + e];
+  }
+  part[p][e] = v;
+  __syncthreads();
+#pragma unroll
+  for (int q = 1; q < kParts; ++q) v += part[q][e];
+  if (p == 0 && v != 0 && e < kBins - 1) {
     const int sh = e ? e - 1 : 0;
     const int q = sh >> 4, r = sh & 15;
     const unsigned long long lo = v << r;
     const unsigned long long hi = r ? (v >> (64 - r)) : 0ull;
-    x[q + 0] += (uint32_t)(lo & 0xFFFFu);
-    x[q + 1] += (uint32_t)((lo >> 16) & 0xFFFFu);
-    x[q + 2] += (uint32_t)((lo >> 32) & 0xFFFFu);
-    x[q + 3] += (uint32_t)((lo >> 48) & 0xFFFFu);
-    x[q + 4] += (uint32_t)(hi & 0xFFFFu);
+    atomicAdd(&xl[q + 0], (uint32_t)(lo & 0xFFFFu));
+    atomicAdd(&xl[q + 1], (uint32_t)((lo >> 16) & 0xFFFFu));
+    atomicAdd(&xl[q + 2], (uint32_t)((lo >> 32) & 0xFFFFu));
+    atomicAdd(&xl[q + 3], (uint32_t)((lo >> 48) & 0xFFFFu));
+    atomicAdd(&xl[q + 4], (uint32_t)(hi & 0xFFFFu));
   }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  uint32_t x[kLimbs];
+#pragma unroll
+  for (int i = 0; i < kLimbs; ++i) x[i] = xl[i];
   uint32_t carry = 0;
   for (int i = 0; i < kLimbs; ++i) {
     const uint32_t t = x[i] + carry;
@@ -268,23 +288,22 @@ __global__ __launch_bounds__(kPackThreads) void k_unpack(const uint4* __restrict
 
 }  // namespace
 
-hipError_t launch_zero_bins(unsigned long long* bins, hipStream_t s) {
-  hipLaunchKernelGGL(k_zero_bins, dim3(1), dim3(kBins), 0, s, bins);
-  return hipGetLastError();
-}
-
-hipError_t launch_absmean_bins(const float* w, int64_t count, unsigned long long* bins, hipStream_t s) {
+int absmean_blocks(int64_t count) {
   const int64_t n4 = count / 4;
   int64_t blocks = (n4 + kBinThreads * kBinLoads - 1) / (kBinThreads * kBinLoads);
-  if (blocks > 2048) blocks = 2048;  // 2^19 threads: at most 2^20 values per lane for count <= 2^39
-  if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(k_absmean_bins, dim3((unsigned)blocks), dim3(kBinThreads), 0, s,
-                     reinterpret_cast<const float4*>(w), n4, bins);
+  if (blocks > kAbsmeanMaxBlocks) blocks = kAbsmeanMaxBlocks;
+  return blocks < 1 ? 1 : (int)blocks;
+}
+
+hipError_t launch_absmean_bins(const float* w, int64_t count, unsigned long long* ws, hipStream_t s) {
+  hipLaunchKernelGGL(k_absmean_bins, dim3((unsigned)absmean_blocks(count)), dim3(kBinThreads), 0, s,
+                     reinterpret_cast<const float4*>(w), count / 4, ws);
   return hipGetLastError();
 }
 
-hipError_t launch_gamma_fold(const unsigned long long* bins, int64_t count, float* gamma, hipStream_t s) {
-  hipLaunchKernelGGL(k_gamma_fold, dim3(1), dim3(kBins), 0, s, bins, (unsigned long long)count, gamma);
+hipError_t launch_gamma_fold(const unsigned long long* ws, int64_t count, float* gamma, hipStream_t s) {
+  hipLaunchKernelGGL(k_gamma_fold, dim3(1), dim3(kFoldThreads), 0, s, ws, absmean_blocks(count),
+                     (unsigned long long)count, gamma);
   return hipGetLastError();
 }
 

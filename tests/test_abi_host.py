@@ -37,23 +37,26 @@ def test_sizes():
     assert bl.bl_packed_bytes(0, 64) == 0
     assert bl.bl_packed_bytes(16, 63) == 0
     assert bl.bl_packed_bytes(16, 1 << 23) == 0
-    assert bl.bl_ternarize_pack_workspace_bytes(57344, 8192) == 2048
+    WS = 256 * 256 * 8
+    assert bl.bl_ternarize_pack_workspace_bytes(57344, 8192) == WS
+    assert bl.bl_ternarize_pack_workspace_bytes(16, 64) == WS
     assert bl.bl_ternarize_pack_workspace_bytes(0, 64) == 0
 
 
 def test_ternarize_pack_validation():
     f = lib.bl_ternarize_pack
-    assert f(None, 16, 64, FAKE, FAKE, FAKE, 2048, None) == BL_ERR_NULL
-    assert f(FAKE, 16, 64, FAKE, FAKE, None, 2048, None) == BL_ERR_NULL
-    assert f(FAKE, 0, 64, FAKE, FAKE, FAKE, 2048, None) == BL_ERR_SHAPE
-    assert f(FAKE, 16, 96, FAKE, FAKE, FAKE, 2048, None) == BL_ERR_SHAPE
-    assert f(FAKE, 16, 0, FAKE, FAKE, FAKE, 2048, None) == BL_ERR_SHAPE
-    assert f(FAKE, 1 << 31, 64, FAKE, FAKE, FAKE, 2048, None) == BL_ERR_SHAPE
+    WS = 256 * 256 * 8
+    assert f(None, 16, 64, FAKE, FAKE, FAKE, WS, None) == BL_ERR_NULL
+    assert f(FAKE, 16, 64, FAKE, FAKE, None, WS, None) == BL_ERR_NULL
+    assert f(FAKE, 0, 64, FAKE, FAKE, FAKE, WS, None) == BL_ERR_SHAPE
+    assert f(FAKE, 16, 96, FAKE, FAKE, FAKE, WS, None) == BL_ERR_SHAPE
+    assert f(FAKE, 16, 0, FAKE, FAKE, FAKE, WS, None) == BL_ERR_SHAPE
+    assert f(FAKE, 1 << 31, 64, FAKE, FAKE, FAKE, WS, None) == BL_ERR_SHAPE
     # more than 2^39 weights: the exact integer sum of |w| could overflow
-    assert f(FAKE, (1 << 17) + 16, 1 << 22, FAKE, FAKE, FAKE, 2048, None) == BL_ERR_SHAPE
-    assert f(FAKE + 4, 16, 64, FAKE, FAKE, FAKE, 2048, None) == BL_ERR_ALIGN
-    assert f(FAKE, 16, 64, FAKE + 8, FAKE, FAKE, 2048, None) == BL_ERR_ALIGN
-    assert f(FAKE, 16, 64, FAKE, FAKE, FAKE, 2047, None) == BL_ERR_WORKSPACE
+    assert f(FAKE, (1 << 17) + 16, 1 << 22, FAKE, FAKE, FAKE, WS, None) == BL_ERR_SHAPE
+    assert f(FAKE + 4, 16, 64, FAKE, FAKE, FAKE, WS, None) == BL_ERR_ALIGN
+    assert f(FAKE, 16, 64, FAKE + 8, FAKE, FAKE, WS, None) == BL_ERR_ALIGN
+    assert f(FAKE, 16, 64, FAKE, FAKE, FAKE, WS - 1, None) == BL_ERR_WORKSPACE
 
 
 def test_quant_act_validation():
