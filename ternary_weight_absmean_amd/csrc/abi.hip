@@ -62,7 +62,7 @@ bl_status bl_linear(const uint8_t* packed, const float* gamma, const int8_t* xq,
       (acc && !aligned(acc, 4)) || (y && !aligned(y, 2)))
     return BL_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
-  if (m <= 16) return from_hip(bl::launch_gemv(packed, gamma, xq, alpha, m, n, k, acc, y, s));
+  if (bl::gemv_serves(m, n)) return from_hip(bl::launch_gemv(packed, gamma, xq, alpha, m, n, k, acc, y, s));
   return from_hip(bl::launch_gemm(packed, gamma, xq, alpha, m, n, k, acc, y, s));
 }
 
@@ -81,7 +81,7 @@ bl_status bl_bitlinear(const uint8_t* packed, const float* gamma, const uint16_t
     return from_hip(bl::launch_gemv_fused(packed, gamma, x, m, n, k, xq, alpha, acc, y, s));
   hipError_t e = bl::launch_quant_act(x, m, k, xq, alpha, s);
   if (e != hipSuccess || n == 0) return from_hip(e);
-  if (m <= 16) return from_hip(bl::launch_gemv(packed, gamma, xq, alpha, m, n, k, acc, y, s));
+  if (bl::gemv_serves(m, n)) return from_hip(bl::launch_gemv(packed, gamma, xq, alpha, m, n, k, acc, y, s));
   return from_hip(bl::launch_gemm(packed, gamma, xq, alpha, m, n, k, acc, y, s));
 }
 

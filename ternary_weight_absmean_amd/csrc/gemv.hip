@@ -567,7 +567,7 @@ __global__ __launch_bounds__(kW * 64) void k_gemv_direct(const uint4* __restrict
 // workgroup.  The next chunk's activations and weights are loaded into
 // registers while the current chunk is multiplied; two barriers per chunk
 // guard the single LDS buffer.  Codes become signed trits with v_perm.
-template <int kRT, int kW, int kGW>
+template <int kRT, int kW, int kGW, int kTB>
 __global__ __launch_bounds__(kW * 64) void k_gemv_lds(const uint4* __restrict__ packed,
                                                        const float* __restrict__ gamma_ptr,
                                                        const int8_t* __restrict__ xq,
@@ -577,11 +577,13 @@ __global__ __launch_bounds__(kW * 64) void k_gemv_lds(const uint4* __restrict__ 
   constexpr int kT = kW * 64;
   constexpr int kC = kW * kGW * 256;          // columns per chunk
   constexpr int kLd = kC + 16;                // LDS row stride
-  constexpr int kPieces = 16 * kC / 16;       // 16-byte pieces per chunk (16 token rows)
+  constexpr int kRowsX = 16 * kTB;            // token rows staged
+  constexpr int kPieces = kRowsX * kC / 16;   // 16-byte pieces per chunk
   constexpr int kXLoads = kPieces / kT;       // per thread
+  constexpr int kAcc = kTB == 1 ? 2 : 1;      // independent accumulator chains per (tile, token block)
   static_assert(kPieces % kT == 0, "chunk must split evenly over the threads");
-  __shared__ uint4 xs_raw[16 * kLd / 16];
-  __shared__ v4i partial[kRT][kW][64];
+  static_assert(kRT * kTB * kW * 1024 <= kRowsX * kLd, "partial sums reuse the activation buffer");
+  __shared__ uint4 xs_raw[kRowsX * kLd / 16];
   int8_t* xs = reinterpret_cast<int8_t*>(xs_raw);
 
   const int tid = threadIdx.x;
@@ -590,14 +592,13 @@ __global__ __launch_bounds__(kW * 64) void k_gemv_lds(const uint4* __restrict__ 
   const int64_t tile0 = (int64_t)blockIdx.x * kRT;
   const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
   const int tiles_here = (int)min((int64_t)kRT, row_tiles - tile0);
-  const int64_t tok0 = (int64_t)blockIdx.y * 16;
-  const int rows = (int)min((int64_t)16, m - tok0);
+  const int64_t tok0 = (int64_t)blockIdx.y * kRowsX;
+  const int rows = (int)min((int64_t)kRowsX, m - tok0);
   const int kt_count = (int)(k / kTileCols);
   const int groups = (kt_count + 3) / 4;
   const int chunks = (int)((k + kC - 1) / kC);
   const int sub = lane >> 4;
   const int col = lane & 15;
-  const bool has_tok = col < rows;
 
   const uint32_t tile_bytes = (uint32_t)(kt_count * kTileBytes);
   __amdgpu_buffer_rsrc_t wrsrc[kRT];
@@ -606,7 +607,11 @@ __global__ __launch_bounds__(kW * 64) void k_gemv_lds(const uint4* __restrict__ 
     wrsrc[rt] = buffer_rsrc(packed + (tile0 + rt) * kt_count * (kTileBytes / 16), rt < tiles_here ? tile_bytes : 0u);
   const __amdgpu_buffer_rsrc_t xrsrc = buffer_rsrc(xq + tok0 * k, (uint32_t)(rows * k));
   const float gamma = buffer_load_f32(buffer_rsrc(gamma_ptr, 4), 0);
-  const float alpha_tok = buffer_load_f32(buffer_rsrc(alpha + tok0, (uint32_t)(rows * 4)), has_tok ? col * 4 : kOutOfRange);
+  const __amdgpu_buffer_rsrc_t arsrc = buffer_rsrc(alpha + tok0, (uint32_t)(rows * 4));
+  float alpha_tok[kTB];
+#pragma unroll
+  for (int tb = 0; tb < kTB; ++tb)
+    alpha_tok[tb] = buffer_load_f32(arsrc, 16 * tb + col < rows ? (uint32_t)((16 * tb + col) * 4) : kOutOfRange);
 
   // piece p of a chunk: token row p / (kC / 16), 16 bytes at column 16 * (p % (kC / 16))
   auto load_x = [&](int c, uint4 (&v)[kXLoads]) {
@@ -630,9 +635,13 @@ __global__ __launch_bounds__(kW * 64) void k_gemv_lds(const uint4* __restrict__ 
     }
   };
 
-  v4i acc[kRT][2];
+  v4i acc[kRT][kTB][kAcc];
 #pragma unroll
-  for (int rt = 0; rt < kRT; ++rt) acc[rt][0] = acc[rt][1] = v4i{0, 0, 0, 0};
+  for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+    for (int tb = 0; tb < kTB; ++tb)
+#pragma unroll
+      for (int j = 0; j < kAcc; ++j) acc[rt][tb][j] = v4i{0, 0, 0, 0};
   uint4 xv[kXLoads];
   uint4 a_cur[kRT][kGW];
   load_x(0, xv);
@@ -652,16 +661,19 @@ __global__ __launch_bounds__(kW * 64) void k_gemv_lds(const uint4* __restrict__ 
     }
 #pragma unroll
     for (int u = 0; u < kGW; ++u) {
-      // local tile 4 * (wave + u * kW) + sub of this chunk, field f
-      const int8_t* xt = xs + col * kLd + (4 * (wave + u * kW) + sub) * kTileCols;
-      uint4 b[4];
 #pragma unroll
-      for (int f = 0; f < 4; ++f) b[f] = *reinterpret_cast<const uint4*>(xt + 16 * f);
+      for (int tb = 0; tb < kTB; ++tb) {
+        // local tile 4 * (wave + u * kW) + sub of this chunk, field f, token row 16 tb + col
+        const int8_t* xt = xs + (16 * tb + col) * kLd + (4 * (wave + u * kW) + sub) * kTileCols;
+        uint4 b[4];
 #pragma unroll
-      for (int rt = 0; rt < kRT; ++rt) {
+        for (int f = 0; f < 4; ++f) b[f] = *reinterpret_cast<const uint4*>(xt + 16 * f);
 #pragma unroll
-        for (int f = 0; f < 4; ++f)
-          acc[rt][f & 1] = mfma_16x16x64(unpack_field(a_cur[rt][u], f), as_v4i(b[f]), acc[rt][f & 1]);
+        for (int rt = 0; rt < kRT; ++rt) {
+#pragma unroll
+          for (int f = 0; f < 4; ++f)
+            acc[rt][tb][f % kAcc] = mfma_16x16x64(unpack_field(a_cur[rt][u], f), as_v4i(b[f]), acc[rt][tb][f % kAcc]);
+        }
       }
     }
     if (c + 1 < chunks) {
@@ -672,23 +684,31 @@ __global__ __launch_bounds__(kW * 64) void k_gemv_lds(const uint4* __restrict__ 
       }
     }
   }
-#pragma unroll
-  for (int rt = 0; rt < kRT; ++rt) {
-    add4(acc[rt][0], acc[rt][1]);
-    partial[rt][wave][lane] = acc[rt][0];
-  }
+  // the waves' partial sums, in the activation buffer once everyone is done with it
   __syncthreads();
-  // wave w finishes row tiles w, w + kW, ...
-  if (!has_tok) return;
-  const float scale = (gamma * alpha_tok) / 127.0f;
+  v4i* partial = reinterpret_cast<v4i*>(xs_raw);  // [kRT][kTB][kW][64]
 #pragma unroll
-  for (int rt = 0; rt < kRT; ++rt) {
-    if (rt % kW != wave || rt >= tiles_here) continue;
-    v4i sum = partial[rt][0][lane];
+  for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
-    for (int w = 1; w < kW; ++w) add4(sum, partial[rt][w][lane]);
-    store_tile(sum, (tile0 + rt) * kTileRows + 4 * sub, tok0 + col, n, scale, acc_out, y_out);
-  }
+    for (int tb = 0; tb < kTB; ++tb) {
+      v4i a = acc[rt][tb][0];
+      if (kAcc == 2) add4(a, acc[rt][tb][kAcc - 1]);
+      partial[((rt * kTB + tb) * kW + wave) * 64 + lane] = a;
+    }
+  __syncthreads();
+  // wave w finishes the (row tile, token block) pairs w, w + kW, ...
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+    for (int tb = 0; tb < kTB; ++tb) {
+      const int pair = rt * kTB + tb;
+      if (pair % kW != wave || rt >= tiles_here || 16 * tb + col >= rows) continue;
+      v4i sum = partial[(pair * kW) * 64 + lane];
+#pragma unroll
+      for (int w = 1; w < kW; ++w) add4(sum, partial[(pair * kW + w) * 64 + lane]);
+      const float scale = (gamma * alpha_tok[tb]) / 127.0f;
+      store_tile(sum, (tile0 + rt) * kTileRows + 4 * sub, tok0 + 16 * tb + col, n, scale, acc_out, y_out);
+    }
 }
 
 }  // namespace
@@ -749,14 +769,24 @@ hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* 
   if ((m + 15) / 16 > 65535) return hipErrorInvalidValue;
   const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
   const uint4* p = reinterpret_cast<const uint4*>(packed);
+  if (m > 16) {
+    // up to 64 tokens per workgroup: the unpacked weights serve 4 token blocks
+    const int rt = row_tiles >= 512 ? 2 : 1;
+    const dim3 grid((unsigned)((row_tiles + rt - 1) / rt), (unsigned)((m + 63) / 64));
+    if (rt == 2)
+      hipLaunchKernelGGL((k_gemv_lds<2, 4, 1, 4>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
+    else
+      hipLaunchKernelGGL((k_gemv_lds<1, 4, 1, 4>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
+    return hipGetLastError();
+  }
   if (m >= 2) {
     // two row tiles per workgroup once there are ~2 per CU
     const int rt = row_tiles >= 512 ? 2 : 1;
     const dim3 grid((unsigned)((row_tiles + rt - 1) / rt), (unsigned)((m + 15) / 16));
     if (rt == 2)
-      hipLaunchKernelGGL((k_gemv_lds<2, 4, 4>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
+      hipLaunchKernelGGL((k_gemv_lds<2, 4, 4, 1>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
     else
-      hipLaunchKernelGGL((k_gemv_lds<1, 4, 4>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
+      hipLaunchKernelGGL((k_gemv_lds<1, 4, 4, 1>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
     return hipGetLastError();
   }
   // one token: its activation bytes are few, so each lane loads its own

@@ -25,7 +25,10 @@ hipError_t launch_unpack(const uint8_t* packed, int64_t n, int64_t k, int8_t* q,
 // Per-token absmax int8 quantizer.
 hipError_t launch_quant_act(const uint16_t* x, int64_t m, int64_t k, int8_t* xq, float* alpha, hipStream_t s);
 
-// Ternary x int8 products (m <= 16: GEMV; larger m: LDS-tiled GEMM).
+// Ternary x int8 products: GEMV-style kernels that stream the weights once
+// per 16 or 64 tokens (up to 16 tokens, and up to 64 unless the matrix has
+// enough rows to keep the GEMM's larger tiles busy), else the LDS-tiled GEMM.
+inline bool gemv_serves(int64_t m, int64_t n) { return m <= 16 || (m <= 64 && (n + 15) / 16 < 2048); }
 hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
                        int64_t n, int64_t k, int32_t* acc, uint16_t* y, hipStream_t s);
 // Fused per-token quantization + product for a small token block

@@ -200,7 +200,11 @@ def test_linear_brute_force_shapes(m, n, k):
     check_linear(u8(buf), f32(np.array([gamma])), qw, gamma, xq_np=xq, alpha_np=alpha)
 
 
-@pytest.mark.parametrize("m,n,k", [(16, 16400, 1024), (5, 32800, 320), (9, 16416, 2112)])
+@pytest.mark.parametrize("m,n,k", [(16, 16400, 1024), (5, 32800, 320), (9, 16416, 2112),
+                                   # 17..64 tokens in one workgroup (four token blocks), ragged chunk
+                                   (40, 1000, 4160), (64, 8200, 320),
+                                   # the same token counts on a matrix with many row tiles: the GEMM
+                                   (20, 32784, 128)])
 def test_linear_multi_tile_workgroups(m, n, k):
     """Token blocks whose activation loads serve 2 or 4 row tiles per
     workgroup, with a ragged last workgroup."""
