@@ -307,6 +307,7 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_m1(const uint4* __restric
                                                            const uint4* __restrict__ x, float* __restrict__ alpha,
                                                            int8_t* __restrict__ xq_out, int n, int k,
                                                            int32_t* __restrict__ acc_out, uint16_t* __restrict__ y_out) {
+  constexpr int kB = kGroupsPerBatch;  // weight groups per batch (larger batches measured no faster)
   extern __shared__ uint4 xw_raw[];  // [wave][groups of this wave][256 bytes]
   __shared__ v4i partial[kRT][kW][64];
   __shared__ int wave_max[kW];
@@ -353,11 +354,11 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_m1(const uint4* __restric
   };
   // this wave's gi-th group within a row tile
   auto w_off = [&](int gi) { return (uint32_t)((wave + gi * kW) * 1024 + lane * 16); };
-  uint4 a_cur[kGroupsPerBatch];
+  uint4 a_cur[kB];
   {
     const __amdgpu_buffer_rsrc_t r0 = tile_rsrc(0);
 #pragma unroll
-    for (int u = 0; u < kGroupsPerBatch; ++u) a_cur[u] = buffer_load16(r0, w_off(u));
+    for (int u = 0; u < kB; ++u) a_cur[u] = buffer_load16(r0, w_off(u));
   }
   const float gamma = buffer_load_f32(buffer_rsrc(gamma_ptr, 4), 0);
   // keep these loads here, in flight while the activations are reduced
@@ -403,16 +404,16 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_m1(const uint4* __restric
     v4i acc1 = {0, 0, 0, 0}, acc4 = acc1, acc16a = acc1, acc16b = acc1;
     const __amdgpu_buffer_rsrc_t cur_rsrc = tile_rsrc(rt);
     const __amdgpu_buffer_rsrc_t next_rsrc = tile_rsrc(rt + 1);  // empty past the last tile
-    for (int gi = 0; gi < my_groups; gi += kGroupsPerBatch) {
+    for (int gi = 0; gi < my_groups; gi += kB) {
       // next batch: more groups of this tile, else the first groups of the next
-      const bool same = gi + kGroupsPerBatch < my_groups;
-      const int ngi = same ? gi + kGroupsPerBatch : 0;
-      uint4 a_next[kGroupsPerBatch];
+      const bool same = gi + kB < my_groups;
+      const int ngi = same ? gi + kB : 0;
+      uint4 a_next[kB];
 #pragma unroll
-      for (int u = 0; u < kGroupsPerBatch; ++u)
+      for (int u = 0; u < kB; ++u)
         a_next[u] = buffer_load16(same ? cur_rsrc : next_rsrc, w_off(ngi + u));
 #pragma unroll
-      for (int u = 0; u < kGroupsPerBatch; ++u) {
+      for (int u = 0; u < kB; ++u) {
         // groups past this wave's share carry zero codes; any region slot will do
         const int gl = min(gi + u, max_groups - 1);
         const uint4* xt = reinterpret_cast<const uint4*>(region + gl * 256) + 4 * sub;
@@ -425,11 +426,11 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_m1(const uint4* __restric
         acc16b = mfma_16x16x64(mask4(a_cur[u], 0x30303030u, 2), as_v4i(b[3]), acc16b);
       }
 #pragma unroll
-      for (int u = 0; u < kGroupsPerBatch; ++u) a_cur[u] = a_next[u];
+      for (int u = 0; u < kB; ++u) a_cur[u] = a_next[u];
     }
     if (my_groups == 0 && rt + 1 < kRT) {  // keep the stream aligned: nothing was loaded for this tile
 #pragma unroll
-      for (int u = 0; u < kGroupsPerBatch; ++u) a_cur[u] = buffer_load16(next_rsrc, w_off(u));
+      for (int u = 0; u < kB; ++u) a_cur[u] = buffer_load16(next_rsrc, w_off(u));
     }
     // exact: acc4 holds 4x, acc16a/b 16x the code sums; minus this wave's x sum
     v4i part = acc1;
