@@ -63,17 +63,28 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* __restrict__ pac
   const int sub = lane >> 4;
   const int col = lane & 15;
 
-  // Workgroups are dealt to the XCDs round-robin (id % 8).  Give each XCD a
-  // contiguous run of tiles in token-block-major order, so the workgroups an
-  // XCD runs at once share one activation tile in that XCD's L2 while the
-  // weight blocks stream past it.
+  // Workgroups are dealt to the XCDs round-robin (id % 8).  Each XCD gets a
+  // contiguous run of tiles in a grouped order: groups of kGroupN weight
+  // blocks, token blocks outer and weight blocks inner within a group.  The
+  // ~64 workgroups an XCD runs at once then cover about 8 weight blocks x 8
+  // token blocks, whose operands both fit that XCD's 4 MB L2; each XCD reads
+  // its share of the weights once and the activations once per group.
+#ifndef GEMM_GROUP_N
+#define GEMM_GROUP_N 8
+#endif
+  constexpr int64_t kGroupN = GEMM_GROUP_N;
   const int64_t tiles = (int64_t)gridDim.x;
+  const int64_t blocks_m = tiles / blocks_n;
   const int64_t full = tiles / kXcds * kXcds;  // ids past the last full round keep their order
-  const int64_t tile = (int64_t)blockIdx.x >= full
-                           ? (int64_t)blockIdx.x
-                           : (int64_t)(blockIdx.x % kXcds) * (tiles / kXcds) + blockIdx.x / kXcds;
-  const int64_t bn = tile % blocks_n;
-  const int64_t bm = tile / blocks_n;
+  const int64_t t = (int64_t)blockIdx.x >= full
+                        ? (int64_t)blockIdx.x
+                        : (int64_t)(blockIdx.x % kXcds) * (tiles / kXcds) + blockIdx.x / kXcds;
+  const int64_t group = t / (kGroupN * blocks_m);
+  const int64_t first_bn = group * kGroupN;
+  const int64_t group_n = min(kGroupN, blocks_n - first_bn);
+  const int64_t local = t - group * kGroupN * blocks_m;
+  const int64_t bn = first_bn + local % group_n;
+  const int64_t bm = local / group_n;
   const int64_t n0 = bn * kBN;
   const int64_t m0 = bm * kBM;
   const int kt_count = (int)(k / kTileCols);
