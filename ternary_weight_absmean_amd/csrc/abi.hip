@@ -77,7 +77,7 @@ bl_status bl_bitlinear(const uint8_t* packed, const float* gamma, const uint16_t
       !aligned(gamma, 4) || (acc && !aligned(acc, 4)) || (y && !aligned(y, 2)))))
     return BL_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
-  if (n > 0 && m <= 16 && bl::gemv_fused_applies(m, k))
+  if (n > 0 && m <= 16 && bl::gemv_fused_applies(m, n, k))
     return from_hip(bl::launch_gemv_fused(packed, gamma, x, m, n, k, xq, alpha, acc, y, s));
   hipError_t e = bl::launch_quant_act(x, m, k, xq, alpha, s);
   if (e != hipSuccess || n == 0) return from_hip(e);

@@ -286,31 +286,30 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_fused(const uint4* __rest
 
 constexpr int kM1MaxSlots = 14;  // 16-byte bf16 chunks per lane (own groups only: rows up to k = 28672)
 
-// Single-token BitLinear (m = 1).  Wave w of kW multiplies the
-// 256-column groups w, w + kW, ... and quantizes exactly those into its own
-// LDS region, which only it reads.  The row's absmax is either reduced by
-// every wave over the whole row in registers (no barrier before the
-// products), or, with kShare, from per-wave maxima of the own groups
-// exchanged through LDS (one barrier, a quarter of the loads).  The row is
-// loaded in a wave-dependent order so that the wave's own groups come first
-// and fill all 64 lanes: slot i of lane l holds chunk (l % 32) of the wave's
-// group rank 2i + l / 32, own groups ranked first, then the others by index.
-// Each wave subtracts the activation sum of its own columns from its partial
-// products, so the waves' partials add up to sum q*x; one barrier then
-// combines them.  A workgroup handles kRT consecutive 16-row tiles, reusing
-// the quantized row; the weight loads of all its tiles form one stream,
-// prefetched a batch ahead.  kC = slots per lane (ceil(groups / 2), or
-// ceil(own groups / 2) with kShare).
-template <int kRT, int kC, int kW, bool kShare>
-__global__ __launch_bounds__(kW * 64) void k_bitlinear_m1(const uint4* __restrict__ packed,
-                                                           const float* __restrict__ gamma_ptr,
-                                                           const uint4* __restrict__ x, float* __restrict__ alpha,
-                                                           int8_t* __restrict__ xq_out, int n, int k,
-                                                           int32_t* __restrict__ acc_out, uint16_t* __restrict__ y_out) {
+// BitLinear for one token, or a few (m <= kM = 4) with short rows,
+// quantization fused.  Wave w of the four multiplies the 256-column groups
+// w, w + 4, ... and quantizes exactly those, for every token, into its own
+// LDS region, which only it reads.  The tokens' absmaxes come from per-wave
+// maxima of the own groups exchanged through LDS (one barrier).  Slot i of
+// lane l holds chunk (l % 32) of the wave's own group rank 2i + l / 32, so
+// all 64 lanes quantize.  Each wave subtracts the activation sums of its own
+// columns from its partial products, so the waves' partials add up to
+// sum q*x; one barrier then combines them.  A workgroup handles kRT
+// consecutive 16-row tiles, reusing the quantized tokens; the weight loads
+// of all its tiles form one stream, prefetched a batch ahead.  kC = slots
+// per lane (ceil(own groups / 2)).
+template <int kRT, int kC, int kM>
+__global__ __launch_bounds__(kWaves * 64) void k_bitlinear_m1(const uint4* __restrict__ packed,
+                                                               const float* __restrict__ gamma_ptr,
+                                                               const uint4* __restrict__ x, float* __restrict__ alpha,
+                                                               int8_t* __restrict__ xq_out, int m, int n, int k,
+                                                               int32_t* __restrict__ acc_out,
+                                                               uint16_t* __restrict__ y_out) {
+  constexpr int kW = kWaves;
   constexpr int kB = kGroupsPerBatch;  // weight groups per batch (larger batches measured no faster)
-  extern __shared__ uint4 xw_raw[];  // [wave][groups of this wave][256 bytes]
+  extern __shared__ uint4 xw_raw[];    // [wave][own group rank][token][256 bytes]
   __shared__ v4i partial[kRT][kW][64];
-  __shared__ int wave_max[kW];
+  __shared__ int wave_max[kW][kM];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -323,28 +322,24 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_m1(const uint4* __restric
   const int max_groups = (groups + kW - 1) / kW;
   const int sub = lane >> 4;
   const int col = lane & 15;
+  const int tc = min(col, kM - 1);  // token of this lane's MFMA column (columns past the block repeat one)
   const int half = lane >> 5;
   const int r = lane & 31;
 
-  // group of rank u in this wave's order: own groups w + kW u first, then
-  // the rest ascending (the v-th group not congruent to w mod kW)
-  auto group_of_rank = [&](int u) {
-    if (u < my_groups) return wave + kW * u;
-    if (kShare) return groups;  // not loaded
-    const int v = u - my_groups;
-    const int j = v % (kW - 1);
-    return (v / (kW - 1)) * kW + j + (j >= wave ? 1 : 0);
-  };
-  // activations first (loads retire in order), then the first weight batch
-  const __amdgpu_buffer_rsrc_t xrsrc = buffer_rsrc(x, (uint32_t)(k * 2));
-  uint4 xr[kC];
+  // activations first (loads retire in order), then the first weight batch.
+  // Slot i of lane l: chunk l % 32 of own group rank 2i + l / 32 (group
+  // w + kW * rank), for every token; ranks past this wave's share, tokens
+  // past m and columns past k read as zero.
+  const __amdgpu_buffer_rsrc_t xrsrc = buffer_rsrc(x, (uint32_t)(m * k * 2));
+  uint4 xr[kM][kC];
 #pragma unroll
   for (int i = 0; i < kC; ++i) {
-    // wave-uniform group indices of the two ranks, then one select per lane
-    const int g0 = group_of_rank(2 * i), g1 = group_of_rank(2 * i + 1);
-    const uint32_t o0 = g0 < groups ? (uint32_t)(g0 * 512) : kOutOfRange;
-    const uint32_t o1 = g1 < groups ? (uint32_t)(g1 * 512) : kOutOfRange;
-    xr[i] = buffer_load16(xrsrc, (half ? o1 : o0) + (uint32_t)(r * 16));
+    const int rank = 2 * i + half;
+    const int g = wave + kW * rank;
+#pragma unroll
+    for (int t = 0; t < kM; ++t)
+      xr[t][i] = buffer_load16(xrsrc, rank < my_groups && g * 32 + r < k / 8 ? (uint32_t)(t * k * 2 + g * 512 + r * 16)
+                                                                          : kOutOfRange);
   }
   // Weights: one resource per row tile, so that groups past k (and a whole
   // tile past n) read as zero codes instead of the next tile's bytes.
@@ -364,38 +359,63 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_m1(const uint4* __restric
   // keep these loads here, in flight while the activations are reduced
   __builtin_amdgcn_sched_barrier(0);
 
-  // absmax of the whole row, in this wave alone (chunks past k read as zero)
-  u16x2 m2 = {0, 0};
+  // per-token absmax: this wave's columns, then the waves' maxima through LDS
+  float amax[kM], s[kM];
 #pragma unroll
-  for (int i = 0; i < kC; ++i) m2 = absmax_step(m2, xr[i]);
-  int mx = wave_reduce<true>((int)max(m2.x, m2.y));
-  if (kShare) {
-    if (lane == 0) wave_max[wave] = mx;
-    __syncthreads();
+  for (int t = 0; t < kM; ++t) {
+    u16x2 m2 = {0, 0};
 #pragma unroll
-    for (int w = 0; w < kW; ++w) mx = max(mx, wave_max[w]);
+    for (int i = 0; i < kC; ++i) m2 = absmax_step(m2, xr[t][i]);
+    const int mx = wave_reduce<true>((int)max(m2.x, m2.y));
+    if (lane == 0) wave_max[wave][t] = mx;
   }
-  const float amax = __uint_as_float((uint32_t)mx << 16);
-  const float s = 127.0f / fmaxf(amax, 1e-5f);  // IEEE division, as in bl_quant_act
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < kM; ++t) {
+    int mx = wave_max[0][t];
+#pragma unroll
+    for (int w = 1; w < kW; ++w) mx = max(mx, wave_max[w][t]);
+    amax[t] = __uint_as_float((uint32_t)mx << 16);
+    s[t] = 127.0f / fmaxf(amax[t], 1e-5f);  // IEEE division, as in bl_quant_act
+  }
 
-  // quantize this wave's own groups: rank t = 2i + half lands at byte
-  // 256 t + 8 r of the wave's region
-  int8_t* region = reinterpret_cast<int8_t*>(xw_raw) + wave * max_groups * 256;
-  uint2* gdst = (blockIdx.x == 0 && xq_out) ? reinterpret_cast<uint2*>(xq_out) : nullptr;
-  int sum = 0;
+  // quantize this wave's own groups: (rank, token) lands at byte
+  // 256 * (rank * kM + token) + 8 r of the wave's region
+  int8_t* region = reinterpret_cast<int8_t*>(xw_raw) + wave * max_groups * kM * 256;
+  const bool first_block = blockIdx.x == 0;
+  int sum[kM];
+#pragma unroll
+  for (int t = 0; t < kM; ++t) sum[t] = 0;
 #pragma unroll
   for (int i = 0; i < kC; ++i) {
     if (2 * i >= my_groups) break;  // wave-uniform
-    const int t = 2 * i + half;
-    if (t < my_groups) {
-      const uint2 q = act_codes8(xr[i], s, sum);
-      reinterpret_cast<uint2*>(region + t * 256)[r] = q;
-      const int chunk = (wave + kW * t) * 32 + r;
-      if (gdst && chunk < k / 8) gdst[chunk] = q;
+    const int rank = 2 * i + half;
+    if (rank < my_groups) {
+      const int chunk = (wave + kW * rank) * 32 + r;
+#pragma unroll
+      for (int t = 0; t < kM; ++t) {
+        const uint2 q = act_codes8(xr[t][i], s[t], sum[t]);
+        reinterpret_cast<uint2*>(region + (rank * kM + t) * 256)[r] = q;
+        if (first_block && xq_out && t < m && chunk < k / 8) reinterpret_cast<uint2*>(xq_out + (int64_t)t * k)[chunk] = q;
+      }
     }
   }
-  sum = wave_reduce<false>(sum);
-  if (blockIdx.x == 0 && wave == 0 && lane == 0 && alpha) alpha[0] = amax;
+#pragma unroll
+  for (int t = 0; t < kM; ++t) sum[t] = wave_reduce<false>(sum[t]);
+  if (first_block && wave == 0 && lane < m && lane < kM && alpha) {
+    float a = amax[0];
+#pragma unroll
+    for (int t = 1; t < kM; ++t) a = lane == t ? amax[t] : a;
+    alpha[lane] = a;
+  }
+  // this lane's token: its activation sum and absmax (uniform values, selected)
+  int my_sum = sum[0];
+  float my_amax = amax[0];
+#pragma unroll
+  for (int t = 1; t < kM; ++t) {
+    my_sum = tc == t ? sum[t] : my_sum;
+    my_amax = tc == t ? amax[t] : my_amax;
+  }
   // this wave's own LDS writes are complete before its reads below
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
 
@@ -416,7 +436,7 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_m1(const uint4* __restric
       for (int u = 0; u < kB; ++u) {
         // groups past this wave's share carry zero codes; any region slot will do
         const int gl = min(gi + u, max_groups - 1);
-        const uint4* xt = reinterpret_cast<const uint4*>(region + gl * 256) + 4 * sub;
+        const uint4* xt = reinterpret_cast<const uint4*>(region + (gl * kM + tc) * 256) + 4 * sub;
         uint4 b[4];
 #pragma unroll
         for (int f = 0; f < 4; ++f) b[f] = xt[f];
@@ -434,23 +454,23 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_m1(const uint4* __restric
     }
     // exact: acc4 holds 4x, acc16a/b 16x the code sums; minus this wave's x sum
     v4i part = acc1;
-    part.x += (acc4.x >> 2) + (acc16a.x >> 4) + (acc16b.x >> 4) - sum;
-    part.y += (acc4.y >> 2) + (acc16a.y >> 4) + (acc16b.y >> 4) - sum;
-    part.z += (acc4.z >> 2) + (acc16a.z >> 4) + (acc16b.z >> 4) - sum;
-    part.w += (acc4.w >> 2) + (acc16a.w >> 4) + (acc16b.w >> 4) - sum;
+    part.x += (acc4.x >> 2) + (acc16a.x >> 4) + (acc16b.x >> 4) - my_sum;
+    part.y += (acc4.y >> 2) + (acc16a.y >> 4) + (acc16b.y >> 4) - my_sum;
+    part.z += (acc4.z >> 2) + (acc16a.z >> 4) + (acc16b.z >> 4) - my_sum;
+    part.w += (acc4.w >> 2) + (acc16a.w >> 4) + (acc16b.w >> 4) - my_sum;
     partial[rt][wave][lane] = part;
   }
   __syncthreads();
-  // wave w finishes row tiles w, w + kW, ...; column 0 of the MFMA tile is the token
-  if (col != 0) return;
-  const float scale = (gamma * amax) / 127.0f;
+  // wave w finishes row tiles w, w + kW, ...; MFMA column c is token c
+  if (col >= m || col >= kM) return;
+  const float scale = (gamma * my_amax) / 127.0f;
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
     if (rt % kW != wave || rt >= tiles_here) continue;
     v4i acc = partial[rt][0][lane];
 #pragma unroll
     for (int w = 1; w < kW; ++w) add4(acc, partial[rt][w][lane]);
-    store_tile(acc, (int64_t)(tile0 + rt) * kTileRows + 4 * sub, 0, n, scale, acc_out, y_out);
+    store_tile(acc, (int64_t)(tile0 + rt) * kTileRows + 4 * sub, col, n, scale, acc_out, y_out);
   }
 }
 
@@ -755,15 +775,6 @@ FusedPlan fused_plan(int64_t m, int64_t n, int64_t k) {
 #define FUSED_MAX_TOKEN_COLUMNS 32767
 #endif
 
-// Every workgroup of k_bitlinear_fused quantizes its whole token block, so
-// it pays off while m * k is small (up to 8 tokens of 2560, 4 of 6912);
-// larger blocks go through the quantizer and k_gemv_direct.  One token takes
-// the single-token kernel whenever it applies.
-bool gemv_fused_applies(int64_t m, int64_t k) {
-  if (m < 1 || m > 16) return false;
-  if (m > 1 && m * k > FUSED_MAX_TOKEN_COLUMNS) return false;
-  return fused_plan(m, 1, k).rt > 0;
-}
 
 hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
                        int64_t n, int64_t k, int32_t* acc, uint16_t* y, hipStream_t s) {
@@ -804,61 +815,66 @@ hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* 
 
 namespace {
 
-typedef void (*M1Kernel)(const uint4*, const float*, const uint4*, float*, int8_t*, int, int, int32_t*, uint16_t*);
+typedef void (*M1Kernel)(const uint4*, const float*, const uint4*, float*, int8_t*, int, int, int, int32_t*,
+                         uint16_t*);
 struct M1Config {
-  int rt = 0, waves = 0;
-  M1Kernel kernel = nullptr;  // none when the row needs more than kM1MaxSlots slots per lane
+  int rt = 0;
+  M1Kernel kernel = nullptr;  // none when the rows need more slots per lane than the token count allows
 };
 
-template <int kRT, int kW, bool kShare>
-M1Kernel m1_pick(int64_t groups) {
-  const int64_t own = (groups + kW - 1) / kW;
-  const int64_t slots = kShare ? (own + 1) / 2 : (groups + 1) / 2;
-  if (slots <= 2) return k_bitlinear_m1<kRT, 2, kW, kShare>;
-  if (slots <= 5) return k_bitlinear_m1<kRT, 5, kW, kShare>;
-  if (slots <= kM1MaxSlots) return k_bitlinear_m1<kRT, kM1MaxSlots, kW, kShare>;
+template <int kRT>
+M1Kernel m1_pick(int64_t m, int64_t groups) {
+  const int64_t slots = ((groups + kWaves - 1) / kWaves + 1) / 2;
+  if (m == 1) {
+    if (slots <= 2) return k_bitlinear_m1<kRT, 2, 1>;
+    if (slots <= 5) return k_bitlinear_m1<kRT, 5, 1>;
+    if (slots <= kM1MaxSlots) return k_bitlinear_m1<kRT, kM1MaxSlots, 1>;
+  } else if (m <= 4 && slots <= 2) {
+    return k_bitlinear_m1<kRT, 2, 4>;
+  }
   return nullptr;
 }
 
-#ifndef M1_WAVES
-#define M1_WAVES 4
-#endif
-#ifndef M1_SHARE
-#define M1_SHARE true
-#endif
-
-M1Config m1_config(int64_t groups, int64_t row_tiles) {
+M1Config m1_config(int64_t m, int64_t groups, int64_t row_tiles) {
+  // Several tokens: every workgroup quantizes all of them, which pays off
+  // only for short rows and few row tiles (measured: rows of 2560 with 160
+  // or 240 row tiles; not 6912-column rows or 864+ row tiles).
+  if (m > 1 && (m > 4 || row_tiles >= 512)) return M1Config{};
   // two row tiles per workgroup for short rows once there are more than ~2
-  // tiles per CU (the quantized row is reused); long rows keep one tile per
-  // workgroup, whose weight stream is already long enough to hide latency
-#ifdef M1_RT
-  const int rt = M1_RT;
-#else
+  // tiles per CU (the quantized tokens are reused); long rows keep one tile
+  // per workgroup, whose weight stream is already long enough
   const int rt = row_tiles >= 512 && groups <= 16 ? 2 : 1;
-#endif
-  M1Config c{rt, M1_WAVES, nullptr};
-#ifdef M1_RT
-  if (rt == 4) c.kernel = m1_pick<4, M1_WAVES, M1_SHARE>(groups);
-  else
-#endif
-  if (rt == 2) c.kernel = m1_pick<2, M1_WAVES, M1_SHARE>(groups);
-  else c.kernel = m1_pick<1, M1_WAVES, M1_SHARE>(groups);
+  M1Config c;
+  c.rt = rt;
+  c.kernel = rt == 2 ? m1_pick<2>(m, groups) : m1_pick<1>(m, groups);
   return c;
 }
 
 }  // namespace
 
+// Every workgroup of k_bitlinear_fused quantizes its whole token block, so
+// it pays off while m * k is small (up to 8 tokens of 2560, 4 of 6912);
+// larger blocks go through the quantizer and k_gemv_lds.  k_bitlinear_m1
+// takes one token, and up to 4 on small matrices, whenever it applies.
+bool gemv_fused_applies(int64_t m, int64_t n, int64_t k) {
+  if (m < 1 || m > 16) return false;
+  if (m1_config(m, (k / kTileCols + 3) / 4, (n + kTileRows - 1) / kTileRows).kernel) return true;
+  if (m > 1 && m * k > FUSED_MAX_TOKEN_COLUMNS) return false;
+  return fused_plan(m, 1, k).rt > 0;
+}
+
 hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t n,
                              int64_t k, int8_t* xq, float* alpha, int32_t* acc, uint16_t* y, hipStream_t s) {
-  if (m > 16 || !gemv_fused_applies(m, k)) return hipErrorInvalidValue;
-  const M1Config c = m == 1 ? m1_config((k / kTileCols + 3) / 4, (n + kTileRows - 1) / kTileRows) : M1Config{};
+  if (m > 16 || !gemv_fused_applies(m, n, k)) return hipErrorInvalidValue;
+  const M1Config c = m1_config(m, (k / kTileCols + 3) / 4, (n + kTileRows - 1) / kTileRows);
   if (c.kernel) {
     const int64_t groups = (k / kTileCols + 3) / 4;
     const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
-    const size_t lds = (size_t)c.waves * (size_t)((groups + c.waves - 1) / c.waves) * 256;
+    const int64_t tokens = m == 1 ? 1 : 4;
+    const size_t lds = (size_t)kWaves * (size_t)((groups + kWaves - 1) / kWaves) * (size_t)tokens * 256;
     const dim3 grid((unsigned)((row_tiles + c.rt - 1) / c.rt));
-    hipLaunchKernelGGL(c.kernel, grid, dim3(64 * c.waves), lds, s, reinterpret_cast<const uint4*>(packed), gamma,
-                       reinterpret_cast<const uint4*>(x), alpha, xq, (int)n, (int)k, acc, y);
+    hipLaunchKernelGGL(c.kernel, grid, dim3(64 * kWaves), lds, s, reinterpret_cast<const uint4*>(packed), gamma,
+                       reinterpret_cast<const uint4*>(x), alpha, xq, (int)m, (int)n, (int)k, acc, y);
     return hipGetLastError();
   }
   const FusedPlan f = fused_plan(m, n, k);

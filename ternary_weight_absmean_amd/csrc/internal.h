@@ -34,7 +34,7 @@ hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* 
 // Fused per-token quantization + product for a small token block
 // (gemv_fused_applies: one token, or m * k small); writes xq/alpha (if non-NULL)
 // exactly as launch_quant_act would.
-bool gemv_fused_applies(int64_t m, int64_t k);
+bool gemv_fused_applies(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t n,
                              int64_t k, int8_t* xq, float* alpha, int32_t* acc, uint16_t* y, hipStream_t s);
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,

@@ -332,6 +332,10 @@ def test_linear_is_deterministic():
                                    (8, 16400, 2560), (16, 32800, 320), (5, 2000, 6912),
                                    # block-quantizing kernel with eight waves, one and two row tiles
                                    (4, 600, 6912), (3, 9000, 8000),
+                                   # few-token kernel (4 token slots), partial last column group; and
+                                   # shapes just past its limits
+                                   (2, 70, 2624), (4, 1000, 4096), (4, 8000, 2560), (4, 8200, 2560),
+                                   (7, 530, 2112), (6, 16400, 320), (4, 33, 10240),
                                    # eight-wave kernel for long rows (k >= 16384)
                                    (1, 530, 16384), (7, 70, 16448), (16, 40, 32768),
                                    (3, 48, 2560), (4, 3840, 2560), (5, 40, 6912), (16, 64, 1024), (16, 31, 2560),
