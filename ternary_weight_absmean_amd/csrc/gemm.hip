@@ -69,10 +69,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* __restrict__ pac
   // ~64 workgroups an XCD runs at once then cover about 8 weight blocks x 8
   // token blocks, whose operands both fit that XCD's 4 MB L2; each XCD reads
   // its share of the weights once and the activations once per group.
-#ifndef GEMM_GROUP_N
-#define GEMM_GROUP_N 8
-#endif
-  constexpr int64_t kGroupN = GEMM_GROUP_N;
+  constexpr int64_t kGroupN = 8;
   const int64_t tiles = (int64_t)gridDim.x;
   const int64_t blocks_m = tiles / blocks_n;
   const int64_t full = tiles / kXcds * kXcds;  // ids past the last full round keep their order

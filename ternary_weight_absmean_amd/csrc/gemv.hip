@@ -752,17 +752,8 @@ FusedPlan fused_plan(int64_t m, int64_t n, int64_t k) {
   // tiles; two row tiles per workgroup once there are ~2 per CU.  A single
   // token (rows too long for the single-token kernel): eight waves for long
   // rows, two row tiles once there are ~4 per CU.
-#ifdef FUSED_W
-  int w = FUSED_W;
-#else
   int w = m == 1 ? (k >= 16384 ? 8 : 4) : (row_tiles >= 512 && k <= 4096 ? 4 : 8);
-#endif
-#ifdef FUSED_RT
-  int rt = FUSED_RT;
-#else
   int rt = m == 1 ? (row_tiles >= 1024 ? 2 : 1) : (row_tiles >= 512 ? 2 : 1);
-#endif
-  if (w == 8 && rt > 2) rt = 2;
   const size_t dyn = gemv_lds_bytes(m, k);
   while (rt > 1 && dyn + fused_static_lds(rt, w) > (size_t)kLdsBudget) rt /= 2;
   if (dyn + fused_static_lds(rt, w) > (size_t)kLdsBudget) return FusedPlan{};
@@ -771,9 +762,7 @@ FusedPlan fused_plan(int64_t m, int64_t n, int64_t k) {
 
 }  // namespace
 
-#ifndef FUSED_MAX_TOKEN_COLUMNS
-#define FUSED_MAX_TOKEN_COLUMNS 32767
-#endif
+constexpr int64_t kFusedMaxTokenColumns = 32767;  // m * k beyond which a block's quantization costs too much
 
 
 hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
@@ -859,7 +848,7 @@ M1Config m1_config(int64_t m, int64_t groups, int64_t row_tiles) {
 bool gemv_fused_applies(int64_t m, int64_t n, int64_t k) {
   if (m < 1 || m > 16) return false;
   if (m1_config(m, (k / kTileCols + 3) / 4, (n + kTileRows - 1) / kTileRows).kernel) return true;
-  if (m > 1 && m * k > FUSED_MAX_TOKEN_COLUMNS) return false;
+  if (m > 1 && m * k > kFusedMaxTokenColumns) return false;
   return fused_plan(m, 1, k).rt > 0;
 }
 
@@ -888,8 +877,6 @@ hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const ui
       hipLaunchKernelGGL((k_bitlinear_fused<2, 8>), grid, dim3(512), lds, s, p, gamma, xv, alpha, xq, m, n, k, acc, y);
     else
       hipLaunchKernelGGL((k_bitlinear_fused<1, 8>), grid, dim3(512), lds, s, p, gamma, xv, alpha, xq, m, n, k, acc, y);
-  } else if (f.rt == 4) {
-    hipLaunchKernelGGL((k_bitlinear_fused<4, 4>), grid, dim3(256), lds, s, p, gamma, xv, alpha, xq, m, n, k, acc, y);
   } else if (f.rt == 2) {
     hipLaunchKernelGGL((k_bitlinear_fused<2, 4>), grid, dim3(256), lds, s, p, gamma, xv, alpha, xq, m, n, k, acc, y);
   } else if (f.rt == 1) {
