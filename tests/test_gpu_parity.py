@@ -378,3 +378,48 @@ def test_bitlinear_2b_stack_layer_decode():
         want_y, want_acc, _, _ = oracle.bitlinear_forward(want_packed, want_gamma, x, n)
         np.testing.assert_array_equal(host(acc), want_acc)
         assert_bf16_within_one_ulp(host(y), want_y)
+
+
+def check_bitlinear_sampled(w, x, rows=None):
+    """bl_bitlinear (the benchmark's call) against the oracle's quantizer and
+    product on the given output rows (all when None), every token."""
+    n, k = w.shape
+    packed, gamma = bl.bl_ternarize_pack(f32(w))
+    acc, y, xq, alpha = bl.bl_bitlinear(packed, gamma, bf16(x), n)
+    want_gamma = oracle.absmean(w)
+    assert host(gamma).view(np.uint32)[0] == np.float32(want_gamma).view(np.uint32)
+    qw = oracle.ternarize(w, want_gamma)
+    want_xq, want_alpha = oracle.quant_act(x)
+    np.testing.assert_array_equal(host(xq), want_xq)
+    np.testing.assert_array_equal(host(alpha).view(np.uint32), want_alpha.view(np.uint32))
+    rows = np.arange(n) if rows is None else rows
+    want_acc = oracle.linear_mul(qw[rows], want_xq)
+    np.testing.assert_array_equal(host(acc)[:, rows], want_acc)
+    assert_bf16_within_one_ulp(host(y)[:, rows], oracle.rescale(want_acc, want_gamma, want_alpha))
+
+
+@pytest.mark.parametrize("m", [4, 16, 64])
+def test_bitlinear_2b_stack_batched_decode(m):
+    """The benchmark's batched-decode call on the 2B layer-0 shapes: seeded
+    weights, independent N(0, 1) token rows."""
+    wl = datagen.WORKLOAD_STACK_2B
+    for pi, (name, k, n) in enumerate(datagen.STACK_2B_PROJ):
+        w = datagen.weights(datagen.stream_id(wl, 0, pi, datagen.TENSOR_W), n, k)
+        x = datagen.activations_bf16(datagen.stream_id(wl, 0, pi, datagen.TENSOR_X) + 7 * m, m, k, [], 1.0)
+        say(f"bl_bitlinear 2B layer 0 {name} m={m}")
+        check_bitlinear_sampled(w, x)
+
+
+@pytest.mark.parametrize("proj", [0, 1])
+@pytest.mark.parametrize("m", [1, 16])
+def test_bitlinear_70b_decode(proj, m):
+    """The benchmark's 70B-shaped decode call (full shapes, sampled rows)."""
+    wl = datagen.WORKLOAD_70B
+    name, k, n = datagen.LAYER_70B_PROJ[proj]
+    w = datagen.weights(datagen.stream_id(wl, 0, proj, datagen.TENSOR_W), n, k)
+    cols = datagen.outlier_columns(wl, k, datagen.n_outliers_70b(k))
+    x = datagen.activations_bf16(datagen.stream_id(wl, 0, proj, datagen.TENSOR_X) + m, m, k, cols,
+                                 datagen.LAYER_70B_OUTLIER_MULT)
+    rows = np.sort(np.random.default_rng(proj + m).choice(n, size=1024, replace=False))
+    say(f"bl_bitlinear 70B {name} m={m}")
+    check_bitlinear_sampled(w, x, rows)
