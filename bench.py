@@ -60,6 +60,7 @@ def parse_args():
     p.add_argument("--calib", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
                    help="FETCH_SIZE and WRITE_SIZE runs of --calibrate-copy")
     p.add_argument("--command", action="append", default=[], help="command that produced an input (repeatable)")
+    p.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"), help="where --summarize writes")
     return p.parse_args()
 
 
@@ -379,9 +380,9 @@ def summarize(args):
             lines.append(f"| {k} | {100 * util:.1f}% | {n_inst:.0f} | {ops:.4g} | "
                          f"{ops / (insts.get(k, (0, dur, 0))[1] * 1e-9) / 1e12 if n_inst else 0:.1f} |")
         lines.append("")
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    os.makedirs(args.out_dir, exist_ok=True)
     if traffic and args.workload:
-        path = os.path.join(ROOT, "profiles", "traffic.json")
+        path = os.path.join(args.out_dir, "traffic.json")
         try:
             with open(path) as f:
                 stored = json.load(f)
@@ -392,7 +393,7 @@ def summarize(args):
         with open(path, "w") as f:
             json.dump(stored, f, indent=1, sort_keys=True)
             f.write("\n")
-    with open(os.path.join(ROOT, "profiles", f"{name}.md"), "w") as f:
+    with open(os.path.join(args.out_dir, f"{name}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
     return 0
