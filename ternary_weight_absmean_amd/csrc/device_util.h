@@ -8,12 +8,20 @@ namespace bl {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-// fp32 -> bf16 bit pattern, round to nearest even (finite inputs; overflow
-// rounds to infinity as IEEE requires).
+// fp32 -> bf16 bit pattern, round to nearest even, by the conversion
+// instruction (v_cvt_pk_bf16_f32; checked equal to the integer rounding
+// (b + 0x7FFF + ((b >> 16) & 1)) >> 16 on 2^24 finite values including
+// exact ties).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t b = __float_as_uint(f);
-  b += 0x7FFFu + ((b >> 16) & 1u);
-  return (uint16_t)(b >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// two fp32 -> two bf16 in one dword (lo in bits 0..15)
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 // Signed trits of one 2-bit field of four packed bytes.  The field's codes

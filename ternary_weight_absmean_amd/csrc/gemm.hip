@@ -218,8 +218,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* __restrict__ pac
       if (vec_ok && row0 + 3 < n) {
         if (acc_out) *reinterpret_cast<int4*>(acc_out + tok * n + row0) = make_int4(vals[0], vals[1], vals[2], vals[3]);
         if (y_out) {
-          const uint32_t lo = f32_to_bf16_rne((float)vals[0] * scale) | ((uint32_t)f32_to_bf16_rne((float)vals[1] * scale) << 16);
-          const uint32_t hi = f32_to_bf16_rne((float)vals[2] * scale) | ((uint32_t)f32_to_bf16_rne((float)vals[3] * scale) << 16);
+          const uint32_t lo = f32x2_to_bf16x2((float)vals[0] * scale, (float)vals[1] * scale);
+          const uint32_t hi = f32x2_to_bf16x2((float)vals[2] * scale, (float)vals[3] * scale);
           *reinterpret_cast<uint2*>(y_out + tok * n + row0) = make_uint2(lo, hi);
         }
       } else {

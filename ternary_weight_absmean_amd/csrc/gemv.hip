@@ -73,10 +73,8 @@ __device__ __forceinline__ void store_tile(const v4i& acc, int64_t row0, int64_t
   if (row0 + 3 < n && (!yp || ((uintptr_t)yp & 7) == 0) && (!ap || ((uintptr_t)ap & 15) == 0)) {
     if (ap) *reinterpret_cast<int4*>(ap) = make_int4(vals[0], vals[1], vals[2], vals[3]);
     if (yp)
-      *reinterpret_cast<uint2*>(yp) = make_uint2((uint32_t)f32_to_bf16_rne((float)vals[0] * scale) |
-                                                     ((uint32_t)f32_to_bf16_rne((float)vals[1] * scale) << 16),
-                                                 (uint32_t)f32_to_bf16_rne((float)vals[2] * scale) |
-                                                     ((uint32_t)f32_to_bf16_rne((float)vals[3] * scale) << 16));
+      *reinterpret_cast<uint2*>(yp) = make_uint2(f32x2_to_bf16x2((float)vals[0] * scale, (float)vals[1] * scale),
+                                                 f32x2_to_bf16x2((float)vals[2] * scale, (float)vals[3] * scale));
     return;
   }
 #pragma unroll
