@@ -209,6 +209,7 @@ def main() -> int:
     extras = None
     if not args.no_extras:
         extras = measure_extras(args, linears, lib)
+    stream = stream_reference(torch)
 
     # ------------------------------------------------------------ CPU oracle baseline
     cpu = None
@@ -240,7 +241,9 @@ def main() -> int:
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gemv_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": stored_traffic(STACK_WORKLOAD, STACK_KERNEL, avg_bytes),
                      "avg_launch_us": round(avg_us, 3),
-                     "algorithmic_bytes_per_launch": round(avg_bytes, 1)},
+                     "algorithmic_bytes_per_launch": round(avg_bytes, 1),
+                     "measured_hbm_reference": stream,
+                     "frac_of_measured_read": round(gemv_gbps / stream["read_GBps"], 4)},
         "packer": {"weights": len(linears), "fp32_GB": round(w_bytes / 1e9, 3), "ms": round(pack_ms, 3),
                    "GBps_fp32_read": round(w_bytes / (pack_ms * 1e-3) / 1e9, 1)},
         "cpu_baseline": cpu,
@@ -581,8 +584,12 @@ def measure_extras(args, linears, lib):
             x = act(datagen.stream_id(wl, i // 4, i % 4, datagen.TENSOR_X) + 7 * m, m, lin["k"], wl, 0, 1.0)
             items.append((lin["packed"], lin["gamma"], x, lin["n"], lin["k"], *bufs(m, lin["n"], lin["k"])))
         ms = _graph_time_ms(torch, layer_fn(items, m), max(5, args.steps // 10))
+        ops = 2.0 * m * sum(lin["n"] * lin["k"] for lin in linears)
         batched[f"M={m}"] = {"ms_per_step": round(ms, 4), "tokens_per_s": round(m * 1000.0 / ms, 1),
-                             "weight_GBps": round(weight_bytes / (ms * 1e-3) / 1e9, 1)}
+                             "weight_GBps": round(weight_bytes / (ms * 1e-3) / 1e9, 1),
+                             "frac_of_hbm_peak": round(weight_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                             "TOPS": round(ops / (ms * 1e-3) / 1e12, 1),
+                             "frac_of_int8_mfma_peak": round(ops / (ms * 1e-3) / 1e12 / MFMA_I8_PEAK_TOPS, 4)}
         del items
     out["batched_decode_2b_stack"] = batched
 
@@ -622,11 +629,23 @@ def measure_extras(args, linears, lib):
     return out
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(args, outliers):
     """The CPU oracle (plain C, OpenMP over output rows) on a bounded sample:
     the first layer's four linears of the same stack, one token each,
-    repeated until about --cpu-seconds of CPU time; scaled to tokens/s of the
-    full stack.  The oracle packs its own weights (untimed, offline)."""
+    repeated for about --cpu-seconds at all threads and half that at one
+    thread; scaled to tokens/s of the full stack.  The oracle packs its own
+    weights (untimed, offline)."""
     import datagen
     import oracle
 
@@ -639,21 +658,55 @@ def cpu_baseline(args, outliers):
         x = datagen.activations_bf16(datagen.stream_id(wl, 0, pi, datagen.TENSOR_X), 1, k, outliers[k],
                                      datagen.STACK_2B_OUTLIER_MULT)
         prepared.append((packed, gamma, x, n))
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
-    done = 0
-    t0 = time.perf_counter()
-    while True:
-        for packed, gamma, x, n in prepared:
-            oracle.bitlinear_forward(packed, gamma, x, n)
-        done += 1
-        elapsed = time.perf_counter() - t0
-        if elapsed >= args.cpu_seconds:
-            break
-    layers_per_s = done / elapsed
-    return {"value": round(layers_per_s / args.layers, 4), "unit": "tokens/s", "cores": threads,
+
+    def layers_per_s(seconds):
+        done = 0
+        t0 = time.perf_counter()
+        while True:
+            for packed, gamma, x, n in prepared:
+                oracle.bitlinear_forward(packed, gamma, x, n)
+            done += 1
+            elapsed = time.perf_counter() - t0
+            if elapsed >= seconds:
+                return done, elapsed
+
+    all_threads = oracle.set_threads(int(os.environ.get("OMP_NUM_THREADS", "0") or 0))
+    done, elapsed = layers_per_s(args.cpu_seconds)
+    oracle.set_threads(1)
+    done1, elapsed1 = layers_per_s(args.cpu_seconds / 2)
+    oracle.set_threads(all_threads)
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
+    return {"value": round(done / elapsed / args.layers, 4), "unit": "tokens/s", "cores": all_threads,
             "kind": "oracle",
-            "sample": f"layer 0 of the 2B-shaped stack (4 linears, M=1) run {done}x in {elapsed:.1f} s; "
-                      f"tokens/s = layers/s / {args.layers}"}
+            "sample": f"layer 0 of the 2B-shaped stack (4 linears, M=1) run {done}x in {elapsed:.1f} s at "
+                      f"{all_threads} threads; tokens/s = layers/s / {args.layers}",
+            "value_1_thread": round(done1 / elapsed1 / args.layers, 4),
+            "cpu_model": _cpu_model(), "nproc": os.cpu_count(), "affinity_cpus": affinity}
+
+
+def stream_reference(torch):
+    """Measured HBM ceilings on this machine for context: a 1 GiB device copy
+    (read + write) and a sum over 1 GiB (read), each timed over 3 runs."""
+    dev = torch.device("cuda", 0)
+    src = torch.ones(1 << 27, dtype=torch.int64, device=dev)  # 1 GiB
+    dst = torch.empty_like(src)
+    out = {}
+    for name, fn, nbytes in (("copy_GBps", lambda: dst.copy_(src), 2 << 30), ("read_GBps", lambda: src.sum(), 1 << 30)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = round(nbytes * 3 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
 
 
 if __name__ == "__main__":

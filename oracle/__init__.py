@@ -85,6 +85,8 @@ def _load():
         lib.orc_rescale.restype = None
         lib.orc_bitlinear_forward.argtypes = [p, ctypes.c_float, p, i64, i64, i64, p, p, p, p]
         lib.orc_bitlinear_forward.restype = ctypes.c_int
+        lib.orc_set_threads.argtypes = [ctypes.c_int]
+        lib.orc_set_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -207,3 +209,9 @@ def bitlinear_forward(packed: np.ndarray, gamma, x_bf16: np.ndarray, n: int):
     if rc != 0:
         raise ValueError("k must be a multiple of 64")
     return y, acc, xq, alpha
+
+
+def set_threads(n: int = 0) -> int:
+    """Set the OpenMP thread count of the oracle's loops (0: leave it);
+    returns the count now in effect."""
+    return int(_load().orc_set_threads(int(n)))

@@ -40,6 +40,7 @@
  *    Rows are padded to a multiple of 16 with code 1.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -384,4 +385,11 @@ int orc_bitlinear_forward(const uint8_t* packed, float gamma, const uint16_t* x,
     }
     orc_rescale(acc, m, n, gamma, alpha, y);
     return 0;
+}
+
+/* Thread count of the OpenMP loops above (results never depend on it; the
+ * benchmark's CPU-baseline leg times the oracle at one thread and at all). */
+int orc_set_threads(int n) {
+  if (n > 0) omp_set_num_threads(n);
+  return omp_get_max_threads();
 }
