@@ -29,27 +29,59 @@ FLAGS = [
 ]
 
 
+RESOURCE_REMARKS = "-Rpass-analysis=kernel-resource-usage"
+
+
+def kernel_resources(compiler_output: str) -> dict:
+    """Per-kernel resource usage from the compiler's resource remarks:
+    {mangled name: {"VGPRs": .., "AGPRs": .., "ScratchSize [bytes/lane]": .., ...}}."""
+    kernels, current = {}, None
+    for ln in compiler_output.splitlines():
+        if "remark:" not in ln:
+            continue
+        body = ln.split("remark:", 1)[1].split("[-Rpass-analysis", 1)[0].strip()
+        if body.startswith("Function Name:"):
+            current = body.split(":", 1)[1].strip()
+            kernels[current] = {}
+        elif current and ":" in body:
+            key, val = body.rsplit(":", 1)
+            kernels[current][key.strip()] = val.strip()
+    return kernels
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source in parallel and link the shared library."""
+    """Compile every HIP source in parallel and link the shared library.
+    Every kernel must run from registers: a kernel with scratch memory (a
+    spill, or a register array indexed at run time) fails the build."""
     with tempfile.TemporaryDirectory(prefix="bitlinear_build_") as tmp:
         procs, objs = [], []
         for src in SOURCES:
             obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
-            cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [HIPCC, *FLAGS, RESOURCE_REMARKS, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd))
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
             objs.append(obj)
-        failed = []
+        failed, scratch = [], []
         for src, p in procs:
             out, _ = p.communicate()
-            lines = [ln for ln in out.splitlines() if "packed-fp32-ops" not in ln]
+            lines = [ln for ln in out.splitlines() if "packed-fp32-ops" not in ln and "remark:" not in ln
+                     and "kernel-resource-usage" not in ln]
             if lines and (verbose or p.returncode):
                 print("\n".join(lines))
             if p.returncode:
                 failed.append(src)
+                continue
+            for name, res in kernel_resources(out).items():
+                if verbose:
+                    print(f"{src}: {name}: VGPRs {res.get('VGPRs')} AGPRs {res.get('AGPRs')} "
+                          f"scratch {res.get('ScratchSize [bytes/lane]')} LDS {res.get('LDS Size [bytes/block]')}")
+                if res.get("ScratchSize [bytes/lane]", "0") != "0":
+                    scratch.append(f"{src}: {name} ({res['ScratchSize [bytes/lane]']} bytes/lane)")
         if failed:
             raise RuntimeError(f"hipcc failed for {failed}")
+        if scratch:
+            raise RuntimeError("kernels using scratch memory: " + "; ".join(scratch))
         tmp_lib = LIB_PATH + ".tmp"
         subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib], check=True)
         os.replace(tmp_lib, LIB_PATH)
