@@ -45,7 +45,14 @@ constexpr int kStepK = 256;             // columns per step
 constexpr int kXRow = kStepK / 16;     // 16-byte chunks per token row in LDS
 constexpr int kXcds = 8;                // accelerator complex dies, each with its own L2
 
-template <int kTB, int kRB>  // 16-token (4 or 8) and 16-row (2 or 4) MFMA blocks per wave
+// kTB, kRB: 16-token (4 or 8) and 16-row (2 or 4) MFMA blocks per wave.
+// kFixedBuffers: the step loop is unrolled by two so that every LDS read and
+// every DMA names one of the two activation buffers at compile time; the
+// compiler then knows that the DMA into one buffer cannot touch the reads of
+// the other and does not wait for the DMA before reading.  Without it (fewer
+// registers: more workgroups per CU) each step's reads wait for the DMA just
+// issued.
+template <int kTB, int kRB, bool kFixedBuffers>
 __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* __restrict__ packed, const float* __restrict__ gamma_ptr,
                                                  const int8_t* __restrict__ xq, const float* __restrict__ alpha,
                                                  int64_t m, int64_t n, int64_t k, int64_t blocks_n,
@@ -54,7 +61,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* __restrict__ pac
   constexpr int kWN = 16 * kRB;                       // weight rows per wave
   constexpr int kBN = kWaves * kWN;                   // weight rows per workgroup
   constexpr int kXDma = kBM * kStepK / 1024 / kWaves; // 1 KiB LDS-DMA loads per wave per step
-  __shared__ uint4 xs[2][kBM * kXRow];
+  __shared__ uint4 xs0[kBM * kXRow];  // activation tile buffers: two distinct LDS objects
+  __shared__ uint4 xs1[kBM * kXRow];
   __shared__ int row_sum[kBM];
 
   const int tid = threadIdx.x;
@@ -104,7 +112,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* __restrict__ pac
   // 4*load + i/16, stored chunk i%16.  Stored chunk p of row r holds source
   // chunk p ^ (r % 16), so the lane fetches that one.
   const int dma_row0 = wave * kXDma * 4 + (lane >> 4);
-  auto load_x = [&](int s, int buf) {
+  auto load_x = [&](int s, uint4* dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < kXDma; ++j) {
       const int row = dma_row0 + 4 * j;
@@ -112,14 +120,14 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* __restrict__ pac
       const uint32_t col_byte = (uint32_t)(s * kStepK + 16 * c);
       const uint32_t off = (s < full_steps || col_byte < kk) ? (uint32_t)row * kk + col_byte : kOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xrsrc, (__attribute__((address_space(3))) void*)(xs[buf] + (wave * kXDma + j) * 64), 16, off, 0, 0, 0);
+          xrsrc, (__attribute__((address_space(3))) void*)(dst + (wave * kXDma + j) * 64), 16, off, 0, 0, 0);
     }
   };
   // weights: row block rb of this wave, step s; lane = (tile sub, row col).
   // Past-the-end tiles of a partial step are clamped to the last tile: they
   // meet zero activations.
   const uint32_t w_off0 = (uint32_t)(wave * kRB * kt_count) * kTileBytes + (uint32_t)col * 16u;
-  auto load_w = [&](int s, uint4* r) {
+  auto load_w = [&](int s, uint4* r) __attribute__((always_inline)) {
     const uint32_t kt = (uint32_t)min(4 * s + sub, kt_count - 1);
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb)
@@ -142,13 +150,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* __restrict__ pac
 
   uint4 w_cur[kRB], w_next[kRB];
   load_w(0, w_cur);
-  load_x(0, 0);
+  load_x(0, xs0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  auto compute = [&](int buf) {
+  auto compute = [&](const uint4* xbuf) __attribute__((always_inline)) {
     // token row tb*16 + col, chunk 4*sub + f, stored at chunk (4*sub + f) ^ col
-    const uint4* xt = xs[buf] + col * kXRow;
+    const uint4* xt = xbuf + col * kXRow;
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       v4i b[kTB];
@@ -176,17 +184,32 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* __restrict__ pac
     }
   };
 
-  for (int s = 0; s + 1 < steps; ++s) {
-    const int buf = s & 1;
+  // one step: prefetch step s + 1 into wr, multiply the tile in rd
+  auto step = [&](int s, const uint4* rd, uint4* wr) __attribute__((always_inline)) {
     load_w(s + 1, w_next);
-    load_x(s + 1, buf ^ 1);
-    compute(buf);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA into buf ^ 1 has landed
-    __syncthreads();                // ... and every other wave's, and nobody reads buf any more
+    load_x(s + 1, wr);
+    compute(rd);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA into wr has landed
+    __syncthreads();                // ... and every other wave's, and nobody reads rd any more
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) w_cur[rb] = w_next[rb];
+  };
+  if constexpr (kFixedBuffers) {
+    int s = 0;
+    for (; s + 2 < steps; s += 2) {
+      step(s, xs0, xs1);
+      step(s + 1, xs1, xs0);
+    }
+    if (s + 1 < steps) {
+      step(s, xs0, xs1);
+      compute(xs1);
+    } else {
+      compute(xs0);
+    }
+  } else {
+    for (int s = 0; s + 1 < steps; ++s) step(s, (s & 1) ? xs1 : xs0, (s & 1) ? xs0 : xs1);
+    compute(((steps - 1) & 1) ? xs1 : xs0);
   }
-  compute((steps - 1) & 1);
 
   // per-token activation sums: add the four column-tile lanes of each token,
   // then the four waves' fields
@@ -242,24 +265,27 @@ hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* 
                        int64_t n, int64_t k, int32_t* acc, uint16_t* y, hipStream_t s) {
   // Largest tile that still gives the chip enough workgroups: 256 rows x 128
   // tokens with >= 4 per CU, else 256 x 64 with >= 2 per CU, else 128 x 64.
+  // Fixed buffers (unrolled steps, more registers) where they measured
+  // faster: always for 128 x 64 tiles (same occupancy either way), for
+  // 256 x 64 tiles only with long rows (the extra registers cost a
+  // workgroup per CU, which the short-row shapes need more); the 256 x 128
+  // tile does not fit its registers unrolled.
   auto count = [&](int64_t rows, int64_t toks) { return ((n + rows - 1) / rows) * ((m + toks - 1) / toks); };
   const uint8_t* p = packed;
-  if (count(256, 128) >= 1024) {
-    const int64_t blocks_n = (n + 255) / 256, blocks = count(256, 128);
+  auto launch = [&](auto kern, int64_t rows, int64_t toks) {
+    const int64_t blocks_n = (n + rows - 1) / rows, blocks = count(rows, toks);
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_gemm<8, 4>), dim3((unsigned)blocks), dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, blocks_n,
-                       acc, y);
-  } else if (count(256, 64) >= 512) {
-    const int64_t blocks_n = (n + 255) / 256, blocks = count(256, 64);
-    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_gemm<4, 4>), dim3((unsigned)blocks), dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, blocks_n,
-                       acc, y);
-  } else {
-    const int64_t blocks_n = (n + 127) / 128, blocks = count(128, 64);
-    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_gemm<4, 2>), dim3((unsigned)blocks), dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, blocks_n,
-                       acc, y);
-  }
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, blocks_n, acc, y);
+    return hipSuccess;
+  };
+  hipError_t e;
+  if (count(256, 128) >= 1024)
+    e = launch(k_gemm<8, 4, false>, 256, 128);
+  else if (count(256, 64) >= 512)
+    e = k >= 8192 ? launch(k_gemm<4, 4, true>, 256, 64) : launch(k_gemm<4, 4, false>, 256, 64);
+  else
+    e = launch(k_gemm<4, 2, true>, 128, 64);
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 
