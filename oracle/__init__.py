@@ -85,6 +85,14 @@ def _load():
         lib.orc_rescale.restype = None
         lib.orc_bitlinear_forward.argtypes = [p, ctypes.c_float, p, i64, i64, i64, p, p, p, p]
         lib.orc_bitlinear_forward.restype = ctypes.c_int
+        lib.orc_glu.argtypes = [p, i64, i64, ctypes.c_float, p, p]
+        lib.orc_glu.restype = None
+        lib.orc_pack_glu.argtypes = [p, i64, i64, p]
+        lib.orc_pack_glu.restype = ctypes.c_int
+        lib.orc_unpack_glu.argtypes = [p, i64, i64, p]
+        lib.orc_unpack_glu.restype = ctypes.c_int
+        lib.orc_bitlinear_glu_forward.argtypes = [p, ctypes.c_float, p, i64, i64, i64, p, p, p, p]
+        lib.orc_bitlinear_glu_forward.restype = ctypes.c_int
         lib.orc_set_threads.argtypes = [ctypes.c_int]
         lib.orc_set_threads.restype = ctypes.c_int
         _lib = lib
@@ -209,6 +217,64 @@ def bitlinear_forward(packed: np.ndarray, gamma, x_bf16: np.ndarray, n: int):
     if rc != 0:
         raise ValueError("k must be a multiple of 64")
     return y, acc, xq, alpha
+
+
+def glu(acc: np.ndarray, gamma, alpha: np.ndarray) -> np.ndarray:
+    """Squared-ReLU gating of a gate+up product: acc [m][2f] (gate rows, then
+    up rows) -> h [m][f] bf16 bits, h = relu(g)^2 * u from the exact rescaled
+    values, rounded once."""
+    acc = _c(acc, np.int32)
+    alpha = _c(alpha, np.float32)
+    m, n2 = acc.shape
+    assert n2 % 2 == 0
+    h = np.empty((m, n2 // 2), np.uint16)
+    _load().orc_glu(_p(acc), m, n2 // 2, float(np.float32(gamma)), _p(alpha), _p(h))
+    return h
+
+
+def pack_glu(q: np.ndarray) -> np.ndarray:
+    """Pack a gate+up ternary matrix [2f][k] with alternating gate/up 16-row tiles."""
+    q = _c(q, np.int8)
+    n2, k = q.shape
+    out = np.empty(packed_bytes(n2, k), np.uint8)
+    rc = _load().orc_pack_glu(_p(q), n2 // 2, k, _p(out))
+    if rc != 0 or n2 % 2:
+        raise ValueError(f"orc_pack_glu failed ({rc})")
+    return out
+
+
+def unpack_glu(packed: np.ndarray, f: int, k: int) -> np.ndarray:
+    packed = _c(packed, np.uint8)
+    if packed.size != packed_bytes(2 * f, k):
+        raise ValueError("packed buffer has the wrong size")
+    q = np.empty((2 * f, k), np.int8)
+    rc = _load().orc_unpack_glu(_p(packed), f, k, _p(q))
+    if rc != 0:
+        raise ValueError(f"orc_unpack_glu failed ({rc})")
+    return q
+
+
+def ternarize_pack_glu(w: np.ndarray):
+    """Gate+up weights [2f][k] -> (packed in the alternating order, gamma of the whole matrix)."""
+    g = absmean(w)
+    return pack_glu(ternarize(w, g)), g
+
+
+def bitlinear_glu_forward(packed: np.ndarray, gamma, x_bf16: np.ndarray, f: int):
+    """Quantize, gate+up product from the alternating packing, squared-ReLU
+    gating: returns (h bf16 bits [m][f], acc [m][2f], xq, alpha)."""
+    packed = _c(packed, np.uint8)
+    x = _c(x_bf16, np.uint16)
+    m, k = x.shape
+    xq = np.empty((m, k), np.int8)
+    alpha = np.empty(m, np.float32)
+    acc = np.empty((m, 2 * f), np.int32)
+    h = np.empty((m, f), np.uint16)
+    rc = _load().orc_bitlinear_glu_forward(_p(packed), float(np.float32(gamma)), _p(x), m, f, k,
+                                           _p(xq), _p(alpha), _p(acc), _p(h))
+    if rc != 0:
+        raise ValueError("k must be a multiple of 64 and f of 16")
+    return h, acc, xq, alpha
 
 
 def set_threads(n: int = 0) -> int:

@@ -387,6 +387,97 @@ int orc_bitlinear_forward(const uint8_t* packed, float gamma, const uint16_t* x,
     return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Squared-ReLU gating after a fused gate+up BitLinear.                      */
+/* ------------------------------------------------------------------------ */
+/*
+ * Sources: deepmox.com chapter 8, section "A low-bit model is a whole-stack
+ * design", and onilabs.co, "A Two-Billion Ternary Bet": the 2B4T model places
+ * squared ReLU in its feed-forward block, beside the ternary linear layers.
+ * Readings (the pages give no formula):
+ *  - the feed-forward block is gated, as the gate and up projections of the
+ *    2B-shaped model imply: one BitLinear with 2f output rows (one gamma, the
+ *    whole matrix's) whose rows 0..f-1 are the gate and f..2f-1 the up
+ *    projection; h = relu(g)^2 * u elementwise;
+ *  - g and u are the exact rescaled products acc * gamma * alpha / 127 (no
+ *    intermediate rounding); h is evaluated in binary64 and rounded once to
+ *    bf16 (nearest, ties to even).
+ */
+
+/* h[i][j] = bf16(relu(g)^2 * u), g = acc[i][j] * s_i, u = acc[i][f + j] * s_i,
+ * s_i = gamma * alpha[i] / 127; acc is [m][2f] in gate-then-up row order. */
+void orc_glu(const int32_t* acc, int64_t m, int64_t f, float gamma, const float* alpha, uint16_t* h) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < f; ++j) {
+            double s = (double)gamma * (double)alpha[i] / 127.0;
+            double g = (double)acc[i * 2 * f + j] * s;
+            double u = (double)acc[i * 2 * f + f + j] * s;
+            double r = g > 0.0 ? g : 0.0;
+            h[i * f + j] = orc_bf16_from_double(r * r * u);
+        }
+}
+
+/* Row order of a gate+up matrix in its packed form: 16-row tiles alternate,
+ * packed row tile 2t = gate rows 16t..16t+15, packed row tile 2t + 1 = up rows
+ * 16t..16t+15 (rows f + 16t .. of the [2f][k] matrix); f % 16 == 0.  Returns
+ * the source row of packed row p. */
+static int64_t glu_source_row(int64_t p, int64_t f) {
+    int64_t tile = p / 16, r = p % 16;
+    return (tile % 2 == 0 ? 0 : f) + 16 * (tile / 2) + r;
+}
+
+/* Pack a gate+up ternary matrix q [2f][k] in the alternating tile order.
+ * Returns 0, -1 on a bad shape, -2 if a value is not a trit. */
+int orc_pack_glu(const int8_t* q, int64_t f, int64_t k, uint8_t* packed) {
+    if (k % 64 != 0 || f < 0 || f % 16 != 0) return -1;
+    int8_t* perm = (int8_t*)malloc((size_t)(2 * f * k > 0 ? 2 * f * k : 1));
+    if (!perm) return -1;
+    for (int64_t p = 0; p < 2 * f; ++p) memcpy(perm + p * k, q + glu_source_row(p, f) * k, (size_t)k);
+    int rc = orc_pack(perm, 2 * f, k, packed);
+    free(perm);
+    return rc;
+}
+
+/* Inverse of orc_pack_glu: q [2f][k] in gate-then-up row order. */
+int orc_unpack_glu(const uint8_t* packed, int64_t f, int64_t k, int8_t* q) {
+    if (k % 64 != 0 || f < 0 || f % 16 != 0) return -1;
+    int8_t* perm = (int8_t*)malloc((size_t)(2 * f * k > 0 ? 2 * f * k : 1));
+    if (!perm) return -1;
+    int rc = orc_unpack(packed, 2 * f, k, perm);
+    if (rc == 0)
+        for (int64_t p = 0; p < 2 * f; ++p) memcpy(q + glu_source_row(p, f) * k, perm + p * k, (size_t)k);
+    free(perm);
+    return rc;
+}
+
+/* Feed-forward front half from gate+up weights packed in the alternating
+ * order: quantize x per token, take the integer products reading each trit
+ * from the packed buffer, gate.  acc [m][2f] is returned in gate-then-up
+ * order; xq, alpha, acc and h are caller-provided. */
+int orc_bitlinear_glu_forward(const uint8_t* packed, float gamma, const uint16_t* x, int64_t m, int64_t f,
+                              int64_t k, int8_t* xq, float* alpha, int32_t* acc, uint16_t* h) {
+    if (k % 64 != 0 || f % 16 != 0) return -1;
+    orc_quant_act(x, m, k, xq, alpha);
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < 2 * f; ++p) {
+        int64_t j = glu_source_row(p, f);
+        for (int64_t i = 0; i < m; ++i) {
+            int64_t s = 0;
+            for (int64_t t = 0; t < k; ++t) {
+                int64_t byte;
+                int bit;
+                trit_position(p, t, k, &byte, &bit);
+                int w = (int)((packed[byte] >> bit) & 3u) - 1;
+                s += (int64_t)w * xq[i * k + t];
+            }
+            acc[i * 2 * f + j] = (int32_t)s;
+        }
+    }
+    orc_glu(acc, m, f, gamma, alpha, h);
+    return 0;
+}
+
 /* Thread count of the OpenMP loops above (results never depend on it; the
  * benchmark's CPU-baseline leg times the oracle at one thread and at all). */
 int orc_set_threads(int n) {

@@ -14,7 +14,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 PINS = [os.path.join(ROOT, "tests", "test_oracle_absmean.py"),
-        os.path.join(ROOT, "tests", "test_oracle_act_linear.py")]
+        os.path.join(ROOT, "tests", "test_oracle_act_linear.py"),
+        os.path.join(ROOT, "tests", "test_oracle_glu.py")]
 
 MUTANTS = {
     "ternarize_round_half_away": ("float r = rintf(scaled);", "float r = roundf(scaled);"),
@@ -42,6 +43,13 @@ MUTANTS = {
     "rescale_128": ("(double)acc[i * n + j] * (double)gamma * (double)alpha[i] / 127.0;",
                     "(double)acc[i * n + j] * (double)gamma * (double)alpha[i] / 128.0;"),
     "bf16_round_half_away": ("double r = nearbyint(ldexp(a, -ulp_exp));", "double r = round(ldexp(a, -ulp_exp));"),
+    "glu_no_relu": ("double r = g > 0.0 ? g : 0.0;", "double r = g;"),
+    "glu_not_squared": ("h[i * f + j] = orc_bf16_from_double(r * r * u);",
+                        "h[i * f + j] = orc_bf16_from_double(r * u);"),
+    "glu_halves_swapped": ("return (tile % 2 == 0 ? 0 : f) + 16 * (tile / 2) + r;",
+                           "return (tile % 2 == 0 ? f : 0) + 16 * (tile / 2) + r;"),
+    "glu_up_from_gate_row": ("double u = (double)acc[i * 2 * f + f + j] * s;",
+                             "double u = (double)acc[i * 2 * f + j] * s;"),
     "unpack_codes_not_trits": ("q[row * k + col] = (int8_t)((int)((packed[byte] >> bit) & 3u) - 1);",
                                "q[row * k + col] = (int8_t)((int)((packed[byte] >> bit) & 3u));"),
 }
