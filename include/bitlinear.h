@@ -17,7 +17,9 @@
  *        per 8-bit storage unit, moves packed weights from HBM on chip,
  *        unpacks them and computes with the 8-bit activations.
  *   [P3] onilabs.co, "A Two-Billion Ternary Bet": activations are quantized
- *        dynamically; scale factors are staged for mixed-precision compute.
+ *        dynamically; scale factors are staged for mixed-precision compute;
+ *        the 2B4T model uses squared ReLU in its feed-forward block (as does
+ *        [P2], same section).
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
@@ -131,6 +133,46 @@ bl_status bl_linear(const uint8_t* packed, const float* gamma, const int8_t* xq,
  * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_HIP. */
 bl_status bl_bitlinear(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t n, int64_t k,
                        int8_t* xq, float* alpha, int32_t* acc, uint16_t* y, void* stream);
+
+/* ---- Gated feed-forward front half: gate+up BitLinear + squared ReLU ----
+ * A feed-forward block with f hidden units has one gate+up BitLinear of 2f
+ * output rows (rows 0..f-1 the gate, rows f..2f-1 the up projection; one
+ * gamma for the whole matrix) followed by squared-ReLU gating [P2, P3]:
+ *   h[i][j] = bf16(relu(g)^2 * u),  g = acc[i][j] * s,  u = acc[i][f + j] * s,
+ *   s = gamma * alpha[i] / 127,
+ * with acc the exact int32 products as in bl_linear.  g and u are not rounded
+ * to bf16 first; h is evaluated in fp32 (within one bf16 ulp of the exactly
+ * rounded value) and relu(g) = 0 gives +0 * u (so -0 for negative u).
+ * f must be a positive multiple of 16. */
+
+/* Weight preparation for a gate+up matrix: exactly bl_ternarize_pack of the
+ * [2f][k] matrix w (gamma of all 2f*k weights), except that the packed row
+ * tiles alternate: packed row tile 2t holds gate rows 16t..16t+15 and packed
+ * row tile 2t+1 holds up rows 16t..16t+15 (rows f+16t.. of w), so that both
+ * halves of 16 outputs sit next to each other.  packed has
+ * bl_packed_bytes(2f, k) bytes; bl_unpack_ternary(packed, 2f, k) returns the
+ * rows in that packed order.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE (f not a positive multiple of 16, bad k,
+ *         2f*k > 2^39), BL_ERR_ALIGN, BL_ERR_WORKSPACE, BL_ERR_HIP. */
+bl_status bl_ternarize_pack_glu(const float* w, int64_t f, int64_t k, uint8_t* packed, float* gamma,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Gated product from quantized activations: packed/gamma from
+ * bl_ternarize_pack_glu, xq/alpha from bl_quant_act ([m][k]).
+ *   h      out [m][f] bf16 bit patterns.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_HIP. */
+bl_status bl_linear_glu(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha,
+                        int64_t m, int64_t f, int64_t k, uint16_t* h, void* stream);
+
+/* The gated front half in one call: per-token quantization of x (xq and
+ * alpha written exactly as bl_quant_act would) and the gated product, with
+ * exactly the results of bl_quant_act followed by bl_linear_glu.  One token
+ * (and up to 4 with short rows) takes a single kernel.
+ *   x      [m][k] bf16; xq out [m][k] int8; alpha out [m] fp32;
+ *   h      out [m][f] bf16 bit patterns.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_HIP. */
+bl_status bl_bitlinear_glu(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t f,
+                           int64_t k, int8_t* xq, float* alpha, uint16_t* h, void* stream);
 
 /* Unpack a packed buffer back to trits (test and inspection helper [P2]):
  * q[j][t] in {-1, 0, 1} for the n real rows.  A code 3 (never produced by

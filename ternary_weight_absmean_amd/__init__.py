@@ -21,6 +21,7 @@ from ._build import LIB_PATH, INCLUDE
 __all__ = [
     "BitLinearError", "bl_packed_bytes", "bl_ternarize_pack_workspace_bytes", "bl_ternarize_pack",
     "bl_quant_act", "bl_linear", "bl_bitlinear", "bl_unpack_ternary", "bl_status_string", "library", "declared_symbols",
+    "bl_ternarize_pack_glu", "bl_linear_glu", "bl_bitlinear_glu",
 ]
 
 
@@ -50,6 +51,12 @@ _lib.bl_linear.restype = ctypes.c_int
 _lib.bl_bitlinear.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]
 _lib.bl_bitlinear.restype = ctypes.c_int
 _lib.bl_unpack_ternary.argtypes = [_P, _I64, _I64, _P, _P]
+_lib.bl_ternarize_pack_glu.argtypes = [_P, _I64, _I64, _P, _P, _P, _SZ, _P]
+_lib.bl_ternarize_pack_glu.restype = ctypes.c_int
+_lib.bl_linear_glu.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P]
+_lib.bl_linear_glu.restype = ctypes.c_int
+_lib.bl_bitlinear_glu.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P]
+_lib.bl_bitlinear_glu.restype = ctypes.c_int
 _lib.bl_unpack_ternary.restype = ctypes.c_int
 _lib.bl_status_string.argtypes = [ctypes.c_int]
 _lib.bl_status_string.restype = ctypes.c_char_p
@@ -192,6 +199,69 @@ def bl_bitlinear(packed: torch.Tensor, gamma: torch.Tensor, x: torch.Tensor, n: 
     _check("bl_bitlinear", _lib.bl_bitlinear(_ptr(packed), _ptr(gamma), _ptr(x), m, n, k, _ptr(xq), _ptr(alpha),
                                              _ptr(acc), _ptr(y), _stream(dev)))
     return acc, y, xq, alpha
+
+
+def bl_ternarize_pack_glu(w: torch.Tensor, packed: torch.Tensor | None = None, gamma: torch.Tensor | None = None,
+                          workspace: torch.Tensor | None = None):
+    """fp32 gate+up weights ``[2f][k]`` (gate rows first) -> (packed with
+    alternating gate/up row tiles, gamma fp32 [1])."""
+    _need(w, "w", torch.float32)
+    n2, k = w.shape
+    f = n2 // 2
+    nbytes = bl_packed_bytes(n2, k)
+    if packed is None:
+        packed = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=w.device)
+    if gamma is None:
+        gamma = torch.empty(1, dtype=torch.float32, device=w.device)
+    ws = bl_ternarize_pack_workspace_bytes(n2, k)
+    if workspace is None:
+        workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=w.device)
+    if n2 % 2:
+        raise ValueError("a gate+up matrix has an even number of rows")
+    _check("bl_ternarize_pack_glu", _lib.bl_ternarize_pack_glu(_ptr(w), f, k, _ptr(packed), _ptr(gamma),
+                                                               _ptr(workspace), workspace.numel(), _stream(w.device)))
+    return packed, gamma
+
+
+def bl_linear_glu(packed: torch.Tensor, gamma: torch.Tensor, xq: torch.Tensor, alpha: torch.Tensor, f: int,
+                  h: torch.Tensor | None = None) -> torch.Tensor:
+    """Gated product from int8 activations ``[m][k]``: h bf16 [m][f]."""
+    _need(xq, "xq", torch.int8)
+    m, k = xq.shape
+    if h is None:
+        h = torch.empty((m, f), dtype=torch.bfloat16, device=xq.device)
+    _need(h, "h", torch.bfloat16, (m, f))
+    _need(packed, "packed", torch.uint8)
+    if packed.numel() < bl_packed_bytes(2 * f, k):
+        raise ValueError("packed buffer is smaller than bl_packed_bytes(2f, k)")
+    _check("bl_linear_glu", _lib.bl_linear_glu(_ptr(packed), _ptr(gamma), _ptr(xq), _ptr(alpha), m, f, k, _ptr(h),
+                                               _stream(xq.device)))
+    return h
+
+
+def bl_bitlinear_glu(packed: torch.Tensor, gamma: torch.Tensor, x: torch.Tensor, f: int,
+                     xq: torch.Tensor | None = None, alpha: torch.Tensor | None = None,
+                     h: torch.Tensor | None = None):
+    """bf16 activations ``[m][k]`` through quantization, the gate+up product
+    and squared-ReLU gating: returns (h bf16 [m][f], xq, alpha)."""
+    _need(x, "x", torch.bfloat16)
+    m, k = x.shape
+    dev = x.device
+    if xq is None:
+        xq = torch.empty((m, k), dtype=torch.int8, device=dev)
+    if alpha is None:
+        alpha = torch.empty(m, dtype=torch.float32, device=dev)
+    if h is None:
+        h = torch.empty((m, f), dtype=torch.bfloat16, device=dev)
+    _need(xq, "xq", torch.int8, (m, k))
+    _need(alpha, "alpha", torch.float32, (m,))
+    _need(h, "h", torch.bfloat16, (m, f))
+    _need(packed, "packed", torch.uint8)
+    if packed.numel() < bl_packed_bytes(2 * f, k):
+        raise ValueError("packed buffer is smaller than bl_packed_bytes(2f, k)")
+    _check("bl_bitlinear_glu", _lib.bl_bitlinear_glu(_ptr(packed), _ptr(gamma), _ptr(x), m, f, k, _ptr(xq),
+                                                     _ptr(alpha), _ptr(h), _stream(dev)))
+    return h, xq, alpha
 
 
 def bl_unpack_ternary(packed: torch.Tensor, n: int, k: int, q: torch.Tensor | None = None) -> torch.Tensor:

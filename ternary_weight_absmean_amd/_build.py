@@ -83,7 +83,8 @@ def build(verbose: bool = False) -> str:
         if scratch:
             raise RuntimeError("kernels using scratch memory: " + "; ".join(scratch))
         tmp_lib = LIB_PATH + ".tmp"
-        subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib], check=True)
+        subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", *objs, "-o", tmp_lib],
+                       check=True)
         os.replace(tmp_lib, LIB_PATH)
     return LIB_PATH
 

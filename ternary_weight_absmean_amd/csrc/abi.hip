@@ -85,6 +85,59 @@ bl_status bl_bitlinear(const uint8_t* packed, const float* gamma, const uint16_t
   return from_hip(bl::launch_gemm(packed, gamma, xq, alpha, m, n, k, acc, y, s));
 }
 
+bl_status bl_ternarize_pack_glu(const float* w, int64_t f, int64_t k, uint8_t* packed, float* gamma, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!w || !packed || !gamma || !workspace) return BL_ERR_NULL;
+  if (f < 16 || f % 16 != 0 || 2 * f > BL_MAX_N || !valid_k(k) || !product_ok(2 * f + 16, k) ||
+      2 * f * k > (1LL << 39))
+    return BL_ERR_SHAPE;
+  if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(gamma, 4) || !aligned(workspace, 16)) return BL_ERR_ALIGN;
+  if (workspace_bytes < bl_ternarize_pack_workspace_bytes(2 * f, k)) return BL_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  unsigned long long* bins = (unsigned long long*)workspace;
+  hipError_t e = bl::launch_absmean_bins(w, 2 * f * k, bins, s);
+  if (e == hipSuccess) e = bl::launch_gamma_fold(bins, 2 * f * k, gamma, s);
+  if (e == hipSuccess) e = bl::launch_ternarize_pack(w, 2 * f, k, gamma, packed, s, f);
+  return from_hip(e);
+}
+
+namespace {
+
+bl_status check_glu_product(int64_t m, int64_t f, int64_t k) {
+  if (m < 0 || m > BL_MAX_M || f < 16 || f % 16 != 0 || 2 * f > BL_MAX_N || !valid_k(k) || !product_ok(m, k) ||
+      !product_ok(2 * f + 16, k) || !product_ok(m, 2 * f))
+    return BL_ERR_SHAPE;
+  return BL_OK;
+}
+
+}  // namespace
+
+bl_status bl_linear_glu(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
+                        int64_t f, int64_t k, uint16_t* h, void* stream) {
+  if (bl_status st = check_glu_product(m, f, k)) return st;
+  if (m == 0) return BL_OK;  // empty tensors may carry NULL pointers
+  if (!packed || !gamma || !xq || !alpha || !h) return BL_ERR_NULL;
+  if (!aligned(packed, 16) || !aligned(xq, 16) || !aligned(gamma, 4) || !aligned(alpha, 4) || !aligned(h, 2))
+    return BL_ERR_ALIGN;
+  return from_hip(bl::launch_gemm_glu(packed, gamma, xq, alpha, m, f, k, h, (hipStream_t)stream));
+}
+
+bl_status bl_bitlinear_glu(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t f,
+                           int64_t k, int8_t* xq, float* alpha, uint16_t* h, void* stream) {
+  if (bl_status st = check_glu_product(m, f, k)) return st;
+  if (m == 0) return BL_OK;
+  if (!packed || !gamma || !x || !xq || !alpha || !h) return BL_ERR_NULL;
+  if (!aligned(packed, 16) || !aligned(x, 16) || !aligned(xq, 16) || !aligned(gamma, 4) || !aligned(alpha, 4) ||
+      !aligned(h, 2))
+    return BL_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  if (bl::gemv_fused_glu_applies(m, f, k))
+    return from_hip(bl::launch_gemv_fused_glu(packed, gamma, x, m, f, k, xq, alpha, h, s));
+  hipError_t e = bl::launch_quant_act(x, m, k, xq, alpha, s);
+  if (e != hipSuccess) return from_hip(e);
+  return from_hip(bl::launch_gemm_glu(packed, gamma, xq, alpha, m, f, k, h, s));
+}
+
 bl_status bl_unpack_ternary(const uint8_t* packed, int64_t n, int64_t k, int8_t* q, void* stream) {
   if (n < 0 || n > BL_MAX_N || !valid_k(k) || !product_ok(n + 16, k)) return BL_ERR_SHAPE;
   if (n == 0) return BL_OK;

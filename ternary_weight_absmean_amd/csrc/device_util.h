@@ -27,6 +27,15 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
 // Signed trits of one 2-bit field of four packed bytes.  The field's codes
 // (0, 1, 2 = trit + 1) select bytes 0xFF, 0x00, 0x01 of a constant table with
 // v_perm_b32 (selector bytes 0..3 index the second operand).
+// Squared-ReLU gating of one output from the exact integer products of its
+// gate and up rows: relu(g)^2 * u with g = acc_g * scale, u = acc_u * scale
+// (scale = gamma * alpha / 127), in fp32 without contraction.
+__device__ __forceinline__ float glu_value(int acc_g, int acc_u, float scale) {
+  const float g = (float)acc_g * scale;
+  const float r = g > 0.0f ? g : 0.0f;
+  return (r * r) * ((float)acc_u * scale);
+}
+
 __device__ __forceinline__ int trits_of_field(uint32_t packed4, int field) {
   const uint32_t table = 0x000100FFu;  // byte0 = -1, byte1 = 0, byte2 = +1
   uint32_t sel = (packed4 >> (2 * field)) & 0x03030303u;

@@ -52,7 +52,11 @@ constexpr int kXcds = 8;                // accelerator complex dies, each with i
 // the other and does not wait for the DMA before reading.  Without it (fewer
 // registers: more workgroups per CU) each step's reads wait for the DMA just
 // issued.
-template <int kTB, int kRB, bool kFixedBuffers>
+// kGlu: the matrix is a gate+up matrix packed with alternating gate/up row
+// tiles; a wave's row blocks 2p and 2p + 1 are then the gate and up rows of
+// the same 16 outputs, and the epilogue writes h = bf16(relu(g)^2 * u) into
+// y_out ([m][n / 2]); acc_out is unused.
+template <int kTB, int kRB, bool kFixedBuffers, bool kGlu = false>
 __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* __restrict__ packed, const float* __restrict__ gamma_ptr,
                                                  const int8_t* __restrict__ xq, const float* __restrict__ alpha,
                                                  int64_t m, int64_t n, int64_t k, int64_t blocks_n,
@@ -223,6 +227,36 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* __restrict__ pac
   __syncthreads();
 
   const float gamma = *gamma_ptr;
+  if constexpr (kGlu) {
+    static_assert(kRB % 2 == 0, "gate/up row blocks come in pairs");
+    const int64_t f = n / 2;
+    const int64_t t0 = (n0 + wave * kWN) / (2 * kTileRows);  // gate tile of row blocks 0 and 1
+#pragma unroll
+    for (int tb = 0; tb < kTB; ++tb) {
+      const int tok_local = tb * 16 + col;
+      const int64_t tok = m0 + tok_local;
+      if (tok >= m) continue;
+      const int xsum = row_sum[tok_local];
+      const float scale = (gamma * alpha[tok]) / 127.0f;
+#pragma unroll
+      for (int p = 0; p < kRB / 2; ++p) {
+        const int64_t col0 = (t0 + p) * kTileRows + 4 * sub;  // four outputs of h
+        if (col0 >= f) continue;
+        const v4i& ga = acc[2 * p][tb];
+        const v4i& ua = acc[2 * p + 1][tb];
+        const float h[4] = {glu_value(ga.x - xsum, ua.x - xsum, scale), glu_value(ga.y - xsum, ua.y - xsum, scale),
+                            glu_value(ga.z - xsum, ua.z - xsum, scale), glu_value(ga.w - xsum, ua.w - xsum, scale)};
+        uint16_t* hp = y_out + tok * f + col0;  // f % 16 == 0: all four are inside the row
+        if (((uintptr_t)hp & 7) == 0) {
+          *reinterpret_cast<uint2*>(hp) = make_uint2(f32x2_to_bf16x2(h[0], h[1]), f32x2_to_bf16x2(h[2], h[3]));
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) hp[i] = f32_to_bf16_rne(h[i]);
+        }
+      }
+    }
+    return;
+  }
   // 4 consecutive outputs per lane: one 16-byte int32 / 8-byte bf16 store when
   // every row start is aligned for it
   const bool vec_ok = (n % 4) == 0 && ((uintptr_t)acc_out % 16) == 0 && ((uintptr_t)y_out % 8) == 0;
@@ -261,8 +295,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* __restrict__ pac
 
 }  // namespace
 
-hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
-                       int64_t n, int64_t k, int32_t* acc, uint16_t* y, hipStream_t s) {
+namespace {
+
+template <bool kGlu>
+hipError_t launch_gemm_impl(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
+                            int64_t n, int64_t k, int32_t* acc, uint16_t* y, hipStream_t s) {
   // Largest tile that still gives the chip enough workgroups: 256 rows x 128
   // tokens with >= 4 per CU, else 256 x 64 with >= 2 per CU, else 128 x 64.
   // Fixed buffers (unrolled steps, more registers) where they measured
@@ -280,13 +317,25 @@ hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* 
   };
   hipError_t e;
   if (count(256, 128) >= 1024)
-    e = launch(k_gemm<8, 4, false>, 256, 128);
+    e = launch(k_gemm<8, 4, false, kGlu>, 256, 128);
   else if (count(256, 64) >= 512)
-    e = k >= 8192 ? launch(k_gemm<4, 4, true>, 256, 64) : launch(k_gemm<4, 4, false>, 256, 64);
+    e = k >= 8192 ? launch(k_gemm<4, 4, true, kGlu>, 256, 64) : launch(k_gemm<4, 4, false, kGlu>, 256, 64);
   else
-    e = launch(k_gemm<4, 2, true>, 128, 64);
+    e = launch(k_gemm<4, 2, true, kGlu>, 128, 64);
   if (e != hipSuccess) return e;
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
+                       int64_t n, int64_t k, int32_t* acc, uint16_t* y, hipStream_t s) {
+  return launch_gemm_impl<false>(packed, gamma, xq, alpha, m, n, k, acc, y, s);
+}
+
+hipError_t launch_gemm_glu(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
+                           int64_t f, int64_t k, uint16_t* h, hipStream_t s) {
+  return launch_gemm_impl<true>(packed, gamma, xq, alpha, m, 2 * f, k, nullptr, h, s);
 }
 
 }  // namespace bl

@@ -87,6 +87,22 @@ __device__ __forceinline__ void store_tile(const v4i& acc, int64_t row0, int64_t
   }
 }
 
+// Gated outputs h[tok][col0 .. col0 + 3] = bf16(relu(g)^2 * u) from the exact
+// products of four gate rows (g) and the four matching up rows (u).
+__device__ __forceinline__ void store_glu_tile(const v4i& g, const v4i& u, int64_t col0, int64_t tok, int64_t f,
+                                               float scale, uint16_t* __restrict__ h_out) {
+  const float h[4] = {glu_value(g.x, u.x, scale), glu_value(g.y, u.y, scale), glu_value(g.z, u.z, scale),
+                      glu_value(g.w, u.w, scale)};
+  uint16_t* hp = h_out + tok * f + col0;
+  if (col0 + 3 < f && ((uintptr_t)hp & 7) == 0) {
+    *reinterpret_cast<uint2*>(hp) = make_uint2(f32x2_to_bf16x2(h[0], h[1]), f32x2_to_bf16x2(h[2], h[3]));
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (col0 + i < f) hp[i] = f32_to_bf16_rne(h[i]);
+}
+
 // Partial reduction of `v` over the `g = min(tpr, 64)` lanes of a token row
 // group inside one wave; lanes with (tid % g) == 0 then write the group's value
 // to scratch[tid / g].  A row's value is the max/sum of its tpr/g entries.
@@ -295,8 +311,11 @@ constexpr int kM1MaxSlots = 14;  // 16-byte bf16 chunks per lane (own groups onl
 // sum q*x; one barrier then combines them.  A workgroup handles kRT
 // consecutive 16-row tiles, reusing the quantized tokens; the weight loads
 // of all its tiles form one stream, prefetched a batch ahead.  kC = slots
-// per lane (ceil(own groups / 2)).
-template <int kRT, int kC, int kM>
+// per lane (ceil(own groups / 2)).  kGlu: the matrix is a gate+up matrix
+// packed with alternating gate/up row tiles and kRT = 2, so the workgroup's
+// two tiles are the gate and up rows of the same 16 outputs; wave 0 writes
+// h = bf16(relu(g)^2 * u) into y_out ([m][n / 2]).
+template <int kRT, int kC, int kM, bool kGlu = false>
 __global__ __launch_bounds__(kWaves * 64) void k_bitlinear_m1(const uint4* __restrict__ packed,
                                                                const float* __restrict__ gamma_ptr,
                                                                const uint4* __restrict__ x, float* __restrict__ alpha,
@@ -462,6 +481,18 @@ __global__ __launch_bounds__(kWaves * 64) void k_bitlinear_m1(const uint4* __res
   // wave w finishes row tiles w, w + kW, ...; MFMA column c is token c
   if (col >= m || col >= kM) return;
   const float scale = (gamma * my_amax) / 127.0f;
+  if constexpr (kGlu) {
+    static_assert(kRT == 2, "a gate tile and its up tile per workgroup");
+    if (wave != 0) return;
+    v4i g = partial[0][0][lane], u = partial[1][0][lane];
+#pragma unroll
+    for (int w = 1; w < kW; ++w) {
+      add4(g, partial[0][w][lane]);
+      add4(u, partial[1][w][lane]);
+    }
+    store_glu_tile(g, u, (int64_t)(tile0 / 2) * kTileRows + 4 * sub, col, n / 2, scale, y_out);
+    return;
+  }
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
     if (rt % kW != wave || rt >= tiles_here) continue;
@@ -822,6 +853,29 @@ M1Kernel m1_pick(int64_t m, int64_t groups) {
   return nullptr;
 }
 
+template <int kRT>
+M1Kernel m1_pick_glu(int64_t m, int64_t groups) {
+  const int64_t slots = ((groups + kWaves - 1) / kWaves + 1) / 2;
+  if (m == 1) {
+    if (slots <= 2) return k_bitlinear_m1<kRT, 2, 1, true>;
+    if (slots <= 5) return k_bitlinear_m1<kRT, 5, 1, true>;
+    if (slots <= kM1MaxSlots) return k_bitlinear_m1<kRT, kM1MaxSlots, 1, true>;
+  } else if (m <= 4 && slots <= 2) {
+    return k_bitlinear_m1<kRT, 2, 4, true>;
+  }
+  return nullptr;
+}
+
+// The gated form always takes two row tiles (a gate tile and its up tile)
+// per workgroup; the token rules are those of m1_config.
+M1Config m1_config_glu(int64_t m, int64_t groups, int64_t row_tiles) {
+  if (m > 1 && (m > 4 || row_tiles >= 512)) return M1Config{};
+  M1Config c;
+  c.rt = 2;
+  c.kernel = m1_pick_glu<2>(m, groups);
+  return c;
+}
+
 M1Config m1_config(int64_t m, int64_t groups, int64_t row_tiles) {
   // Several tokens: every workgroup quantizes all of them, which pays off
   // only for short rows and few row tiles (measured: rows of 2560 with 160
@@ -848,6 +902,25 @@ bool gemv_fused_applies(int64_t m, int64_t n, int64_t k) {
   if (m1_config(m, (k / kTileCols + 3) / 4, (n + kTileRows - 1) / kTileRows).kernel) return true;
   if (m > 1 && m * k > kFusedMaxTokenColumns) return false;
   return fused_plan(m, 1, k).rt > 0;
+}
+
+bool gemv_fused_glu_applies(int64_t m, int64_t f, int64_t k) {
+  if (m < 1 || m > 4 || f < 16 || f % 16 != 0) return false;
+  return m1_config_glu(m, (k / kTileCols + 3) / 4, 2 * f / kTileRows).kernel != nullptr;
+}
+
+hipError_t launch_gemv_fused_glu(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t f,
+                                 int64_t k, int8_t* xq, float* alpha, uint16_t* h, hipStream_t s) {
+  if (!gemv_fused_glu_applies(m, f, k)) return hipErrorInvalidValue;
+  const int64_t groups = (k / kTileCols + 3) / 4;
+  const int64_t row_tiles = 2 * f / kTileRows;
+  const M1Config c = m1_config_glu(m, groups, row_tiles);
+  const int64_t tokens = m == 1 ? 1 : 4;
+  const size_t lds = (size_t)kWaves * (size_t)((groups + kWaves - 1) / kWaves) * (size_t)tokens * 256;
+  const dim3 grid((unsigned)(row_tiles / 2));
+  hipLaunchKernelGGL(c.kernel, grid, dim3(64 * kWaves), lds, s, reinterpret_cast<const uint4*>(packed), gamma,
+                     reinterpret_cast<const uint4*>(x), alpha, xq, (int)m, (int)(2 * f), (int)k, nullptr, h);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t n,

@@ -18,8 +18,10 @@ constexpr int kAbsmeanMaxBlocks = 256;
 constexpr size_t kPackWorkspaceBytes = (size_t)kAbsmeanMaxBlocks * 256 * sizeof(unsigned long long);
 hipError_t launch_absmean_bins(const float* w, int64_t count, unsigned long long* ws, hipStream_t s);
 hipError_t launch_gamma_fold(const unsigned long long* ws, int64_t count, float* gamma, hipStream_t s);
+// glu_f > 0: w is [2 * glu_f][k] gate rows then up rows, packed with
+// alternating gate/up 16-row tiles (n == 2 * glu_f, glu_f % 16 == 0).
 hipError_t launch_ternarize_pack(const float* w, int64_t n, int64_t k, const float* gamma, uint8_t* packed,
-                                 hipStream_t s);
+                                 hipStream_t s, int64_t glu_f = 0);
 hipError_t launch_unpack(const uint8_t* packed, int64_t n, int64_t k, int8_t* q, hipStream_t s);
 
 // Per-token absmax int8 quantizer.
@@ -39,5 +41,16 @@ hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const ui
                              int64_t k, int8_t* xq, float* alpha, int32_t* acc, uint16_t* y, hipStream_t s);
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
                        int64_t n, int64_t k, int32_t* acc, uint16_t* y, hipStream_t s);
+
+// Squared-ReLU gated products from gate+up weights packed with alternating
+// gate/up row tiles (n = 2f rows): h[i][j] = bf16(relu(g)^2 * u), g and u the
+// rescaled products of gate row j and up row j; h is [m][f].
+hipError_t launch_gemm_glu(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
+                           int64_t f, int64_t k, uint16_t* h, hipStream_t s);
+// One kernel for quantization + gated product, where the single-token (or
+// few-token, short-row) kernel applies.
+bool gemv_fused_glu_applies(int64_t m, int64_t f, int64_t k);
+hipError_t launch_gemv_fused_glu(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t f,
+                                 int64_t k, int8_t* xq, float* alpha, uint16_t* h, hipStream_t s);
 
 }  // namespace bl

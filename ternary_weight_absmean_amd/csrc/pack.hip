@@ -240,9 +240,12 @@ constexpr int kPackThreads = 256;
 // rotations, and lanes 0..3 of each 16 store the dwords.  Rows past n get
 // code 1 (trit 0).  Code = q + 1, q = clamp(round_half_even(w / (gamma +
 // 1e-5)), -1, 1) with IEEE fp32 division.
+// glu_f > 0: w is a gate+up matrix [2 * glu_f][k] (gate rows first) and the
+// packed row tiles alternate gate and up: packed tile 2t holds gate rows
+// 16t..16t+15, tile 2t + 1 the up rows 16t..16t+15 (glu_f % 16 == 0).
 __global__ __launch_bounds__(kPackThreads) void k_ternarize_pack(const float4* __restrict__ w4, int64_t n, int64_t k,
                                                                   const float* __restrict__ gamma_ptr,
-                                                                  uint32_t* __restrict__ packed) {
+                                                                  uint32_t* __restrict__ packed, int64_t glu_f) {
   const int64_t k4 = k / 4;
   const int64_t n_pad = (n + kTileRows - 1) / kTileRows * kTileRows;
   const int64_t idx = (int64_t)blockIdx.x * kPackThreads + threadIdx.x;  // float4 index in the padded matrix
@@ -267,7 +270,13 @@ __global__ __launch_bounds__(kPackThreads) void k_ternarize_pack(const float4* _
   // OR over the four lanes of the same dword (lane offsets 4 and 8 within the 16-lane row)
   part |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)part, 0x124, 0xF, 0xF, false);  // row_ror:4
   part |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)part, 0x128, 0xF, 0xF, false);  // row_ror:8
-  if (j < 4) packed[(((row / kTileRows) * (k / kTileCols) + kt) * kTileRows + (row % kTileRows)) * 4 + j] = part;
+  int64_t prow = row;  // row of the packed matrix
+  if (glu_f > 0) {
+    const bool up = row >= glu_f;
+    const int64_t r = up ? row - glu_f : row;
+    prow = (r / kTileRows) * (2 * kTileRows) + (up ? kTileRows : 0) + r % kTileRows;
+  }
+  if (j < 4) packed[(((prow / kTileRows) * (k / kTileCols) + kt) * kTileRows + (prow % kTileRows)) * 4 + j] = part;
 }
 
 __global__ __launch_bounds__(kPackThreads) void k_unpack(const uint4* __restrict__ packed, int64_t n, int64_t k,
@@ -308,13 +317,13 @@ hipError_t launch_gamma_fold(const unsigned long long* ws, int64_t count, float*
 }
 
 hipError_t launch_ternarize_pack(const float* w, int64_t n, int64_t k, const float* gamma, uint8_t* packed,
-                                 hipStream_t s) {
+                                 hipStream_t s, int64_t glu_f) {
   const int64_t n_pad = (n + kTileRows - 1) / kTileRows * kTileRows;
   const int64_t threads = n_pad * (k / 4);
   const int64_t blocks = (threads + kPackThreads - 1) / kPackThreads;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_ternarize_pack, dim3((unsigned)blocks), dim3(kPackThreads), 0, s,
-                     reinterpret_cast<const float4*>(w), n, k, gamma, reinterpret_cast<uint32_t*>(packed));
+                     reinterpret_cast<const float4*>(w), n, k, gamma, reinterpret_cast<uint32_t*>(packed), glu_f);
   return hipGetLastError();
 }
 

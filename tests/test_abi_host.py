@@ -129,3 +129,30 @@ def test_bitlinear_validation():
     assert call(x=FAKE + 4) == BL_ERR_ALIGN
     assert call(xq=FAKE + 1) == BL_ERR_ALIGN
     assert call(m=0, x=None, xq=None, alpha=None) == BL_OK
+
+
+def test_glu_entry_points_validation():
+    WS = 256 * 256 * 8
+    pack = lib.bl_ternarize_pack_glu
+    assert pack(None, 16, 64, FAKE, FAKE, FAKE, WS, None) == BL_ERR_NULL
+    assert pack(FAKE, 24, 64, FAKE, FAKE, FAKE, WS, None) == BL_ERR_SHAPE   # f not a multiple of 16
+    assert pack(FAKE, 0, 64, FAKE, FAKE, FAKE, WS, None) == BL_ERR_SHAPE
+    assert pack(FAKE, 16, 96, FAKE, FAKE, FAKE, WS, None) == BL_ERR_SHAPE
+    assert pack(FAKE, 1 << 17, 1 << 22, FAKE, FAKE, FAKE, WS, None) == BL_ERR_SHAPE  # 2f*k > 2^39
+    assert pack(FAKE + 4, 16, 64, FAKE, FAKE, FAKE, WS, None) == BL_ERR_ALIGN
+    assert pack(FAKE, 16, 64, FAKE, FAKE, FAKE, WS - 1, None) == BL_ERR_WORKSPACE
+
+    lin = lib.bl_linear_glu
+    assert lin(FAKE, FAKE, FAKE, FAKE, 0, 16, 64, None, None) == BL_OK     # empty
+    assert lin(FAKE, FAKE, FAKE, FAKE, 1, 16, 64, None, None) == BL_ERR_NULL
+    assert lin(FAKE, FAKE, FAKE, FAKE, 1, 8, 64, FAKE, None) == BL_ERR_SHAPE
+    assert lin(FAKE, FAKE, FAKE, FAKE, 1, 16, 100, FAKE, None) == BL_ERR_SHAPE
+    assert lin(FAKE, FAKE, FAKE + 8, FAKE, 1, 16, 64, FAKE, None) == BL_ERR_ALIGN
+    assert lin(FAKE, FAKE, FAKE, FAKE, 1, 16, 64, FAKE + 1, None) == BL_ERR_ALIGN
+
+    bit = lib.bl_bitlinear_glu
+    assert bit(FAKE, FAKE, None, 0, 16, 64, None, None, None, None) == BL_OK
+    assert bit(FAKE, FAKE, FAKE, 1, 16, 64, FAKE, FAKE, None, None) == BL_ERR_NULL
+    assert bit(FAKE, FAKE, FAKE, 1, 17, 64, FAKE, FAKE, FAKE, None) == BL_ERR_SHAPE
+    assert bit(FAKE, FAKE, FAKE, -1, 16, 64, FAKE, FAKE, FAKE, None) == BL_ERR_SHAPE
+    assert bit(FAKE, FAKE, FAKE + 4, 1, 16, 64, FAKE, FAKE, FAKE, None) == BL_ERR_ALIGN
