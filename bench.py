@@ -493,6 +493,15 @@ PROFILE_CASES = {
 }
 
 
+def _repeat(fn, inner):
+    """fn called `inner` times: one graph replay then holds that many calls, so
+    that the per-replay launch gap is spread over them (time / inner)."""
+    def run():
+        for _ in range(inner):
+            fn()
+    return run
+
+
 def _graph_time_ms(torch, fn, reps, warm=2):
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
@@ -559,7 +568,11 @@ def measure_extras(args, linears, lib):
         x = act(datagen.stream_id(wl, 0, 2 if name == "gate_up" else 3, datagen.TENSOR_X) + 2048, m, k, wl,
                 datagen.STACK_2B_OUTLIERS, datagen.STACK_2B_OUTLIER_MULT)
         xq, alpha, y = bufs(m, n, k)
-        ms = _graph_time_ms(torch, layer_fn([(lin["packed"], lin["gamma"], x, n, k, xq, alpha, y)], m), 20)
+        # ten calls per graph replay (a replay of a single ~60 us kernel would
+        # also time the gap between graph launches)
+        inner = 10
+        ms = _graph_time_ms(torch, _repeat(layer_fn([(lin["packed"], lin["gamma"], x, n, k, xq, alpha, y)], m),
+                                           inner), 10) / inner
         # the product alone (quantized activations already in place)
         def gemm_only():
             s = vp(torch.cuda.current_stream().cuda_stream)
@@ -567,13 +580,63 @@ def measure_extras(args, linears, lib):
                                vp(alpha.data_ptr()), m, n, k, None, vp(y.data_ptr()), s)
             if rc:
                 raise RuntimeError(bl.bl_status_string(rc))
-        ms_gemm = _graph_time_ms(torch, gemm_only, 20)
+        ms_gemm = _graph_time_ms(torch, _repeat(gemm_only, inner), 10) / inner
         ops = 2.0 * m * n * k
         prefill[f"{name} M={m} K={k} N={n}"] = {
             "layer_ms": round(ms, 4), "layer_TOPS": round(ops / (ms * 1e-3) / 1e12, 1),
             "gemm_ms": round(ms_gemm, 4), "gemm_TOPS": round(ops / (ms_gemm * 1e-3) / 1e12, 1),
             "gemm_frac_of_int8_mfma_peak": round(ops / (ms_gemm * 1e-3) / 1e12 / MFMA_I8_PEAK_TOPS, 4)}
     out["prefill_2b"] = prefill
+
+    # ---- gated feed-forward of the 2B layer 0: gate+up with squared-ReLU
+    # gating fused (packed with alternating gate/up tiles), then down
+    gu = next(l for l in linears if l["name"] == "gate_up")
+    dn = next(l for l in linears if l["name"] == "down")
+    f = gu["n"] // 2
+    w_gu = torch.from_numpy(datagen.weights(datagen.stream_id(wl, 0, 2, datagen.TENSOR_W), gu["n"], gu["k"])).to(dev)
+    packed_glu, gamma_glu = bl.bl_ternarize_pack_glu(w_gu)
+    del w_gu
+    ffn = {}
+    for m in (1, 2048):
+        x = act(datagen.stream_id(wl, 0, 2, datagen.TENSOR_X) + 4096 + m, m, gu["k"], wl,
+                datagen.STACK_2B_OUTLIERS, datagen.STACK_2B_OUTLIER_MULT)
+        xq = torch.empty((m, gu["k"]), dtype=torch.int8, device=dev)
+        alpha = torch.empty(m, dtype=torch.float32, device=dev)
+        h = torch.empty((m, f), dtype=torch.bfloat16, device=dev)
+        xq2, alpha2, y2 = bufs(m, dn["n"], dn["k"])
+
+        def glu_only():
+            s = vp(torch.cuda.current_stream().cuda_stream)
+            rc = lib.bl_bitlinear_glu(vp(packed_glu.data_ptr()), vp(gamma_glu.data_ptr()), vp(x.data_ptr()), m, f,
+                                      gu["k"], vp(xq.data_ptr()), vp(alpha.data_ptr()), vp(h.data_ptr()), s)
+            if rc:
+                raise RuntimeError(bl.bl_status_string(rc))
+
+        def chain():
+            glu_only()
+            s = vp(torch.cuda.current_stream().cuda_stream)
+            rc = lib.bl_bitlinear(vp(dn["packed"].data_ptr()), vp(dn["gamma"].data_ptr()), vp(h.data_ptr()), m,
+                                  dn["n"], dn["k"], vp(xq2.data_ptr()), vp(alpha2.data_ptr()), None,
+                                  vp(y2.data_ptr()), s)
+            if rc:
+                raise RuntimeError(bl.bl_status_string(rc))
+
+        # several calls per graph replay, so that the gap between graph
+        # launches is spread over them
+        inner = 50 if m == 1 else 10
+        ms_glu = _graph_time_ms(torch, _repeat(glu_only, inner), 10) / inner
+        ms_chain = _graph_time_ms(torch, _repeat(chain, inner), 10) / inner
+        ops = 2.0 * m * gu["n"] * gu["k"]
+        e = {"gate_up_glu_us": round(ms_glu * 1e3, 2), "ffn_gate_up_glu_down_us": round(ms_chain * 1e3, 2)}
+        if m == 1:
+            e["gate_up_glu_weight_GBps"] = round(packed_glu.numel() / (ms_glu * 1e-3) / 1e9, 1)
+        else:
+            e["gate_up_glu_TOPS"] = round(ops / (ms_glu * 1e-3) / 1e12, 1)
+            e["gate_up_glu_frac_of_int8_mfma_peak"] = round(ops / (ms_glu * 1e-3) / 1e12 / MFMA_I8_PEAK_TOPS, 4)
+        ffn[f"M={m}"] = e
+        del x, xq, alpha, h, xq2, alpha2, y2
+    out["ffn_glu_2b_layer0"] = ffn
+    del packed_glu, gamma_glu
 
     # ---- batched decode through the whole 2B stack, M = 4, 16, 64
     batched = {}

@@ -119,7 +119,9 @@ bl_status bl_linear_glu(const uint8_t* packed, const float* gamma, const int8_t*
   if (!packed || !gamma || !xq || !alpha || !h) return BL_ERR_NULL;
   if (!aligned(packed, 16) || !aligned(xq, 16) || !aligned(gamma, 4) || !aligned(alpha, 4) || !aligned(h, 2))
     return BL_ERR_ALIGN;
-  return from_hip(bl::launch_gemm_glu(packed, gamma, xq, alpha, m, f, k, h, (hipStream_t)stream));
+  hipStream_t s = (hipStream_t)stream;
+  if (bl::gemv_serves(m, 2 * f)) return from_hip(bl::launch_gemv_glu(packed, gamma, xq, alpha, m, f, k, h, s));
+  return from_hip(bl::launch_gemm_glu(packed, gamma, xq, alpha, m, f, k, h, s));
 }
 
 bl_status bl_bitlinear_glu(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t f,
@@ -135,6 +137,7 @@ bl_status bl_bitlinear_glu(const uint8_t* packed, const float* gamma, const uint
     return from_hip(bl::launch_gemv_fused_glu(packed, gamma, x, m, f, k, xq, alpha, h, s));
   hipError_t e = bl::launch_quant_act(x, m, k, xq, alpha, s);
   if (e != hipSuccess) return from_hip(e);
+  if (bl::gemv_serves(m, 2 * f)) return from_hip(bl::launch_gemv_glu(packed, gamma, xq, alpha, m, f, k, h, s));
   return from_hip(bl::launch_gemm_glu(packed, gamma, xq, alpha, m, f, k, h, s));
 }
 

@@ -132,7 +132,9 @@ __device__ __forceinline__ int row_total(int row, int tpr, const int* scratch) {
 // amortized over them; the weight loads of all its tiles form one stream,
 // prefetched a batch ahead, with one buffer resource per tile (reads past a
 // tile, or of a tile past n, return zero codes).
-template <int kRT, int kW>
+// kGlu (kRT even): gate+up matrix with alternating gate/up row tiles; wave w
+// gates the tile pairs (2p, 2p + 1) with p = w, w + kW, ... into y_out ([m][n / 2]).
+template <int kRT, int kW, bool kGlu = false>
 __global__ __launch_bounds__(kW * 64) void k_bitlinear_fused(const uint4* __restrict__ packed,
                                                               const float* __restrict__ gamma_ptr,
                                                               const uint4* __restrict__ x, float* __restrict__ alpha,
@@ -284,9 +286,7 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_fused(const uint4* __rest
   const int xsum = row_total<false>(col, kT / rp, red_sum);  // sum q*x = sum c*x - sum x
   const float row_amax = __uint_as_float((uint32_t)row_total<true>(col, kT / rp, red_max) << 16);
   const float scale = (gamma * row_amax) / 127.0f;
-#pragma unroll
-  for (int rt = 0; rt < kRT; ++rt) {
-    if (rt % kW != wave || rt >= tiles_here) continue;
+  auto tile_sum = [&](int rt) {
     v4i acc = partial[rt][0][lane];
 #pragma unroll
     for (int w = 1; w < kW; ++w) add4(acc, partial[rt][w][lane]);
@@ -294,7 +294,22 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_fused(const uint4* __rest
     acc.y -= xsum;
     acc.z -= xsum;
     acc.w -= xsum;
-    store_tile(acc, (tile0 + rt) * kTileRows + 4 * sub, tok0 + col, n, scale, acc_out, y_out);
+    return acc;
+  };
+  if constexpr (kGlu) {
+    static_assert(kRT % 2 == 0, "gate/up tiles come in pairs");
+#pragma unroll
+    for (int p = 0; p < kRT / 2; ++p) {
+      if (p % kW != wave || 2 * p >= tiles_here) continue;
+      store_glu_tile(tile_sum(2 * p), tile_sum(2 * p + 1), (tile0 / 2 + p) * kTileRows + 4 * sub, tok0 + col, n / 2,
+                     scale, y_out);
+    }
+    return;
+  }
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    if (rt % kW != wave || rt >= tiles_here) continue;
+    store_tile(tile_sum(rt), (tile0 + rt) * kTileRows + 4 * sub, tok0 + col, n, scale, acc_out, y_out);
   }
 }
 
@@ -511,7 +526,9 @@ __global__ __launch_bounds__(kWaves * 64) void k_bitlinear_m1(const uint4* __res
 // weight byte falls as 4 * tokens / (16 * kRT).  Codes become signed trits
 // with v_perm.  kB groups per wave form a batch; the next batch's loads are
 // issued before the current batch's products.
-template <int kRT, int kB, int kW>
+// kGlu (kRT even): gate+up matrix with alternating gate/up row tiles; the
+// pairs (2p, 2p + 1) are gated into y_out ([m][n / 2]).
+template <int kRT, int kB, int kW, bool kGlu = false>
 __global__ __launch_bounds__(kW * 64) void k_gemv_direct(const uint4* __restrict__ packed,
                                                           const float* __restrict__ gamma_ptr,
                                                           const int8_t* __restrict__ xq,
@@ -593,6 +610,21 @@ __global__ __launch_bounds__(kW * 64) void k_gemv_direct(const uint4* __restrict
   // wave w finishes row tiles w, w + kW, ...
   if (!has_tok) return;
   const float scale = (gamma * alpha_tok) / 127.0f;
+  if constexpr (kGlu) {
+    static_assert(kRT % 2 == 0, "gate/up tiles come in pairs");
+#pragma unroll
+    for (int p = 0; p < kRT / 2; ++p) {
+      if (p % kW != wave || 2 * p >= tiles_here) continue;
+      v4i g = partial[2 * p][0][lane], u = partial[2 * p + 1][0][lane];
+#pragma unroll
+      for (int w = 1; w < kW; ++w) {
+        add4(g, partial[2 * p][w][lane]);
+        add4(u, partial[2 * p + 1][w][lane]);
+      }
+      store_glu_tile(g, u, (tile0 / 2 + p) * kTileRows + 4 * sub, tok, n / 2, scale, y_out);
+    }
+    return;
+  }
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
     if (rt % kW != wave || rt >= tiles_here) continue;
@@ -617,7 +649,9 @@ __global__ __launch_bounds__(kW * 64) void k_gemv_direct(const uint4* __restrict
 // workgroup.  The next chunk's activations and weights are loaded into
 // registers while the current chunk is multiplied; two barriers per chunk
 // guard the single LDS buffer.  Codes become signed trits with v_perm.
-template <int kRT, int kW, int kGW, int kTB>
+// kGlu (kRT even): gate+up matrix with alternating gate/up row tiles; the
+// (tile pair, token block) items are gated into y_out ([m][n / 2]).
+template <int kRT, int kW, int kGW, int kTB, bool kGlu = false>
 __global__ __launch_bounds__(kW * 64) void k_gemv_lds(const uint4* __restrict__ packed,
                                                        const float* __restrict__ gamma_ptr,
                                                        const int8_t* __restrict__ xq,
@@ -746,6 +780,27 @@ __global__ __launch_bounds__(kW * 64) void k_gemv_lds(const uint4* __restrict__ 
       partial[((rt * kTB + tb) * kW + wave) * 64 + lane] = a;
     }
   __syncthreads();
+  auto pair_sum = [&](int rt, int tb) {
+    const int pair = rt * kTB + tb;
+    v4i sum = partial[(pair * kW) * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < kW; ++w) add4(sum, partial[(pair * kW + w) * 64 + lane]);
+    return sum;
+  };
+  if constexpr (kGlu) {
+    static_assert(kRT % 2 == 0, "gate/up tiles come in pairs");
+#pragma unroll
+    for (int p = 0; p < kRT / 2; ++p)
+#pragma unroll
+      for (int tb = 0; tb < kTB; ++tb) {
+        const int item = p * kTB + tb;
+        if (item % kW != wave || 2 * p >= tiles_here || 16 * tb + col >= rows) continue;
+        const float scale = (gamma * alpha_tok[tb]) / 127.0f;
+        store_glu_tile(pair_sum(2 * p, tb), pair_sum(2 * p + 1, tb), (tile0 / 2 + p) * kTileRows + 4 * sub,
+                       tok0 + 16 * tb + col, n / 2, scale, y_out);
+      }
+    return;
+  }
   // wave w finishes the (row tile, token block) pairs w, w + kW, ...
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt)
@@ -794,41 +849,58 @@ FusedPlan fused_plan(int64_t m, int64_t n, int64_t k) {
 constexpr int64_t kFusedMaxTokenColumns = 32767;  // m * k beyond which a block's quantization costs too much
 
 
-hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
-                       int64_t n, int64_t k, int32_t* acc, uint16_t* y, hipStream_t s) {
+namespace {
+
+// kGlu: gate+up matrix of n rows, alternating gate/up tiles; y is h [m][n / 2]
+// and every workgroup takes an even number of row tiles.
+template <bool kGlu>
+hipError_t launch_gemv_impl(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
+                            int64_t n, int64_t k, int32_t* acc, uint16_t* y, hipStream_t s) {
   if ((m + 15) / 16 > 65535) return hipErrorInvalidValue;
   const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
   const uint4* p = reinterpret_cast<const uint4*>(packed);
   if (m > 16) {
     // up to 64 tokens per workgroup: the unpacked weights serve 4 token blocks
-    const int rt = row_tiles >= 512 ? 2 : 1;
+    const int rt = kGlu || row_tiles >= 512 ? 2 : 1;
     const dim3 grid((unsigned)((row_tiles + rt - 1) / rt), (unsigned)((m + 63) / 64));
     if (rt == 2)
-      hipLaunchKernelGGL((k_gemv_lds<2, 4, 1, 4>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
+      hipLaunchKernelGGL((k_gemv_lds<2, 4, 1, 4, kGlu>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
     else
       hipLaunchKernelGGL((k_gemv_lds<1, 4, 1, 4>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
     return hipGetLastError();
   }
   if (m >= 2) {
     // two row tiles per workgroup once there are ~2 per CU
-    const int rt = row_tiles >= 512 ? 2 : 1;
+    const int rt = kGlu || row_tiles >= 512 ? 2 : 1;
     const dim3 grid((unsigned)((row_tiles + rt - 1) / rt), (unsigned)((m + 15) / 16));
     if (rt == 2)
-      hipLaunchKernelGGL((k_gemv_lds<2, 4, 4, 1>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
+      hipLaunchKernelGGL((k_gemv_lds<2, 4, 4, 1, kGlu>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
     else
       hipLaunchKernelGGL((k_gemv_lds<1, 4, 4, 1>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
     return hipGetLastError();
   }
   // one token: its activation bytes are few, so each lane loads its own
-  const int rt = row_tiles >= 2048 ? 4 : row_tiles >= 512 ? 2 : 1;
+  const int rt = row_tiles >= 2048 ? 4 : row_tiles >= 512 || kGlu ? 2 : 1;
   const dim3 grid((unsigned)((row_tiles + rt - 1) / rt), (unsigned)((m + 15) / 16));
   if (rt == 4)
-    hipLaunchKernelGGL((k_gemv_direct<4, 2, 4>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
+    hipLaunchKernelGGL((k_gemv_direct<4, 2, 4, kGlu>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
   else if (rt == 2)
-    hipLaunchKernelGGL((k_gemv_direct<2, 2, 4>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
+    hipLaunchKernelGGL((k_gemv_direct<2, 2, 4, kGlu>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
   else
     hipLaunchKernelGGL((k_gemv_direct<1, 4, 4>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
+                       int64_t n, int64_t k, int32_t* acc, uint16_t* y, hipStream_t s) {
+  return launch_gemv_impl<false>(packed, gamma, xq, alpha, m, n, k, acc, y, s);
+}
+
+hipError_t launch_gemv_glu(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
+                           int64_t f, int64_t k, uint16_t* h, hipStream_t s) {
+  return launch_gemv_impl<true>(packed, gamma, xq, alpha, m, 2 * f, k, nullptr, h, s);
 }
 
 namespace {
@@ -904,9 +976,25 @@ bool gemv_fused_applies(int64_t m, int64_t n, int64_t k) {
   return fused_plan(m, 1, k).rt > 0;
 }
 
+namespace {
+
+// Block-quantizing kernel for the gated form: two row tiles (a gate tile and
+// its up tile) per workgroup, waves as in fused_plan.
+FusedPlan fused_plan_glu(int64_t m, int64_t n, int64_t k) {
+  FusedPlan p = fused_plan(m, n, k);
+  if (p.rt == 0) return p;
+  p.rt = 2;
+  if (gemv_lds_bytes(m, k) + fused_static_lds(2, p.waves) > (size_t)kLdsBudget) return FusedPlan{};
+  return p;
+}
+
+}  // namespace
+
 bool gemv_fused_glu_applies(int64_t m, int64_t f, int64_t k) {
-  if (m < 1 || m > 4 || f < 16 || f % 16 != 0) return false;
-  return m1_config_glu(m, (k / kTileCols + 3) / 4, 2 * f / kTileRows).kernel != nullptr;
+  if (m < 1 || m > 16 || f < 16 || f % 16 != 0) return false;
+  if (m1_config_glu(m, (k / kTileCols + 3) / 4, 2 * f / kTileRows).kernel) return true;
+  if (m > 1 && m * k > kFusedMaxTokenColumns) return false;
+  return fused_plan_glu(m, 2 * f, k).rt == 2;
 }
 
 hipError_t launch_gemv_fused_glu(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t f,
@@ -915,11 +1003,26 @@ hipError_t launch_gemv_fused_glu(const uint8_t* packed, const float* gamma, cons
   const int64_t groups = (k / kTileCols + 3) / 4;
   const int64_t row_tiles = 2 * f / kTileRows;
   const M1Config c = m1_config_glu(m, groups, row_tiles);
-  const int64_t tokens = m == 1 ? 1 : 4;
-  const size_t lds = (size_t)kWaves * (size_t)((groups + kWaves - 1) / kWaves) * (size_t)tokens * 256;
-  const dim3 grid((unsigned)(row_tiles / 2));
-  hipLaunchKernelGGL(c.kernel, grid, dim3(64 * kWaves), lds, s, reinterpret_cast<const uint4*>(packed), gamma,
-                     reinterpret_cast<const uint4*>(x), alpha, xq, (int)m, (int)(2 * f), (int)k, nullptr, h);
+  const uint4* p = reinterpret_cast<const uint4*>(packed);
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  if (c.kernel) {
+    const int64_t tokens = m == 1 ? 1 : 4;
+    const size_t lds = (size_t)kWaves * (size_t)((groups + kWaves - 1) / kWaves) * (size_t)tokens * 256;
+    const dim3 grid((unsigned)(row_tiles / 2));
+    hipLaunchKernelGGL(c.kernel, grid, dim3(64 * kWaves), lds, s, p, gamma, xv, alpha, xq, (int)m, (int)(2 * f),
+                       (int)k, nullptr, h);
+    return hipGetLastError();
+  }
+  const FusedPlan fp = fused_plan_glu(m, 2 * f, k);
+  const dim3 grid((unsigned)(row_tiles / 2), (unsigned)((m + 15) / 16));
+  const size_t lds = gemv_lds_bytes(m, k);
+  const int64_t n = 2 * f;
+  if (fp.waves == 8)
+    hipLaunchKernelGGL((k_bitlinear_fused<2, 8, true>), grid, dim3(512), lds, s, p, gamma, xv, alpha, xq, m, n, k,
+                       nullptr, h);
+  else
+    hipLaunchKernelGGL((k_bitlinear_fused<2, 4, true>), grid, dim3(256), lds, s, p, gamma, xv, alpha, xq, m, n, k,
+                       nullptr, h);
   return hipGetLastError();
 }
 

@@ -45,6 +45,8 @@ hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* 
 // Squared-ReLU gated products from gate+up weights packed with alternating
 // gate/up row tiles (n = 2f rows): h[i][j] = bf16(relu(g)^2 * u), g and u the
 // rescaled products of gate row j and up row j; h is [m][f].
+hipError_t launch_gemv_glu(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
+                           int64_t f, int64_t k, uint16_t* h, hipStream_t s);
 hipError_t launch_gemm_glu(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
                            int64_t f, int64_t k, uint16_t* h, hipStream_t s);
 // One kernel for quantization + gated product, where the single-token (or

@@ -3,8 +3,9 @@ squared-ReLU gating) against the CPU oracle on the same seeded inputs.
 
 Bar: packed bytes, gamma, int8 activations and alpha bit-exact; h within one
 bf16 ulp of the oracle's exactly rounded value, exact zeros kept.  Cases cover
-the single-token kernel (one workgroup per gate/up tile pair, short and long
-rows), the few-token kernel, and every tile shape of the GEMM path, including
+every product kernel in its gated form -- the single-token and few-token
+kernels (one workgroup per gate/up tile pair), the block-quantizing kernel,
+the LDS-staged and direct products, every tile shape of the GEMM -- with
 ragged token counts, K tails and full 2B- and 70B-shaped matrices (sampled
 token rows where the oracle would take minutes).
 """
@@ -54,8 +55,14 @@ def test_pack_glu_matches_oracle(f, k):
     (1, 16, 64), (1, 48, 320), (1, 160, 2560), (1, 1280, 6912), (1, 16, 28672), (1, 80, 2624),
     # few-token kernel (short rows, few tiles)
     (2, 48, 320), (3, 160, 2560), (4, 32, 4096),
-    # quantizer + GEMM path: tokens past the fused kernels, ragged token blocks
-    (5, 48, 320), (17, 160, 640), (70, 96, 1088), (130, 272, 192), (3, 48, 6912)])
+    # block-quantizing kernel (two tiles per workgroup, four and eight waves)
+    (3, 4096, 2560), (5, 48, 320), (8, 160, 2560), (16, 48, 1024),
+    # quantizer + LDS-staged product (16- and 64-token blocks)
+    (9, 96, 6912), (17, 160, 640), (40, 96, 640), (64, 1040, 320), (3, 48, 6912),
+    # quantizer + GEMM path: past the product's token limits, ragged token blocks
+    (70, 96, 1088), (130, 272, 192),
+    # one token given as int8 (bl_linear_glu): four row tiles per workgroup, ragged last
+    (1, 16400, 64)])
 def test_bitlinear_glu_matches_oracle(m, f, k):
     rng = np.random.default_rng(m * 131 + f * 7 + k)
     w, x = glu_case(rng, f, k, m)
