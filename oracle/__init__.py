@@ -93,6 +93,12 @@ def _load():
         lib.orc_unpack_glu.restype = ctypes.c_int
         lib.orc_bitlinear_glu_forward.argtypes = [p, ctypes.c_float, p, i64, i64, i64, p, p, p, p]
         lib.orc_bitlinear_glu_forward.restype = ctypes.c_int
+        lib.orc_backward_x.argtypes = [p, ctypes.c_float, p, i64, i64, i64, p]
+        lib.orc_backward_x.restype = ctypes.c_int
+        lib.orc_backward_w.argtypes = [p, p, p, i64, i64, i64, p]
+        lib.orc_backward_w.restype = None
+        lib.orc_pack_transposed.argtypes = [p, i64, i64, p]
+        lib.orc_pack_transposed.restype = ctypes.c_int
         lib.orc_set_threads.argtypes = [ctypes.c_int]
         lib.orc_set_threads.restype = ctypes.c_int
         _lib = lib
@@ -275,6 +281,41 @@ def bitlinear_glu_forward(packed: np.ndarray, gamma, x_bf16: np.ndarray, f: int)
     if rc != 0:
         raise ValueError("k must be a multiple of 64 and f of 16")
     return h, acc, xq, alpha
+
+
+def backward_x(packed: np.ndarray, gamma, dy_bf16: np.ndarray, n: int, k: int) -> np.ndarray:
+    """Straight-through input gradient: dx[i][t] = gamma * sum_j dy[i][j] * q[j][t] (fp32 [m][k])."""
+    packed = _c(packed, np.uint8)
+    dy = _c(dy_bf16, np.uint16)
+    m = dy.shape[0]
+    assert dy.shape[1] == n
+    dx = np.empty((m, k), np.float32)
+    if _load().orc_backward_x(_p(packed), float(np.float32(gamma)), _p(dy), m, n, k, _p(dx)) != 0:
+        raise ValueError("k must be a multiple of 64")
+    return dx
+
+
+def backward_w(dy_bf16: np.ndarray, qx: np.ndarray, alpha: np.ndarray) -> np.ndarray:
+    """Straight-through weight gradient: dw[j][t] = sum_i dy[i][j] * alpha_i * qx[i][t] / 127 (fp32 [n][k])."""
+    dy = _c(dy_bf16, np.uint16)
+    qx = _c(qx, np.int8)
+    alpha = _c(alpha, np.float32)
+    m, n = dy.shape
+    k = qx.shape[1]
+    assert qx.shape[0] == m and alpha.shape == (m,)
+    dw = np.empty((n, k), np.float32)
+    _load().orc_backward_w(_p(dy), _p(qx), _p(alpha), m, n, k, _p(dw))
+    return dw
+
+
+def pack_transposed(packed: np.ndarray, n: int, k: int) -> np.ndarray:
+    """Packed q^T ([k][n], n % 64 == 0) from packed q ([n][k])."""
+    packed = _c(packed, np.uint8)
+    out = np.empty(packed_bytes(k, n), np.uint8)
+    rc = _load().orc_pack_transposed(_p(packed), n, k, _p(out))
+    if rc != 0:
+        raise ValueError(f"orc_pack_transposed failed ({rc})")
+    return out
 
 
 def set_threads(n: int = 0) -> int:

@@ -478,6 +478,80 @@ int orc_bitlinear_glu_forward(const uint8_t* packed, float gamma, const uint16_t
     return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Straight-through backward of the BitLinear.                               */
+/* ------------------------------------------------------------------------ */
+/*
+ * Source: bako.co, "BitNet b1.58 and the 1-Bit AI Architecture Revolution",
+ * section "Training Dynamics: The Straight-Through Estimator": the backward
+ * pass treats the rounding step as the identity, so gradients pass through
+ * the quantized weights to high-precision shadow weights, which are
+ * re-quantized at the next forward pass.
+ * Readings: both quantizers (weights and activations, rounding and clipping)
+ * are the identity in the backward pass and their scales (gamma, alpha) are
+ * constants.  The forward in dequantized form is y = xhat * What^T with
+ * xhat[i][t] = alpha_i / 127 * qx[i][t] and What[j][t] = gamma * q[j][t], so
+ *   dx[i][t] = gamma * sum_j dy[i][j] * q[j][t]          (gradient for x)
+ *   dw[j][t] = sum_i dy[i][j] * alpha_i * qx[i][t] / 127  (gradient for the
+ *                                                          shadow weights)
+ * dy is bf16 [m][n]; dx [m][k] and dw [n][k] are fp32, each evaluated in
+ * binary64 and rounded once.
+ */
+static double bf16_to_double(uint16_t h) { return (double)bf16_bits_to_float(h); }
+
+/* dx from packed weights (the layout of orc_pack). */
+int orc_backward_x(const uint8_t* packed, float gamma, const uint16_t* dy, int64_t m, int64_t n, int64_t k,
+                   float* dx) {
+    if (k % 64 != 0) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; ++i) {
+        for (int64_t t = 0; t < k; ++t) {
+            double s = 0.0;
+            for (int64_t j = 0; j < n; ++j) {
+                int64_t byte;
+                int bit;
+                trit_position(j, t, k, &byte, &bit);
+                int w = (int)((packed[byte] >> bit) & 3u) - 1;
+                s += (double)w * bf16_to_double(dy[i * n + j]);
+            }
+            dx[i * k + t] = (float)((double)gamma * s);
+        }
+    }
+    return 0;
+}
+
+/* dw from the int8 activations and their per-token absmax. */
+void orc_backward_w(const uint16_t* dy, const int8_t* qx, const float* alpha, int64_t m, int64_t n, int64_t k,
+                    float* dw) {
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < n; ++j) {
+        for (int64_t t = 0; t < k; ++t) {
+            double s = 0.0;
+            for (int64_t i = 0; i < m; ++i)
+                s += bf16_to_double(dy[i * n + j]) * (double)alpha[i] * (double)qx[i * k + t];
+            dw[j * k + t] = (float)(s / 127.0);
+        }
+    }
+}
+
+/* The packed form of q^T ([k][n], n % 64 == 0) from the packed form of q
+ * ([n][k]): the layout the backward product reads, since it contracts over
+ * the rows of q. */
+int orc_pack_transposed(const uint8_t* packed, int64_t n, int64_t k, uint8_t* packed_t) {
+    if (k % 64 != 0 || n % 64 != 0) return -1;
+    int8_t* q = (int8_t*)malloc((size_t)(n * k > 0 ? n * k : 1));
+    int8_t* qt = (int8_t*)malloc((size_t)(n * k > 0 ? n * k : 1));
+    int rc = (q && qt) ? orc_unpack(packed, n, k, q) : -1;
+    if (rc == 0) {
+        for (int64_t j = 0; j < n; ++j)
+            for (int64_t t = 0; t < k; ++t) qt[t * n + j] = q[j * k + t];
+        rc = orc_pack(qt, k, n, packed_t);
+    }
+    free(q);
+    free(qt);
+    return rc;
+}
+
 /* Thread count of the OpenMP loops above (results never depend on it; the
  * benchmark's CPU-baseline leg times the oracle at one thread and at all). */
 int orc_set_threads(int n) {

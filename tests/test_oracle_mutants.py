@@ -15,7 +15,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 PINS = [os.path.join(ROOT, "tests", "test_oracle_absmean.py"),
         os.path.join(ROOT, "tests", "test_oracle_act_linear.py"),
-        os.path.join(ROOT, "tests", "test_oracle_glu.py")]
+        os.path.join(ROOT, "tests", "test_oracle_glu.py"),
+        os.path.join(ROOT, "tests", "test_oracle_backward.py")]
 
 MUTANTS = {
     "ternarize_round_half_away": ("float r = rintf(scaled);", "float r = roundf(scaled);"),
@@ -50,6 +51,14 @@ MUTANTS = {
                            "return (tile % 2 == 0 ? f : 0) + 16 * (tile / 2) + r;"),
     "glu_up_from_gate_row": ("double u = (double)acc[i * 2 * f + f + j] * s;",
                              "double u = (double)acc[i * 2 * f + j] * s;"),
+    "backward_x_no_gamma": ("dx[i * k + t] = (float)((double)gamma * s);", "dx[i * k + t] = (float)s;"),
+    "backward_x_untransposed": ("                trit_position(j, t, k, &byte, &bit);\n                int w = (int)((packed[byte] >> bit) & 3u) - 1;\n                s += (double)w * bf16_to_double(dy[i * n + j]);",
+                                "                trit_position(t % n, j % k, k, &byte, &bit);\n                int w = (int)((packed[byte] >> bit) & 3u) - 1;\n                s += (double)w * bf16_to_double(dy[i * n + j]);"),
+    "backward_w_no_alpha": ("s += bf16_to_double(dy[i * n + j]) * (double)alpha[i] * (double)qx[i * k + t];",
+                            "s += bf16_to_double(dy[i * n + j]) * (double)qx[i * k + t];"),
+    "backward_w_128": ("dw[j * k + t] = (float)(s / 127.0);", "dw[j * k + t] = (float)(s / 128.0);"),
+    "pack_transposed_not_transposed": ("for (int64_t t = 0; t < k; ++t) qt[t * n + j] = q[j * k + t];",
+                                       "for (int64_t t = 0; t < k; ++t) qt[j * k + t] = q[j * k + t];"),
     "unpack_codes_not_trits": ("q[row * k + col] = (int8_t)((int)((packed[byte] >> bit) & 3u) - 1);",
                                "q[row * k + col] = (int8_t)((int)((packed[byte] >> bit) & 3u));"),
 }
