@@ -56,6 +56,7 @@ extern "C" {
 #define BL_MAX_K (1 << 22)
 #define BL_MAX_M (1 << 24)
 #define BL_MAX_N (1 << 30)
+#define BL_MAX_BACKWARD_N (1 << 24)
 
 typedef enum {
     BL_OK = 0,
@@ -173,6 +174,36 @@ bl_status bl_linear_glu(const uint8_t* packed, const float* gamma, const int8_t*
  * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_HIP. */
 bl_status bl_bitlinear_glu(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t f,
                            int64_t k, int8_t* xq, float* alpha, uint16_t* h, void* stream);
+
+/* ---- Straight-through backward ----
+ * [P1], section "Training Dynamics: The Straight-Through Estimator": the
+ * backward pass treats the rounding step as the identity, so gradients pass
+ * through the quantized weights to full-precision shadow weights, which are
+ * ternarized again at the next forward pass (bl_ternarize_pack).  Both
+ * quantizers are the identity in the backward pass and gamma, alpha are
+ * constants; with the dequantized forward y = xhat What^T (xhat = alpha / 127
+ * * xq, What = gamma * q):
+ *   dx[i][t] = gamma * sum_j dy[i][j] * q[j][t]
+ *   dw[j][t] = sum_i dy[i][j] * alpha[i] * xq[i][t] / 127
+ * dy is bf16 [m][n]; dx and dw are fp32, accumulated in fp32 in any order
+ * (within (n + 2) * 2^-24 * sum |terms| of the exact value for dx). */
+
+/* The packed form of q^T ([k][n], the layout of bl_ternarize_pack with rows t
+ * and columns j) from the packed form of q ([n][k]): the operand of
+ * bl_bitlinear_backward_x, which contracts over the rows of q.  n must be a
+ * positive multiple of 64; packed_t has bl_packed_bytes(k, n) bytes.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_HIP. */
+bl_status bl_pack_transposed(const uint8_t* packed, int64_t n, int64_t k, uint8_t* packed_t, void* stream);
+
+/* Input gradient dx = gamma * dy q.
+ *   packed_t  from bl_pack_transposed of the layer's packed weights; gamma
+ *             the layer's gamma (device).
+ *   dy        [m][n] bf16 bit patterns (16-byte aligned).
+ *   dx        out [m][k] fp32.
+ * n must be a multiple of 64 and at most BL_MAX_BACKWARD_N (2^24).
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_HIP. */
+bl_status bl_bitlinear_backward_x(const uint8_t* packed_t, const float* gamma, const uint16_t* dy, int64_t m,
+                                  int64_t n, int64_t k, float* dx, void* stream);
 
 /* Unpack a packed buffer back to trits (test and inspection helper [P2]):
  * q[j][t] in {-1, 0, 1} for the n real rows.  A code 3 (never produced by

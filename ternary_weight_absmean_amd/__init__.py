@@ -21,7 +21,7 @@ from ._build import LIB_PATH, INCLUDE
 __all__ = [
     "BitLinearError", "bl_packed_bytes", "bl_ternarize_pack_workspace_bytes", "bl_ternarize_pack",
     "bl_quant_act", "bl_linear", "bl_bitlinear", "bl_unpack_ternary", "bl_status_string", "library", "declared_symbols",
-    "bl_ternarize_pack_glu", "bl_linear_glu", "bl_bitlinear_glu",
+    "bl_ternarize_pack_glu", "bl_linear_glu", "bl_bitlinear_glu", "bl_pack_transposed", "bl_bitlinear_backward_x",
 ]
 
 
@@ -57,6 +57,10 @@ _lib.bl_linear_glu.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P]
 _lib.bl_linear_glu.restype = ctypes.c_int
 _lib.bl_bitlinear_glu.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P]
 _lib.bl_bitlinear_glu.restype = ctypes.c_int
+_lib.bl_pack_transposed.argtypes = [_P, _I64, _I64, _P, _P]
+_lib.bl_pack_transposed.restype = ctypes.c_int
+_lib.bl_bitlinear_backward_x.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P, _P]
+_lib.bl_bitlinear_backward_x.restype = ctypes.c_int
 _lib.bl_unpack_ternary.restype = ctypes.c_int
 _lib.bl_status_string.argtypes = [ctypes.c_int]
 _lib.bl_status_string.restype = ctypes.c_char_p
@@ -262,6 +266,34 @@ def bl_bitlinear_glu(packed: torch.Tensor, gamma: torch.Tensor, x: torch.Tensor,
     _check("bl_bitlinear_glu", _lib.bl_bitlinear_glu(_ptr(packed), _ptr(gamma), _ptr(x), m, f, k, _ptr(xq),
                                                      _ptr(alpha), _ptr(h), _stream(dev)))
     return h, xq, alpha
+
+
+def bl_pack_transposed(packed: torch.Tensor, n: int, k: int, packed_t: torch.Tensor | None = None) -> torch.Tensor:
+    """Packed q ``[n][k]`` -> packed q^T ``[k][n]`` (n % 64 == 0)."""
+    _need(packed, "packed", torch.uint8)
+    if packed.numel() < bl_packed_bytes(n, k):
+        raise ValueError("packed buffer is smaller than bl_packed_bytes(n, k)")
+    if packed_t is None:
+        packed_t = torch.empty(max(bl_packed_bytes(k, n), 1), dtype=torch.uint8, device=packed.device)
+    _check("bl_pack_transposed", _lib.bl_pack_transposed(_ptr(packed), n, k, _ptr(packed_t), _stream(packed.device)))
+    return packed_t
+
+
+def bl_bitlinear_backward_x(packed_t: torch.Tensor, gamma: torch.Tensor, dy: torch.Tensor, k: int,
+                            dx: torch.Tensor | None = None) -> torch.Tensor:
+    """Straight-through input gradient: dx fp32 [m][k] = gamma * dy q, from
+    packed q^T (bl_pack_transposed) and dy bf16 [m][n]."""
+    _need(dy, "dy", torch.bfloat16)
+    m, n = dy.shape
+    if dx is None:
+        dx = torch.empty((m, k), dtype=torch.float32, device=dy.device)
+    _need(dx, "dx", torch.float32, (m, k))
+    _need(packed_t, "packed_t", torch.uint8)
+    if packed_t.numel() < bl_packed_bytes(k, n):
+        raise ValueError("packed_t buffer is smaller than bl_packed_bytes(k, n)")
+    _check("bl_bitlinear_backward_x", _lib.bl_bitlinear_backward_x(_ptr(packed_t), _ptr(gamma), _ptr(dy), m, n, k,
+                                                                   _ptr(dx), _stream(dy.device)))
+    return dx
 
 
 def bl_unpack_ternary(packed: torch.Tensor, n: int, k: int, q: torch.Tensor | None = None) -> torch.Tensor:

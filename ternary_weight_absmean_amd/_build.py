@@ -10,7 +10,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libbitlinear.so")
-SOURCES = ["abi.hip", "pack.hip", "quant.hip", "gemv.hip", "gemm.hip"]
+SOURCES = ["abi.hip", "pack.hip", "quant.hip", "gemv.hip", "gemm.hip", "backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

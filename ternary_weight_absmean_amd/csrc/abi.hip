@@ -141,6 +141,24 @@ bl_status bl_bitlinear_glu(const uint8_t* packed, const float* gamma, const uint
   return from_hip(bl::launch_gemm_glu(packed, gamma, xq, alpha, m, f, k, h, s));
 }
 
+bl_status bl_pack_transposed(const uint8_t* packed, int64_t n, int64_t k, uint8_t* packed_t, void* stream) {
+  if (n < 64 || n % 64 != 0 || n > BL_MAX_N || !valid_k(k) || !product_ok(n + 16, k)) return BL_ERR_SHAPE;
+  if (!packed || !packed_t) return BL_ERR_NULL;
+  if (!aligned(packed, 16) || !aligned(packed_t, 16)) return BL_ERR_ALIGN;
+  return from_hip(bl::launch_pack_transposed(packed, n, k, packed_t, (hipStream_t)stream));
+}
+
+bl_status bl_bitlinear_backward_x(const uint8_t* packed_t, const float* gamma, const uint16_t* dy, int64_t m,
+                                  int64_t n, int64_t k, float* dx, void* stream) {
+  if (m < 0 || m > BL_MAX_M || n < 64 || n % 64 != 0 || n > BL_MAX_BACKWARD_N || !valid_k(k) || !product_ok(m, n) ||
+      !product_ok(m, k) || !product_ok(n + 16, k))
+    return BL_ERR_SHAPE;
+  if (m == 0) return BL_OK;
+  if (!packed_t || !gamma || !dy || !dx) return BL_ERR_NULL;
+  if (!aligned(packed_t, 16) || !aligned(gamma, 4) || !aligned(dy, 16) || !aligned(dx, 4)) return BL_ERR_ALIGN;
+  return from_hip(bl::launch_backward_x(packed_t, gamma, dy, m, n, k, dx, (hipStream_t)stream));
+}
+
 bl_status bl_unpack_ternary(const uint8_t* packed, int64_t n, int64_t k, int8_t* q, void* stream) {
   if (n < 0 || n > BL_MAX_N || !valid_k(k) || !product_ok(n + 16, k)) return BL_ERR_SHAPE;
   if (n == 0) return BL_OK;

@@ -42,7 +42,6 @@ namespace bl {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
 constexpr int kGroupsPerBatch = 4;
 constexpr int kLdsBudget = 163840;  // LDS per workgroup (and per CU) on gfx950
 constexpr int kLdsRowPad = 16;          // row stride k + 16 bytes spreads the 16 token rows over the banks

@@ -22,6 +22,11 @@ hipError_t launch_gamma_fold(const unsigned long long* ws, int64_t count, float*
 // alternating gate/up 16-row tiles (n == 2 * glu_f, glu_f % 16 == 0).
 hipError_t launch_ternarize_pack(const float* w, int64_t n, int64_t k, const float* gamma, uint8_t* packed,
                                  hipStream_t s, int64_t glu_f = 0);
+// Packed q^T ([k][n]) from packed q ([n][k]); n % 64 == 0.
+hipError_t launch_pack_transposed(const uint8_t* packed, int64_t n, int64_t k, uint8_t* packed_t, hipStream_t s);
+// Straight-through backward: dx = gamma * dy q from packed q^T; dw = dy^T (alpha / 127 qx).
+hipError_t launch_backward_x(const uint8_t* packed_t, const float* gamma, const uint16_t* dy, int64_t m, int64_t n,
+                             int64_t k, float* dx, hipStream_t s);
 hipError_t launch_unpack(const uint8_t* packed, int64_t n, int64_t k, int8_t* q, hipStream_t s);
 
 // Per-token absmax int8 quantizer.

@@ -279,6 +279,37 @@ __global__ __launch_bounds__(kPackThreads) void k_ternarize_pack(const float4* _
   if (j < 4) packed[(((prow / kTileRows) * (k / kTileCols) + kt) * kTileRows + (prow % kTileRows)) * 4 + j] = part;
 }
 
+// Packed q^T ([k][n]) from packed q ([n][k]), n % 64 == 0.  A workgroup
+// turns the 64 x 64 trit block of q at rows 64 bj.., columns 64 bt.. (row
+// tiles 4 bj..4 bj + 3 of column tile bt, 1 KiB) into the block of q^T at rows
+// 64 bt.., columns 64 bj.. (row tiles 4 bt.. of column tile bj), through LDS as
+// one code per byte.  Thread d of each 64 reads and writes dword d of one
+// 256-byte tile: row d / 4, bytes 4 (d % 4)..+3, i.e. columns 16 f + 4 (d % 4) + i.
+__global__ __launch_bounds__(256) void k_pack_transposed(const uint32_t* __restrict__ packed, int64_t n, int64_t k,
+                                                         uint32_t* __restrict__ packed_t) {
+  __shared__ uint8_t codes[64][64 + 4];  // [row of q in the block][column of q in the block]
+  const int tid = threadIdx.x;
+  const int64_t col_blocks = k / 64;
+  const int64_t bj = (int64_t)blockIdx.x / col_blocks;
+  const int64_t bt = (int64_t)blockIdx.x % col_blocks;
+  const int s = tid >> 6, d = tid & 63;
+  const int r = 16 * s + d / 4, b0 = 4 * (d % 4);
+  const uint32_t w = packed[((4 * bj + s) * col_blocks + bt) * 64 + d];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) codes[r][16 * f + b0 + i] = (uint8_t)((w >> (8 * i + 2 * f)) & 3u);
+  __syncthreads();
+  // row r of the q^T block is column r of the q block; its byte b0 + i, field
+  // f holds column 16 f + b0 + i of q^T = row 16 f + b0 + i of q
+  uint32_t out = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) out |= (uint32_t)codes[16 * f + b0 + i][r] << (8 * i + 2 * f);
+  packed_t[((4 * bt + s) * (n / 64) + bj) * 64 + d] = out;
+}
+
 __global__ __launch_bounds__(kPackThreads) void k_unpack(const uint4* __restrict__ packed, int64_t n, int64_t k,
                                                           int8_t* __restrict__ q) {
   const int64_t kt_count = k / kTileCols;
@@ -324,6 +355,14 @@ hipError_t launch_ternarize_pack(const float* w, int64_t n, int64_t k, const flo
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_ternarize_pack, dim3((unsigned)blocks), dim3(kPackThreads), 0, s,
                      reinterpret_cast<const float4*>(w), n, k, gamma, reinterpret_cast<uint32_t*>(packed), glu_f);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_transposed(const uint8_t* packed, int64_t n, int64_t k, uint8_t* packed_t, hipStream_t s) {
+  const int64_t blocks = (n / 64) * (k / 64);
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_pack_transposed, dim3((unsigned)blocks), dim3(256), 0, s,
+                     reinterpret_cast<const uint32_t*>(packed), n, k, reinterpret_cast<uint32_t*>(packed_t));
   return hipGetLastError();
 }
 

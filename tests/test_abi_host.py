@@ -156,3 +156,18 @@ def test_glu_entry_points_validation():
     assert bit(FAKE, FAKE, FAKE, 1, 17, 64, FAKE, FAKE, FAKE, None) == BL_ERR_SHAPE
     assert bit(FAKE, FAKE, FAKE, -1, 16, 64, FAKE, FAKE, FAKE, None) == BL_ERR_SHAPE
     assert bit(FAKE, FAKE, FAKE + 4, 1, 16, 64, FAKE, FAKE, FAKE, None) == BL_ERR_ALIGN
+
+
+def test_backward_entry_points_validation():
+    tr = lib.bl_pack_transposed
+    assert tr(FAKE, 32, 64, FAKE, None) == BL_ERR_SHAPE      # n not a multiple of 64
+    assert tr(FAKE, 64, 96, FAKE, None) == BL_ERR_SHAPE
+    assert tr(None, 64, 64, FAKE, None) == BL_ERR_NULL
+    assert tr(FAKE + 4, 64, 64, FAKE, None) == BL_ERR_ALIGN
+    bx = lib.bl_bitlinear_backward_x
+    assert bx(FAKE, FAKE, FAKE, 0, 64, 64, FAKE, None) == BL_OK          # empty
+    assert bx(FAKE, FAKE, FAKE, 1, 96, 64, FAKE, None) == BL_ERR_SHAPE   # n % 64
+    assert bx(FAKE, FAKE, FAKE, 1, (1 << 24) + 64, 64, FAKE, None) == BL_ERR_SHAPE
+    assert bx(FAKE, FAKE, None, 1, 64, 64, FAKE, None) == BL_ERR_NULL
+    assert bx(FAKE, FAKE, FAKE + 2, 1, 64, 64, FAKE, None) == BL_ERR_ALIGN
+    assert bx(FAKE, FAKE, FAKE, 1, 64, 64, FAKE + 2, None) == BL_ERR_ALIGN
