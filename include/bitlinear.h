@@ -205,6 +205,25 @@ bl_status bl_pack_transposed(const uint8_t* packed, int64_t n, int64_t k, uint8_
 bl_status bl_bitlinear_backward_x(const uint8_t* packed_t, const float* gamma, const uint16_t* dy, int64_t m,
                                   int64_t n, int64_t k, float* dx, void* stream);
 
+/* Device workspace of bl_bitlinear_backward_w: 2 * (2n + k) * ceil(m/64)*64
+ * bytes (the gradient, scaled by alpha and split into two bf16 parts, and the
+ * int8 activations as bf16, both stored token-contiguous).  Returns 0 for an
+ * invalid shape. */
+size_t bl_backward_w_workspace_bytes(int64_t m, int64_t n, int64_t k);
+
+/* Weight gradient for the shadow weights: dw[j][t] = sum_i dy[i][j] *
+ * alpha[i] * xq[i][t] / 127.  alpha[i] * dy[i][j] (two bf16 values) is split
+ * exactly into two bf16 parts, so every product is exact; the sums are fp32.
+ *   dy         [m][n] bf16 bit patterns; xq [m][k] int8 and alpha [m] fp32 as
+ *              written by bl_quant_act / bl_bitlinear for the layer's input.
+ *   dw         out [n][k] fp32 (overwritten; zero for m = 0).
+ *   workspace  device scratch of workspace_bytes >= bl_backward_w_workspace_bytes;
+ *              contents on entry do not matter and are clobbered.
+ * n must be a multiple of 64 and at most BL_MAX_BACKWARD_N.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_WORKSPACE, BL_ERR_HIP. */
+bl_status bl_bitlinear_backward_w(const uint16_t* dy, const int8_t* xq, const float* alpha, int64_t m, int64_t n,
+                                  int64_t k, float* dw, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Unpack a packed buffer back to trits (test and inspection helper [P2]):
  * q[j][t] in {-1, 0, 1} for the n real rows.  A code 3 (never produced by
  * bl_ternarize_pack) decodes as 0.

@@ -22,6 +22,7 @@ __all__ = [
     "BitLinearError", "bl_packed_bytes", "bl_ternarize_pack_workspace_bytes", "bl_ternarize_pack",
     "bl_quant_act", "bl_linear", "bl_bitlinear", "bl_unpack_ternary", "bl_status_string", "library", "declared_symbols",
     "bl_ternarize_pack_glu", "bl_linear_glu", "bl_bitlinear_glu", "bl_pack_transposed", "bl_bitlinear_backward_x",
+    "bl_backward_w_workspace_bytes", "bl_bitlinear_backward_w",
 ]
 
 
@@ -61,6 +62,10 @@ _lib.bl_pack_transposed.argtypes = [_P, _I64, _I64, _P, _P]
 _lib.bl_pack_transposed.restype = ctypes.c_int
 _lib.bl_bitlinear_backward_x.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P, _P]
 _lib.bl_bitlinear_backward_x.restype = ctypes.c_int
+_lib.bl_backward_w_workspace_bytes.argtypes = [_I64, _I64, _I64]
+_lib.bl_backward_w_workspace_bytes.restype = _SZ
+_lib.bl_bitlinear_backward_w.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _P]
+_lib.bl_bitlinear_backward_w.restype = ctypes.c_int
 _lib.bl_unpack_ternary.restype = ctypes.c_int
 _lib.bl_status_string.argtypes = [ctypes.c_int]
 _lib.bl_status_string.restype = ctypes.c_char_p
@@ -294,6 +299,30 @@ def bl_bitlinear_backward_x(packed_t: torch.Tensor, gamma: torch.Tensor, dy: tor
     _check("bl_bitlinear_backward_x", _lib.bl_bitlinear_backward_x(_ptr(packed_t), _ptr(gamma), _ptr(dy), m, n, k,
                                                                    _ptr(dx), _stream(dy.device)))
     return dx
+
+
+def bl_backward_w_workspace_bytes(m: int, n: int, k: int) -> int:
+    return int(_lib.bl_backward_w_workspace_bytes(m, n, k))
+
+
+def bl_bitlinear_backward_w(dy: torch.Tensor, xq: torch.Tensor, alpha: torch.Tensor, dw: torch.Tensor | None = None,
+                            workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Straight-through weight gradient: dw fp32 [n][k] = dy^T (alpha / 127 xq)."""
+    _need(dy, "dy", torch.bfloat16)
+    _need(xq, "xq", torch.int8)
+    m, n = dy.shape
+    k = xq.shape[1]
+    _need(alpha, "alpha", torch.float32, (m,))
+    if dw is None:
+        dw = torch.empty((n, k), dtype=torch.float32, device=dy.device)
+    _need(dw, "dw", torch.float32, (n, k))
+    ws = bl_backward_w_workspace_bytes(m, n, k)
+    if workspace is None:
+        workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=dy.device)
+    _check("bl_bitlinear_backward_w", _lib.bl_bitlinear_backward_w(_ptr(dy), _ptr(xq), _ptr(alpha), m, n, k, _ptr(dw),
+                                                                   _ptr(workspace), workspace.numel(),
+                                                                   _stream(dy.device)))
+    return dw
 
 
 def bl_unpack_ternary(packed: torch.Tensor, n: int, k: int, q: torch.Tensor | None = None) -> torch.Tensor:

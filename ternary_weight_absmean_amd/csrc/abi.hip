@@ -159,6 +159,27 @@ bl_status bl_bitlinear_backward_x(const uint8_t* packed_t, const float* gamma, c
   return from_hip(bl::launch_backward_x(packed_t, gamma, dy, m, n, k, dx, (hipStream_t)stream));
 }
 
+size_t bl_backward_w_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  if (m < 1 || m > BL_MAX_M || n < 64 || n % 64 != 0 || n > BL_MAX_BACKWARD_N || !valid_k(k) || !product_ok(m + 64, n) ||
+      !product_ok(m + 64, k))
+    return 0;
+  return bl::backward_w_workspace_bytes(m, n, k);
+}
+
+bl_status bl_bitlinear_backward_w(const uint16_t* dy, const int8_t* xq, const float* alpha, int64_t m, int64_t n,
+                                  int64_t k, float* dw, void* workspace, size_t workspace_bytes, void* stream) {
+  if (m < 0 || m > BL_MAX_M || n < 64 || n % 64 != 0 || n > BL_MAX_BACKWARD_N || !valid_k(k) || !product_ok(m + 64, n) ||
+      !product_ok(m + 64, k) || !product_ok(n, k))
+    return BL_ERR_SHAPE;
+  if (!dy && m > 0) return BL_ERR_NULL;
+  if (!dw || (m > 0 && (!xq || !alpha || !workspace))) return BL_ERR_NULL;
+  if (!aligned(dy, 2) || !aligned(alpha, 4) || !aligned(dw, 4) || !aligned(workspace, 16)) return BL_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  if (m == 0) return from_hip(bl::launch_fill_zero(dw, n * k, s));  // empty sum
+  if (workspace_bytes < bl::backward_w_workspace_bytes(m, n, k)) return BL_ERR_WORKSPACE;
+  return from_hip(bl::launch_backward_w(dy, xq, alpha, m, n, k, dw, workspace, s));
+}
+
 bl_status bl_unpack_ternary(const uint8_t* packed, int64_t n, int64_t k, int8_t* q, void* stream) {
   if (n < 0 || n > BL_MAX_N || !valid_k(k) || !product_ok(n + 16, k)) return BL_ERR_SHAPE;
   if (n == 0) return BL_OK;

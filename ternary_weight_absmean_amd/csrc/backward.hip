@@ -1,4 +1,4 @@
-// Straight-through backward of the BitLinear: the input gradient.
+// Straight-through backward of the BitLinear: input and weight gradients.
 //
 // bako.co, "BitNet b1.58 and the 1-Bit AI Architecture Revolution", section
 // "Training Dynamics: The Straight-Through Estimator": the backward pass
@@ -25,6 +25,17 @@
 //     c ^ (r % 16), so the 16 tokens of a B read fall in distinct banks.
 // Tails: rows of q^T past k and tokens past m are never stored; columns past
 // n read as zero gradient (and the trits there are multiplied by zero).
+//
+// The weight gradient dw[j][t] = sum_i alpha_i dy[i][j] xq[i][t] / 127
+// contracts over the tokens, the row index of both inputs, so a preparation
+// kernel first writes them token-contiguous into the caller's workspace:
+// a = alpha_i * dy[i][j] (a product of two bf16 values: 16 significant bits,
+// exact in fp32) split into a_hi = bf16(a) and a_lo = a - a_hi (at most 8
+// significant bits: exact in bf16), transposed to [n][m_pad]; and xq
+// converted to bf16 (exact) and transposed to [k][m_pad]; tokens past m are
+// zero.  k_bwd_w then runs two bf16 MFMAs per tile pair (a_hi and a_lo with
+// the same xq), so every product is exact and only the fp32 accumulation
+// order differs from the exact sum; the sum is divided by 127 at the end.
 #include "device_util.h"
 #include "internal.h"
 
@@ -196,6 +207,149 @@ __global__ __launch_bounds__(256, 2) void k_bwd_x(const uint8_t* __restrict__ pa
   }
 }
 
+constexpr int kPrepTile = 64;
+
+// One 64 x 64 block of the workspace per workgroup.  Blocks [0, nb) take
+// gradient columns j (a_hi and a_lo rows), the rest the activation columns t.
+__global__ __launch_bounds__(256) void k_bwd_w_prep(const uint16_t* __restrict__ dy, const int8_t* __restrict__ xq,
+                                                    const float* __restrict__ alpha, int64_t m, int64_t n, int64_t k,
+                                                    int64_t m_pad, uint16_t* __restrict__ a_hi,
+                                                    uint16_t* __restrict__ a_lo, uint16_t* __restrict__ x_t) {
+  __shared__ uint16_t hi_s[kPrepTile][kPrepTile + 2];
+  __shared__ uint16_t lo_s[kPrepTile][kPrepTile + 2];
+  const int tid = threadIdx.x;
+  const int64_t token_blocks = m_pad / kPrepTile;
+  const int64_t nb = (n / kPrepTile) * token_blocks;
+  const bool grad = (int64_t)blockIdx.x < nb;
+  const int64_t b = grad ? (int64_t)blockIdx.x : (int64_t)blockIdx.x - nb;
+  const int64_t c0 = (b / token_blocks) * kPrepTile;  // first column (j or t)
+  const int64_t i0 = (b % token_blocks) * kPrepTile;  // first token
+  // read: thread -> (token row, 16 consecutive columns), 4 rows per pass
+  const int rr = tid >> 2, cc = 16 * (tid & 3);
+  const int64_t i = i0 + rr;
+  if (grad) {
+    const float al = i < m ? alpha[i] : 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      uint16_t h = 0, l = 0;
+      if (i < m) {
+        const float a = __uint_as_float((uint32_t)dy[i * n + c0 + cc + e] << 16) * al;  // exact
+        h = f32_to_bf16_rne(a);
+        l = (uint16_t)(__float_as_uint(a - __uint_as_float((uint32_t)h << 16)) >> 16);  // exact
+      }
+      hi_s[rr][cc + e] = h;
+      lo_s[rr][cc + e] = l;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float v = i < m ? (float)xq[i * k + c0 + cc + e] : 0.0f;
+      hi_s[rr][cc + e] = (uint16_t)(__float_as_uint(v) >> 16);  // |v| <= 128: exact in bf16
+    }
+  }
+  __syncthreads();
+  // write: thread -> (column, 16 consecutive tokens) of the transposed block
+  const int wc = tid >> 2, wt = 16 * (tid & 3);
+  uint16_t* dst = grad ? a_hi : x_t;
+  uint32_t h8[8], l8[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h8[e] = (uint32_t)hi_s[wt + 2 * e][wc] | ((uint32_t)hi_s[wt + 2 * e + 1][wc] << 16);
+    l8[e] = (uint32_t)lo_s[wt + 2 * e][wc] | ((uint32_t)lo_s[wt + 2 * e + 1][wc] << 16);
+  }
+  const int64_t off = (c0 + wc) * m_pad + i0 + wt;
+  *reinterpret_cast<uint4*>(dst + off) = make_uint4(h8[0], h8[1], h8[2], h8[3]);
+  *reinterpret_cast<uint4*>(dst + off + 8) = make_uint4(h8[4], h8[5], h8[6], h8[7]);
+  if (grad) {
+    *reinterpret_cast<uint4*>(a_lo + off) = make_uint4(l8[0], l8[1], l8[2], l8[3]);
+    *reinterpret_cast<uint4*>(a_lo + off + 8) = make_uint4(l8[4], l8[5], l8[6], l8[7]);
+  }
+}
+
+constexpr int kWStep = 32;           // tokens per step (one MFMA)
+constexpr int kWPitch = kWStep + 8;  // LDS row pitch in bf16: 80 bytes, the 16 rows of a read in distinct banks
+
+// dw = (a_hi + a_lo) x_t^T / 127 over the token-contiguous workspace.  A
+// workgroup (2 x 2 waves) owns 128 rows j x 128 columns t; a wave 64 x 64 =
+// 4 x 4 tiles, two MFMAs per tile per step (a_hi, a_lo).  The three operand
+// tiles (128 x 32 tokens each) go through LDS via registers, double-buffered.
+__global__ __launch_bounds__(256, 2) void k_bwd_w(const uint16_t* __restrict__ a_hi, const uint16_t* __restrict__ a_lo,
+                                                  const uint16_t* __restrict__ x_t, int64_t m_pad, int64_t n,
+                                                  int64_t k, int64_t blocks_t, float* __restrict__ dw) {
+  __shared__ uint4 sh[2][3][128 * kWPitch / 8];  // [buffer][a_hi, a_lo, x_t][row * pitch]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wj = wave >> 1, wt = wave & 1;
+  const int sub = lane >> 4, col = lane & 15;
+  const int64_t j0 = ((int64_t)blockIdx.x / blocks_t) * 128;
+  const int64_t t0 = ((int64_t)blockIdx.x % blocks_t) * 128;
+  const int steps = (int)(m_pad / kWStep);
+  // staging: each operand tile is 128 rows x 64 bytes = 512 pieces of 16 bytes; thread -> pieces tid, tid + 256
+  const int pr0 = tid >> 2, pc = tid & 3;
+  const int rows_j = (int)min((int64_t)128, n - j0), rows_t = (int)min((int64_t)128, k - t0);
+  auto load = [&](int s, uint4 (&v)[3][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = pr0 + 64 * h;
+      const int64_t tok = (int64_t)s * kWStep + 8 * pc;
+      v[0][h] = r < rows_j ? *reinterpret_cast<const uint4*>(a_hi + (j0 + r) * m_pad + tok) : make_uint4(0, 0, 0, 0);
+      v[1][h] = r < rows_j ? *reinterpret_cast<const uint4*>(a_lo + (j0 + r) * m_pad + tok) : make_uint4(0, 0, 0, 0);
+      v[2][h] = r < rows_t ? *reinterpret_cast<const uint4*>(x_t + (t0 + r) * m_pad + tok) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store = [&](int buf, const uint4 (&v)[3][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int o = 0; o < 3; ++o)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) sh[buf][o][((pr0 + 64 * h) * kWPitch + 8 * pc) / 8] = v[o][h];
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint4 v[3][2];
+  load(0, v);
+  store(0, v);
+  __syncthreads();
+  for (int s = 0; s < steps; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < steps) load(s + 1, v);
+    // operands: lane (row col, token group sub) -> 8 tokens 8 sub..8 sub + 7 of its row
+    uint4 bt[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) bt[b] = sh[buf][2][((wt * 64 + b * 16 + col) * kWPitch + 8 * sub) / 8];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int r = (wj * 64 + a * 16 + col) * kWPitch + 8 * sub;
+      const uint4 ah = sh[buf][0][r / 8], al = sh[buf][1][r / 8];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        acc[a][b] = mfma_bf16(ah, bt[b], acc[a][b]);
+        acc[a][b] = mfma_bf16(al, bt[b], acc[a][b]);
+      }
+    }
+    if (s + 1 < steps) store(buf ^ 1, v);
+    __syncthreads();
+  }
+  // lane holds rows 4 sub..4 sub + 3 (j) of column col (t) of each tile
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int64_t t = t0 + wt * 64 + b * 16 + col;
+      const int64_t j = j0 + wj * 64 + a * 16 + 4 * sub;
+      if (t >= k) continue;
+      const float vals[4] = {acc[a][b].x, acc[a][b].y, acc[a][b].z, acc[a][b].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (j + i < n) dw[(j + i) * k + t] = vals[i] / 127.0f;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_backward_x(const uint8_t* packed_t, const float* gamma, const uint16_t* dy, int64_t m, int64_t n,
@@ -205,6 +359,43 @@ hipError_t launch_backward_x(const uint8_t* packed_t, const float* gamma, const 
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_bwd_x<4, 4>), dim3((unsigned)blocks), dim3(256), 0, s, packed_t, gamma, dy, m, n, k,
                      blocks_n, dx);
+  return hipGetLastError();
+}
+
+namespace {
+
+__global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ p, int64_t count) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < count) p[i] = 0.0f;
+}
+
+}  // namespace
+
+hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t s) {
+  if (count == 0) return hipSuccess;
+  const int64_t blocks = (count + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(256), 0, s, p, count);
+  return hipGetLastError();
+}
+
+size_t backward_w_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  const int64_t m_pad = (m + 63) / 64 * 64;
+  return (size_t)(2 * n + k) * (size_t)m_pad * 2;
+}
+
+hipError_t launch_backward_w(const uint16_t* dy, const int8_t* xq, const float* alpha, int64_t m, int64_t n, int64_t k,
+                             float* dw, void* workspace, hipStream_t s) {
+  const int64_t m_pad = (m + 63) / 64 * 64;
+  uint16_t* a_hi = reinterpret_cast<uint16_t*>(workspace);
+  uint16_t* a_lo = a_hi + n * m_pad;
+  uint16_t* x_t = a_lo + n * m_pad;
+  const int64_t prep_blocks = (n / kPrepTile + k / kPrepTile) * (m_pad / kPrepTile);
+  const int64_t blocks_t = (k + 127) / 128, blocks = ((n + 127) / 128) * blocks_t;
+  if (prep_blocks > 0x7FFFFFFF || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_bwd_w_prep, dim3((unsigned)prep_blocks), dim3(256), 0, s, dy, xq, alpha, m, n, k, m_pad, a_hi,
+                     a_lo, x_t);
+  hipLaunchKernelGGL(k_bwd_w, dim3((unsigned)blocks), dim3(256), 0, s, a_hi, a_lo, x_t, m_pad, n, k, blocks_t, dw);
   return hipGetLastError();
 }
 

@@ -27,6 +27,10 @@ hipError_t launch_pack_transposed(const uint8_t* packed, int64_t n, int64_t k, u
 // Straight-through backward: dx = gamma * dy q from packed q^T; dw = dy^T (alpha / 127 qx).
 hipError_t launch_backward_x(const uint8_t* packed_t, const float* gamma, const uint16_t* dy, int64_t m, int64_t n,
                              int64_t k, float* dx, hipStream_t s);
+hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t s);
+size_t backward_w_workspace_bytes(int64_t m, int64_t n, int64_t k);
+hipError_t launch_backward_w(const uint16_t* dy, const int8_t* xq, const float* alpha, int64_t m, int64_t n, int64_t k,
+                             float* dw, void* workspace, hipStream_t s);
 hipError_t launch_unpack(const uint8_t* packed, int64_t n, int64_t k, int8_t* q, hipStream_t s);
 
 // Per-token absmax int8 quantizer.

@@ -171,3 +171,18 @@ def test_backward_entry_points_validation():
     assert bx(FAKE, FAKE, None, 1, 64, 64, FAKE, None) == BL_ERR_NULL
     assert bx(FAKE, FAKE, FAKE + 2, 1, 64, 64, FAKE, None) == BL_ERR_ALIGN
     assert bx(FAKE, FAKE, FAKE, 1, 64, 64, FAKE + 2, None) == BL_ERR_ALIGN
+
+
+def test_backward_w_validation():
+    assert bl.bl_backward_w_workspace_bytes(64, 64, 64) == 2 * (2 * 64 + 64) * 64
+    assert bl.bl_backward_w_workspace_bytes(65, 128, 64) == 2 * (2 * 128 + 64) * 128
+    assert bl.bl_backward_w_workspace_bytes(1, 96, 64) == 0
+    bw = lib.bl_bitlinear_backward_w
+    ws = bl.bl_backward_w_workspace_bytes(3, 64, 64)
+    assert bw(FAKE, FAKE, FAKE, 3, 96, 64, FAKE, FAKE, ws, None) == BL_ERR_SHAPE
+    assert bw(FAKE, FAKE, FAKE, 3, 64, 100, FAKE, FAKE, ws, None) == BL_ERR_SHAPE
+    assert bw(FAKE, None, FAKE, 3, 64, 64, FAKE, FAKE, ws, None) == BL_ERR_NULL
+    assert bw(FAKE, FAKE, FAKE, 3, 64, 64, None, FAKE, ws, None) == BL_ERR_NULL
+    assert bw(FAKE + 1, FAKE, FAKE, 3, 64, 64, FAKE, FAKE, ws, None) == BL_ERR_ALIGN
+    assert bw(FAKE, FAKE, FAKE, 3, 64, 64, FAKE, FAKE + 8, ws, None) == BL_ERR_ALIGN
+    assert bw(FAKE, FAKE, FAKE, 3, 64, 64, FAKE, FAKE, ws - 1, None) == BL_ERR_WORKSPACE

@@ -89,3 +89,52 @@ def test_backward_x_zero_gamma_and_empty():
     empty = bl.bl_bitlinear_backward_x(packed_t, torch.ones(1, device="cuda"),
                                        torch.zeros((0, n), dtype=torch.bfloat16, device="cuda"), k)
     assert empty.shape == (0, k)
+
+
+def assert_dw_close(got, want, dy, xq, alpha):
+    m = dy.shape[0]
+    dyf = datagen.bf16_to_f32(dy).reshape(dy.shape).astype(np.float64)
+    mag = (np.abs(dyf) * alpha.astype(np.float64)[:, None]).T @ np.abs(xq.astype(np.float64)) / 127
+    bound = (m + 2) * 2.0 ** -24 * mag + 2 * np.spacing(np.abs(want).astype(np.float32)).astype(np.float64)
+    err = np.abs(got.astype(np.float64) - want.astype(np.float64))
+    bad = err > bound
+    assert not bad.any(), f"{bad.sum()} of {bad.size} differ beyond the bound; worst {np.max(err - bound):.3e}"
+
+
+def w_case(rng, m, n, k):
+    dy = dy_bits(rng, m, n)
+    x = datagen.activations_bf16(int(rng.integers(1 << 40)), m, k, rng.choice(k, size=min(8, k), replace=False), 20.0)
+    xq, alpha = oracle.quant_act(x)
+    return dy, xq, alpha
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 64, 64), (5, 128, 320), (64, 256, 256), (70, 320, 192), (130, 1024, 640),
+                                   (200, 64, 2560)])
+def test_backward_w_matches_oracle(m, n, k):
+    rng = np.random.default_rng(m * 11 + n + 3 * k)
+    dy, xq, alpha = w_case(rng, m, n, k)
+    say(f"bl_bitlinear_backward_w m={m} n={n} k={k}")
+    dw = host(bl.bl_bitlinear_backward_w(bf16(dy), torch.from_numpy(xq).cuda(), torch.from_numpy(alpha).cuda()))
+    want = oracle.backward_w(dy, xq, alpha)
+    assert_dw_close(dw, want, dy, xq, alpha)
+
+
+@pytest.mark.parametrize("name,n,k", [("gate_up", 13824, 2560), ("down", 2560, 6912)])
+def test_backward_w_2b_layer_sampled(name, n, k):
+    """2B-shaped layer, 2048 tokens; the oracle checks sampled rows of dw."""
+    rng = np.random.default_rng(n + 1)
+    m = 2048
+    dy, xq, alpha = w_case(rng, m, n, k)
+    say(f"bl_bitlinear_backward_w 2B {name} m={m}")
+    dw = host(bl.bl_bitlinear_backward_w(bf16(dy), torch.from_numpy(xq).cuda(), torch.from_numpy(alpha).cuda()))
+    rows = np.unique(np.concatenate([[0, n - 1], rng.choice(n, size=6, replace=False)]))
+    want = oracle.backward_w(np.ascontiguousarray(dy[:, rows]), xq, alpha)
+    assert_dw_close(dw[rows], want, np.ascontiguousarray(dy[:, rows]), xq, alpha)
+
+
+def test_backward_w_empty_tokens_gives_zero():
+    dw = bl.bl_bitlinear_backward_w(torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda"),
+                                    torch.zeros((0, 128), dtype=torch.int8, device="cuda"),
+                                    torch.zeros(0, dtype=torch.float32, device="cuda"),
+                                    dw=torch.full((64, 128), 7.0, device="cuda"))
+    assert not host(dw).any()
