@@ -253,6 +253,7 @@ def main() -> int:
     return 0
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 MFMA_I8_PEAK_TOPS = 5000.0
 CALIB_BYTES = 1 << 30
 STACK_WORKLOAD = "bitnet-b1.58-2B-shaped decode stack, M=1"
@@ -637,6 +638,64 @@ def measure_extras(args, linears, lib):
         del x, xq, alpha, h, xq2, alpha2, y2
     out["ffn_glu_2b_layer0"] = ffn
     del packed_glu, gamma_glu
+
+    # ---- training side, 2B layer 0 gate+up and down at M = 2048: the
+    # straight-through gradients and the per-step re-ternarization
+    train = {}
+    for name in ("gate_up", "down"):
+        lin = next(l for l in linears if l["name"] == name)
+        m, n, k = 2048, lin["n"], lin["k"]
+        w = torch.from_numpy(datagen.weights(datagen.stream_id(wl, 0, 2 if name == "gate_up" else 3,
+                                                               datagen.TENSOR_W), n, k)).to(dev)
+        packed = torch.empty(bl.bl_packed_bytes(n, k), dtype=torch.uint8, device=dev)
+        gamma = torch.empty(1, dtype=torch.float32, device=dev)
+        ws = torch.empty(bl.bl_ternarize_pack_workspace_bytes(n, k), dtype=torch.uint8, device=dev)
+        packed_t = torch.empty(bl.bl_packed_bytes(k, n), dtype=torch.uint8, device=dev)
+        g = torch.Generator(device="cpu").manual_seed(n * 31 + k)
+        dy = (torch.randn((m, n), generator=g) * 0.01).to(torch.bfloat16).to(dev)
+        x = act(datagen.stream_id(wl, 0, 2 if name == "gate_up" else 3, datagen.TENSOR_X) + 8192, m, k, wl,
+                datagen.STACK_2B_OUTLIERS, datagen.STACK_2B_OUTLIER_MULT)
+        xq, alpha = bl.bl_quant_act(x)
+        dx = torch.empty((m, k), dtype=torch.float32, device=dev)
+        dw = torch.empty((n, k), dtype=torch.float32, device=dev)
+        wws = torch.empty(bl.bl_backward_w_workspace_bytes(m, n, k), dtype=torch.uint8, device=dev)
+
+        def repack():
+            s = vp(torch.cuda.current_stream().cuda_stream)
+            rc = lib.bl_ternarize_pack(vp(w.data_ptr()), n, k, vp(packed.data_ptr()), vp(gamma.data_ptr()),
+                                       vp(ws.data_ptr()), ws.numel(), s)
+            rc = rc or lib.bl_pack_transposed(vp(packed.data_ptr()), n, k, vp(packed_t.data_ptr()), s)
+            if rc:
+                raise RuntimeError(bl.bl_status_string(rc))
+
+        def grad_x():
+            s = vp(torch.cuda.current_stream().cuda_stream)
+            rc = lib.bl_bitlinear_backward_x(vp(packed_t.data_ptr()), vp(gamma.data_ptr()), vp(dy.data_ptr()), m, n,
+                                             k, vp(dx.data_ptr()), s)
+            if rc:
+                raise RuntimeError(bl.bl_status_string(rc))
+
+        def grad_w():
+            s = vp(torch.cuda.current_stream().cuda_stream)
+            rc = lib.bl_bitlinear_backward_w(vp(dy.data_ptr()), vp(xq.data_ptr()), vp(alpha.data_ptr()), m, n, k,
+                                             vp(dw.data_ptr()), vp(wws.data_ptr()), wws.numel(), s)
+            if rc:
+                raise RuntimeError(bl.bl_status_string(rc))
+
+        repack()
+        inner = 5
+        ms_pack = _graph_time_ms(torch, _repeat(repack, inner), 5) / inner
+        ms_x = _graph_time_ms(torch, _repeat(grad_x, inner), 5) / inner
+        ms_w = _graph_time_ms(torch, _repeat(grad_w, inner), 5) / inner
+        flops = 2.0 * m * n * k
+        train[f"{name} M={m} K={k} N={n}"] = {
+            "repack_ms": round(ms_pack, 4), "repack_fp32_GBps": round(4.0 * n * k / (ms_pack * 1e-3) / 1e9, 1),
+            "grad_x_ms": round(ms_x, 4), "grad_x_TFLOPS": round(flops / (ms_x * 1e-3) / 1e12, 1),
+            "grad_x_frac_of_bf16_mfma_peak": round(flops / (ms_x * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "grad_w_ms": round(ms_w, 4), "grad_w_TFLOPS": round(flops / (ms_w * 1e-3) / 1e12, 1),
+            "grad_w_frac_of_bf16_mfma_peak": round(flops / (ms_w * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        del w, packed, packed_t, ws, dy, x, xq, alpha, dx, dw, wws
+    out["training_2b_layer0"] = train
 
     # ---- batched decode through the whole 2B stack, M = 4, 16, 64
     batched = {}
