@@ -260,7 +260,12 @@ STACK_WORKLOAD = "bitnet-b1.58-2B-shaped decode stack, M=1"
 STACK_KERNEL = "k_bitlinear_m1"
 # kernel base name -> source file whose hash marks the stored counter figures as current
 KERNEL_SOURCES = {"k_bitlinear_m1": "gemv.hip", "k_bitlinear_fused": "gemv.hip", "k_gemv_direct": "gemv.hip",
-                  "k_gemm": "gemm.hip", "k_quant_act": "quant.hip"}
+                  "k_gemv_lds": "gemv.hip", "k_gemm": "gemm.hip", "k_quant_act": "quant.hip",
+                  "k_bwd_x": "backward.hip", "k_bwd_w": "backward.hip", "k_bwd_w_prep": "backward.hip"}
+# operations per MFMA instruction: int8 16 x 16 x 64 (the forward kernels),
+# bf16 16 x 16 x 32 (the backward kernels), two per multiply-add
+MFMA_OPS = {"k_bwd_x": 16384, "k_bwd_w": 16384}
+MFMA_OPS_DEFAULT = 32768
 CU_SIMDS = 256 * 4
 CLOCK_GHZ = 2.4
 
@@ -370,8 +375,9 @@ def summarize(args):
     if "SQ_VALU_MFMA_BUSY_CYCLES" in counters:
         lines += ["## MFMA utilisation", "",
                   "busy = SQ_VALU_MFMA_BUSY_CYCLES (all SIMDs) / (dispatch duration x 2.4 GHz x 1024 SIMDs); "
-                  "ops = SQ_INSTS_MFMA x 32768 (v_mfma_i32_16x16x64_i8: 16 x 16 x 64 multiply-adds).", "",
-                  "| kernel | MFMA busy | MFMA instructions | int8 ops per dispatch | TOPS over the dispatch |",
+                  "ops = SQ_INSTS_MFMA x 32768 for v_mfma_i32_16x16x64_i8 (16 x 16 x 64 multiply-adds), "
+                  "x 16384 for v_mfma_f32_16x16x32_bf16 (k_bwd_x, k_bwd_w).", "",
+                  "| kernel | MFMA busy | MFMA instructions | ops per dispatch | T(FL)OPS over the dispatch |",
                   "|---|---|---|---|---|"]
         busy = counters["SQ_VALU_MFMA_BUSY_CYCLES"]
         insts = counters.get("SQ_INSTS_MFMA", {})
@@ -380,7 +386,7 @@ def summarize(args):
                 continue
             util = b / (dur * CLOCK_GHZ * CU_SIMDS)
             n_inst = insts.get(k, (0.0, dur, 0))[0]
-            ops = n_inst * 32768
+            ops = n_inst * MFMA_OPS.get(k, MFMA_OPS_DEFAULT)
             lines.append(f"| {k} | {100 * util:.1f}% | {n_inst:.0f} | {ops:.4g} | "
                          f"{ops / (insts.get(k, (0, dur, 0))[1] * 1e-9) / 1e12 if n_inst else 0:.1f} |")
         lines.append("")
@@ -487,8 +493,42 @@ def _profile_70b(args, ms):
     return 0
 
 
+def _profile_training_2b(args):
+    """Layer-0 gate+up and down of the 2B-shaped stack at M = 2048, training
+    side: re-ternarization with the transposed packing, the input gradient and
+    the weight gradient, --reps times each."""
+    import numpy as np
+    import torch
+    import datagen
+    import ternary_weight_absmean_amd as bl
+
+    dev = torch.device("cuda", 0)
+    wl = datagen.WORKLOAD_STACK_2B
+    m = 2048
+    for pi, (name, k, n) in enumerate(datagen.STACK_2B_PROJ):
+        if name not in ("gate_up", "down"):
+            continue
+        w = torch.from_numpy(datagen.weights(datagen.stream_id(wl, 0, pi, datagen.TENSOR_W), n, k)).to(dev)
+        g = torch.Generator(device="cpu").manual_seed(n * 31 + k)
+        dy = (torch.randn((m, n), generator=g) * 0.01).to(torch.bfloat16).to(dev)
+        cols = datagen.outlier_columns(wl, k, datagen.STACK_2B_OUTLIERS)
+        x = datagen.activations_bf16(datagen.stream_id(wl, 0, pi, datagen.TENSOR_X) + 8192, m, k, cols,
+                                     datagen.STACK_2B_OUTLIER_MULT)
+        xq, alpha = bl.bl_quant_act(torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16))
+        ws = torch.empty(bl.bl_backward_w_workspace_bytes(m, n, k), dtype=torch.uint8, device=dev)
+        for _ in range(args.reps):
+            packed, gamma = bl.bl_ternarize_pack(w)
+            packed_t = bl.bl_pack_transposed(packed, n, k)
+            bl.bl_bitlinear_backward_x(packed_t, gamma, dy, k)
+            bl.bl_bitlinear_backward_w(dy, xq, alpha, workspace=ws)
+        torch.cuda.synchronize()
+        print(f"[profile] training_2b {name} M={m} K={k} N={n} x{args.reps}", flush=True)
+    return 0
+
+
 PROFILE_CASES = {
     "prefill_2b": _profile_prefill_2b,
+    "training_2b": _profile_training_2b,
     "decode_70b": lambda args: _profile_70b(args, (1, 16)),
     "prefill_70b": lambda args: _profile_70b(args, (1024,)),
 }
