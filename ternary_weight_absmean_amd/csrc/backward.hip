@@ -282,8 +282,22 @@ __global__ __launch_bounds__(256, 2) void k_bwd_w(const uint16_t* __restrict__ a
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wj = wave >> 1, wt = wave & 1;
   const int sub = lane >> 4, col = lane & 15;
-  const int64_t j0 = ((int64_t)blockIdx.x / blocks_t) * 128;
-  const int64_t t0 = ((int64_t)blockIdx.x % blocks_t) * 128;
+  // the XCD-grouped tile order of the forward GEMM: an XCD's resident
+  // workgroups cover about 8 j-blocks x 8 t-blocks and share their operand
+  // slices in its L2 at each step
+  constexpr int64_t kGroupJ = 8;
+  const int64_t tiles = (int64_t)gridDim.x;
+  const int64_t blocks_j = tiles / blocks_t;
+  const int64_t full = tiles / kXcds * kXcds;
+  const int64_t tt = (int64_t)blockIdx.x >= full
+                         ? (int64_t)blockIdx.x
+                         : (int64_t)(blockIdx.x % kXcds) * (tiles / kXcds) + blockIdx.x / kXcds;
+  const int64_t group = tt / (kGroupJ * blocks_t);
+  const int64_t first_j = group * kGroupJ;
+  const int64_t group_j = min(kGroupJ, blocks_j - first_j);
+  const int64_t local = tt - group * kGroupJ * blocks_t;
+  const int64_t j0 = (first_j + local % group_j) * 128;
+  const int64_t t0 = (local / group_j) * 128;
   const int steps = (int)(m_pad / kWStep);
   // staging: each operand tile is 128 rows x 64 bytes = 512 pieces of 16 bytes; thread -> pieces tid, tid + 256
   const int pr0 = tid >> 2, pc = tid & 3;
