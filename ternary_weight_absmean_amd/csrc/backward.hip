@@ -12,9 +12,9 @@
 // it has the shape of the forward product with bf16 activations:
 //   * the matrix cores run v_mfma_f32_16x16x32_bf16: A = 16 rows of q^T as bf16
 //     values -1, 0, +1 (exact), B = 16 tokens of dy, fp32 accumulation;
-//   * a workgroup (4 waves along the rows of q^T) owns 256 rows x 64 tokens;
-//     each wave 64 rows x 64 tokens = 4 x 4 MFMA tiles;
-//   * each step covers 256 columns j: a wave loads its 64 rows' packed bytes
+//   * a workgroup (4 waves along the rows of q^T) owns 128 rows x 64 tokens;
+//     each wave 32 rows x 64 tokens = 2 x 4 MFMA tiles;
+//   * each step covers 256 columns j: a wave loads its 32 rows' packed bytes
 //     into registers (1 KiB per 16 rows: lane (r, s) holds row r of column
 //     tile s, 64 trits), and MFMA (f, h) takes, per lane, the 8 trits of bytes
 //     8h..8h+7 of field f (columns 64 s + 16 f + 8 h + e) -- eight MFMAs per
@@ -167,12 +167,16 @@ __global__ __launch_bounds__(256, 2) void k_bwd_x(const uint8_t* __restrict__ pa
           for (int tb = 0; tb < kTB; ++tb) acc[rb][tb] = mfma_bf16(a, b[tb], acc[rb][tb]);
         }
       }
+      // one field at a time: keeps the live operand registers (and so the
+      // unrolled step pair) within the register file
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  for (int s = 0; s + 1 < steps; ++s) {
-    uint4* rd = (s & 1) ? xs1 : xs0;
-    uint4* wr = (s & 1) ? xs0 : xs1;
+  // two distinct LDS buffers named at compile time in an unrolled step pair:
+  // the compiler then knows the DMA into one cannot touch the reads of the
+  // other and does not wait for it before reading
+  auto step = [&](int s, const uint4* rd, uint4* wr) __attribute__((always_inline)) {
     load_w(s + 1, w_next);
     load_x(s + 1, wr);
     compute(rd);
@@ -180,8 +184,18 @@ __global__ __launch_bounds__(256, 2) void k_bwd_x(const uint8_t* __restrict__ pa
     __syncthreads();                // ... and every other wave's, and nobody reads rd any more
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) w_cur[rb] = w_next[rb];
+  };
+  int s = 0;
+  for (; s + 2 < steps; s += 2) {
+    step(s, xs0, xs1);
+    step(s + 1, xs1, xs0);
   }
-  compute(((steps - 1) & 1) ? xs1 : xs0);
+  if (s + 1 < steps) {
+    step(s, xs0, xs1);
+    compute(xs1);
+  } else {
+    compute(xs0);
+  }
 
   const float gamma = *gamma_ptr;
   const bool vec_ok = ((uintptr_t)dx % 16) == 0;
@@ -368,10 +382,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_w(const uint16_t* __restrict__ a
 
 hipError_t launch_backward_x(const uint8_t* packed_t, const float* gamma, const uint16_t* dy, int64_t m, int64_t n,
                              int64_t k, float* dx, hipStream_t s) {
-  // 256 rows of q^T x 64 tokens per workgroup
-  const int64_t blocks_n = (k + 255) / 256, blocks = blocks_n * ((m + 63) / 64);
+  // 128 rows of q^T x 64 tokens per workgroup (measured faster than 256 x 64)
+  const int64_t blocks_n = (k + 127) / 128, blocks = blocks_n * ((m + 63) / 64);
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_bwd_x<4, 4>), dim3((unsigned)blocks), dim3(256), 0, s, packed_t, gamma, dy, m, n, k,
+  hipLaunchKernelGGL((k_bwd_x<4, 2>), dim3((unsigned)blocks), dim3(256), 0, s, packed_t, gamma, dy, m, n, k,
                      blocks_n, dx);
   return hipGetLastError();
 }

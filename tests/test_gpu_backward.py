@@ -3,7 +3,7 @@
 Bar: the transposed packing bit-exact; dx within the fp32 accumulation bound
 of the oracle's exactly rounded value: |dx - want| <= (n + 2) * 2^-24 * gamma *
 sum_j |dy[i][j]| + one fp32 ulp of want (the products dy * q are exact; only
-the order of the fp32 sums differs).  Shapes span several 256-row x 64-token
+the order of the fp32 sums differs).  Shapes span several 128-row x 64-token
 workgroups, ragged token counts, a partial last 256-column step, and the
 2B-shaped layers at full size (sampled token rows).
 """
