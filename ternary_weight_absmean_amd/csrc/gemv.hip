@@ -192,7 +192,7 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_fused(const uint4* __rest
   {
     const __amdgpu_buffer_rsrc_t r0 = tile_rsrc(0);
 #pragma unroll
-    for (int u = 0; u < kGroupsPerBatch; ++u) a_cur[u] = buffer_load16(r0, w_off(u));
+    for (int u = 0; u < kGroupsPerBatch; ++u) a_cur[u] = buffer_load16_stream(r0, w_off(u));
   }
   const float gamma = buffer_load_f32(buffer_rsrc(gamma_ptr, 4), 0);
   // keep these loads here, in flight while the activations are reduced
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_fused(const uint4* __rest
       uint4 a_next[kGroupsPerBatch];
 #pragma unroll
       for (int u = 0; u < kGroupsPerBatch; ++u)
-        a_next[u] = buffer_load16(same ? cur_rsrc : next_rsrc, w_off(ngi + u));
+        a_next[u] = buffer_load16_stream(same ? cur_rsrc : next_rsrc, w_off(ngi + u));
 #pragma unroll
       for (int u = 0; u < kGroupsPerBatch; ++u) {
         // tiles past k carry zero codes, so any in-bounds activation bytes will do
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_fused(const uint4* __rest
     }
     if (my_groups == 0 && rt + 1 < kRT) {  // keep the stream aligned: nothing was loaded for this tile
 #pragma unroll
-      for (int u = 0; u < kGroupsPerBatch; ++u) a_cur[u] = buffer_load16(next_rsrc, w_off(u));
+      for (int u = 0; u < kGroupsPerBatch; ++u) a_cur[u] = buffer_load16_stream(next_rsrc, w_off(u));
     }
     // exact: acc4 holds 4x, acc16a/b 16x the code sums
     v4i part = acc1;
@@ -312,11 +312,11 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_fused(const uint4* __rest
   }
 }
 
-constexpr int kM1MaxSlots = 14;  // 16-byte bf16 chunks per lane (own groups only: rows up to k = 28672)
+constexpr int kM1MaxSlots = 7;  // 16-byte bf16 chunks per lane at 8 waves (own groups only: rows up to k = 28672)
 
 // BitLinear for one token, or a few (m <= kM = 4) with short rows,
-// quantization fused.  Wave w of the four multiplies the 256-column groups
-// w, w + 4, ... and quantizes exactly those, for every token, into its own
+// quantization fused.  Wave w of the kWv (4, or 8 for long rows) multiplies
+// the 256-column groups w, w + kWv, ... and quantizes exactly those, for every token, into its own
 // LDS region, which only it reads.  The tokens' absmaxes come from per-wave
 // maxima of the own groups exchanged through LDS (one barrier).  Slot i of
 // lane l holds chunk (l % 32) of the wave's own group rank 2i + l / 32, so
@@ -329,14 +329,14 @@ constexpr int kM1MaxSlots = 14;  // 16-byte bf16 chunks per lane (own groups onl
 // packed with alternating gate/up row tiles and kRT = 2, so the workgroup's
 // two tiles are the gate and up rows of the same 16 outputs; wave 0 writes
 // h = bf16(relu(g)^2 * u) into y_out ([m][n / 2]).
-template <int kRT, int kC, int kM, bool kGlu = false>
-__global__ __launch_bounds__(kWaves * 64) void k_bitlinear_m1(const uint4* __restrict__ packed,
+template <int kRT, int kC, int kM, bool kGlu = false, int kWv = kWaves>
+__global__ __launch_bounds__(kWv * 64) void k_bitlinear_m1(const uint4* __restrict__ packed,
                                                                const float* __restrict__ gamma_ptr,
                                                                const uint4* __restrict__ x, float* __restrict__ alpha,
                                                                int8_t* __restrict__ xq_out, int m, int n, int k,
                                                                int32_t* __restrict__ acc_out,
                                                                uint16_t* __restrict__ y_out) {
-  constexpr int kW = kWaves;
+  constexpr int kW = kWv;
   constexpr int kB = kGroupsPerBatch;  // weight groups per batch (larger batches measured no faster)
   extern __shared__ uint4 xw_raw[];    // [wave][own group rank][token][256 bytes]
   __shared__ v4i partial[kRT][kW][64];
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_bitlinear_m1(const uint4* __res
   {
     const __amdgpu_buffer_rsrc_t r0 = tile_rsrc(0);
 #pragma unroll
-    for (int u = 0; u < kB; ++u) a_cur[u] = buffer_load16(r0, w_off(u));
+    for (int u = 0; u < kB; ++u) a_cur[u] = buffer_load16_stream(r0, w_off(u));
   }
   const float gamma = buffer_load_f32(buffer_rsrc(gamma_ptr, 4), 0);
   // keep these loads here, in flight while the activations are reduced
@@ -462,7 +462,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_bitlinear_m1(const uint4* __res
       uint4 a_next[kB];
 #pragma unroll
       for (int u = 0; u < kB; ++u)
-        a_next[u] = buffer_load16(same ? cur_rsrc : next_rsrc, w_off(ngi + u));
+        a_next[u] = buffer_load16_stream(same ? cur_rsrc : next_rsrc, w_off(ngi + u));
 #pragma unroll
       for (int u = 0; u < kB; ++u) {
         // groups past this wave's share carry zero codes; any region slot will do
@@ -481,7 +481,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_bitlinear_m1(const uint4* __res
     }
     if (my_groups == 0 && rt + 1 < kRT) {  // keep the stream aligned: nothing was loaded for this tile
 #pragma unroll
-      for (int u = 0; u < kB; ++u) a_cur[u] = buffer_load16(next_rsrc, w_off(u));
+      for (int u = 0; u < kB; ++u) a_cur[u] = buffer_load16_stream(next_rsrc, w_off(u));
     }
     // exact: acc4 holds 4x, acc16a/b 16x the code sums; minus this wave's x sum
     v4i part = acc1;
@@ -572,7 +572,7 @@ __global__ __launch_bounds__(kW * 64) void k_gemv_direct(const uint4* __restrict
         b[u][f] = buffer_load16(xrsrc, valid ? (uint32_t)(col * k + kt * kTileCols + 16 * f) : kOutOfRange);
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt)
-        a[rt][u] = buffer_load16(wrsrc[rt], g < groups ? (uint32_t)(g * 1024 + lane * 16) : kOutOfRange);
+        a[rt][u] = buffer_load16_stream(wrsrc[rt], g < groups ? (uint32_t)(g * 1024 + lane * 16) : kOutOfRange);
     }
   };
   v4i acc[kRT][2];
@@ -714,7 +714,7 @@ __global__ __launch_bounds__(kW * 64) void k_gemv_lds(const uint4* __restrict__ 
       const int g = group_of(c, u);
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt)
-        a[rt][u] = buffer_load16(wrsrc[rt], g < groups ? (uint32_t)(g * 1024 + lane * 16) : kOutOfRange);
+        a[rt][u] = buffer_load16_stream(wrsrc[rt], g < groups ? (uint32_t)(g * 1024 + lane * 16) : kOutOfRange);
     }
   };
 
@@ -908,16 +908,23 @@ typedef void (*M1Kernel)(const uint4*, const float*, const uint4*, float*, int8_
                          uint16_t*);
 struct M1Config {
   int rt = 0;
+  int waves = kWaves;
   M1Kernel kernel = nullptr;  // none when the rows need more slots per lane than the token count allows
 };
 
 template <int kRT>
-M1Kernel m1_pick(int64_t m, int64_t groups) {
+M1Kernel m1_pick(int64_t m, int64_t groups, int& waves) {
   const int64_t slots = ((groups + kWaves - 1) / kWaves + 1) / 2;
+  waves = kWaves;
   if (m == 1) {
     if (slots <= 2) return k_bitlinear_m1<kRT, 2, 1>;
     if (slots <= 5) return k_bitlinear_m1<kRT, 5, 1>;
-    if (slots <= kM1MaxSlots) return k_bitlinear_m1<kRT, kM1MaxSlots, 1>;
+    // long rows: eight waves, so each streams half as many groups (measured
+    // 4.9 TB/s against 4.3 with four on rows of 28672)
+    if (((groups + 7) / 8 + 1) / 2 <= kM1MaxSlots) {
+      waves = 8;
+      return k_bitlinear_m1<kRT, kM1MaxSlots, 1, false, 8>;
+    }
   } else if (m <= 4 && slots <= 2) {
     return k_bitlinear_m1<kRT, 2, 4>;
   }
@@ -925,12 +932,18 @@ M1Kernel m1_pick(int64_t m, int64_t groups) {
 }
 
 template <int kRT>
-M1Kernel m1_pick_glu(int64_t m, int64_t groups) {
+M1Kernel m1_pick_glu(int64_t m, int64_t groups, int& waves) {
   const int64_t slots = ((groups + kWaves - 1) / kWaves + 1) / 2;
+  waves = kWaves;
   if (m == 1) {
     if (slots <= 2) return k_bitlinear_m1<kRT, 2, 1, true>;
     if (slots <= 5) return k_bitlinear_m1<kRT, 5, 1, true>;
-    if (slots <= kM1MaxSlots) return k_bitlinear_m1<kRT, kM1MaxSlots, 1, true>;
+    // long rows: eight waves, so each streams half as many groups (measured
+    // 4.9 TB/s against 4.3 with four on rows of 28672)
+    if (((groups + 7) / 8 + 1) / 2 <= kM1MaxSlots) {
+      waves = 8;
+      return k_bitlinear_m1<kRT, kM1MaxSlots, 1, true, 8>;
+    }
   } else if (m <= 4 && slots <= 2) {
     return k_bitlinear_m1<kRT, 2, 4, true>;
   }
@@ -943,7 +956,7 @@ M1Config m1_config_glu(int64_t m, int64_t groups, int64_t row_tiles) {
   if (m > 1 && (m > 4 || row_tiles >= 512)) return M1Config{};
   M1Config c;
   c.rt = 2;
-  c.kernel = m1_pick_glu<2>(m, groups);
+  c.kernel = m1_pick_glu<2>(m, groups, c.waves);
   return c;
 }
 
@@ -952,13 +965,13 @@ M1Config m1_config(int64_t m, int64_t groups, int64_t row_tiles) {
   // only for short rows and few row tiles (measured: rows of 2560 with 160
   // or 240 row tiles; not 6912-column rows or 864+ row tiles).
   if (m > 1 && (m > 4 || row_tiles >= 512)) return M1Config{};
-  // two row tiles per workgroup for short rows once there are more than ~2
-  // tiles per CU (the quantized tokens are reused); long rows keep one tile
-  // per workgroup, whose weight stream is already long enough
-  const int rt = row_tiles >= 512 && groups <= 16 ? 2 : 1;
+  // two row tiles per workgroup (the quantized tokens are reused) for short
+  // rows once there are more than ~2 tiles per CU, for longer rows once there
+  // are ~4 (measured on 8192-column rows: 5.6 TB/s against 5.1 with one)
+  const int rt = (row_tiles >= 512 && groups <= 16) || row_tiles >= 1024 ? 2 : 1;
   M1Config c;
   c.rt = rt;
-  c.kernel = rt == 2 ? m1_pick<2>(m, groups) : m1_pick<1>(m, groups);
+  c.kernel = rt == 2 ? m1_pick<2>(m, groups, c.waves) : m1_pick<1>(m, groups, c.waves);
   return c;
 }
 
@@ -1006,9 +1019,9 @@ hipError_t launch_gemv_fused_glu(const uint8_t* packed, const float* gamma, cons
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   if (c.kernel) {
     const int64_t tokens = m == 1 ? 1 : 4;
-    const size_t lds = (size_t)kWaves * (size_t)((groups + kWaves - 1) / kWaves) * (size_t)tokens * 256;
+    const size_t lds = (size_t)c.waves * (size_t)((groups + c.waves - 1) / c.waves) * (size_t)tokens * 256;
     const dim3 grid((unsigned)(row_tiles / 2));
-    hipLaunchKernelGGL(c.kernel, grid, dim3(64 * kWaves), lds, s, p, gamma, xv, alpha, xq, (int)m, (int)(2 * f),
+    hipLaunchKernelGGL(c.kernel, grid, dim3(64 * c.waves), lds, s, p, gamma, xv, alpha, xq, (int)m, (int)(2 * f),
                        (int)k, nullptr, h);
     return hipGetLastError();
   }
@@ -1033,9 +1046,9 @@ hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const ui
     const int64_t groups = (k / kTileCols + 3) / 4;
     const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
     const int64_t tokens = m == 1 ? 1 : 4;
-    const size_t lds = (size_t)kWaves * (size_t)((groups + kWaves - 1) / kWaves) * (size_t)tokens * 256;
+    const size_t lds = (size_t)c.waves * (size_t)((groups + c.waves - 1) / c.waves) * (size_t)tokens * 256;
     const dim3 grid((unsigned)((row_tiles + c.rt - 1) / c.rt));
-    hipLaunchKernelGGL(c.kernel, grid, dim3(64 * kWaves), lds, s, reinterpret_cast<const uint4*>(packed), gamma,
+    hipLaunchKernelGGL(c.kernel, grid, dim3(64 * c.waves), lds, s, reinterpret_cast<const uint4*>(packed), gamma,
                        reinterpret_cast<const uint4*>(x), alpha, xq, (int)m, (int)n, (int)k, acc, y);
     return hipGetLastError();
   }

@@ -336,8 +336,9 @@ def test_linear_is_deterministic():
                                    # shapes just past its limits
                                    (2, 70, 2624), (4, 1000, 4096), (4, 8000, 2560), (4, 8200, 2560),
                                    (7, 530, 2112), (6, 16400, 320), (4, 33, 10240),
-                                   # eight-wave kernel for long rows (k >= 16384)
-                                   (1, 530, 16384), (7, 70, 16448), (16, 40, 32768),
+                                   # eight-wave kernels for long rows: block-quantizing (k >= 16384) and
+                                   # single-token (k > 10240) with two row tiles, ragged last workgroup and group
+                                   (1, 530, 16384), (7, 70, 16448), (16, 40, 32768), (1, 16400, 10304),
                                    (3, 48, 2560), (4, 3840, 2560), (5, 40, 6912), (16, 64, 1024), (16, 31, 2560),
                                    (17, 40, 2560), (64, 100, 2560), (4, 16, 28672)])
 def test_bitlinear_matches_oracle(m, n, k):
