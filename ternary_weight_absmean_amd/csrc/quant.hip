@@ -17,9 +17,10 @@ namespace {
 
 constexpr int kQuantThreads = 256;
 
-// One workgroup per token row.  Rows of up to 256 * kC chunks of 8 bf16 are
-// held in registers between the absmax and the quantization (one read of
-// the row); longer rows (kC = 0) are read twice, the second time from L2.
+// One workgroup per token row.  Rows of up to 256 * kC chunks of 8 bf16 (kC
+// up to 16: 32768 columns) are held in registers between the absmax and the
+// quantization (one read of the row); longer rows (kC = 0) are read twice,
+// the second time from L2.
 // Loads go through a buffer resource over the row, so chunks past k read as
 // zero and need no branch.  The int8 code is formed by adding 1.5 * 2^23 to
 // the fp32 product x * s (round half to even into the low byte); for finite
@@ -77,6 +78,8 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t m, int64_t k, int8_t* xq,
     hipLaunchKernelGGL(k_quant_act<4>, dim3((unsigned)m), dim3(kQuantThreads), 0, s, xv, k, q, alpha);
   else if (chunks <= 8)
     hipLaunchKernelGGL(k_quant_act<8>, dim3((unsigned)m), dim3(kQuantThreads), 0, s, xv, k, q, alpha);
+  else if (chunks <= 16)
+    hipLaunchKernelGGL(k_quant_act<16>, dim3((unsigned)m), dim3(kQuantThreads), 0, s, xv, k, q, alpha);
   else
     hipLaunchKernelGGL(k_quant_act<0>, dim3((unsigned)m), dim3(kQuantThreads), 0, s, xv, k, q, alpha);
   return hipGetLastError();
