@@ -24,9 +24,11 @@
 //
 // Kernels:
 //   k_bitlinear_m1     one token, quantization fused; each wave quantizes only
-//                      the columns it multiplies (the bench step's kernel)
+//                      the columns it multiplies (single-token decode)
 //   k_bitlinear_fused  a few tokens (m * k small), block quantization fused
-//   k_gemv_lds         2..16 tokens, int8 activations given, staged in LDS
+//   k_gemv_lds         2..64 tokens, int8 activations given, staged in LDS
+//   k_gemv_ring        2..16 tokens on rows of 8192 and more, int8
+//                      activations given, streamed through an LDS ring by DMA
 //   k_gemv_direct      one token, int8 activations given
 // The fused kernels feed the MFMA with the raw codes c = q + 1 and correct
 // with the token's activation sum: sum q*x = sum c*x - sum x.  Masking a
@@ -815,6 +817,157 @@ __global__ __launch_bounds__(kW * 64) void k_gemv_lds(const uint4* __restrict__ 
     }
 }
 
+
+// s_waitcnt immediate that waits until at most n vector memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_at_most(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// Product with int8 activations given, 2 <= m <= 16 tokens, long rows: the
+// token block's activations stream through a ring of four 1024-column LDS
+// buffers filled by DMA (buffer loads that write LDS, no registers) three
+// chunks ahead, so the loads of three chunks are in flight while one is
+// multiplied; one barrier per chunk.  kW = 4 * kRT waves: wave w multiplies
+// 256-column group w % 4 of every chunk for row tile w / 4 of the workgroup
+// (one non-temporal 1 KiB weight load per chunk, in a register ring beside
+// the LDS ring), and the four waves of a tile add their partial sums through
+// LDS at the end.  Token rows are 1024 bytes apart in a buffer, so stored
+// 16-byte piece p of row r holds source piece p ^ (r % 16): the 16 token rows
+// of a B operand read fall in distinct banks.  Pieces past k and rows past m
+// read as zero, so the trits of a partial last group (whose codes past k are
+// zero, i.e. -1) meet zero activations.  The chunk loop is unrolled by the
+// ring size so that every buffer is named at compile time.
+// kGlu (kRT = 2): gate+up matrix with alternating gate/up row tiles; wave 0
+// gates the tile pair into y_out ([m][n / 2]).
+template <int kRT, bool kGlu = false>
+__global__ __launch_bounds__(kRT * 256) void k_gemv_ring(const uint4* __restrict__ packed,
+                                                        const float* __restrict__ gamma_ptr,
+                                                        const int8_t* __restrict__ xq,
+                                                        const float* __restrict__ alpha, int64_t m, int64_t n,
+                                                        int64_t k, int32_t* __restrict__ acc_out,
+                                                        uint16_t* __restrict__ y_out) {
+  constexpr int kW = 4 * kRT;
+  constexpr int kCC = 1024;          // columns per chunk
+  constexpr int kPieces = kCC / 16;  // 16-byte pieces per token row and chunk
+  constexpr int kDma = 16 / kW;      // token rows this wave copies per chunk, one 1 KiB DMA each
+  static_assert(16 % kW == 0, "the 16 token rows split evenly over the waves");
+  static_assert(!kGlu || kRT == 2, "a gate tile and its up tile per workgroup");
+  __shared__ uint4 xs0[16 * kPieces];  // the ring: four distinct LDS objects
+  __shared__ uint4 xs1[16 * kPieces];
+  __shared__ uint4 xs2[16 * kPieces];
+  __shared__ uint4 xs3[16 * kPieces];
+  __shared__ v4i partial[kRT][4][64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int my_rt = wave >> 2;
+  const int my_g = wave & 3;
+  const int sub = lane >> 4;
+  const int col = lane & 15;
+  const int64_t tile0 = (int64_t)blockIdx.x * kRT;
+  const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
+  const int tiles_here = (int)min((int64_t)kRT, row_tiles - tile0);
+  const int64_t tok0 = (int64_t)blockIdx.y * 16;
+  const int rows = (int)min((int64_t)16, m - tok0);
+  const int kt_count = (int)(k / kTileCols);
+  const int chunks = (int)((k + kCC - 1) / kCC);
+  const uint32_t kk = (uint32_t)k;
+
+  const __amdgpu_buffer_rsrc_t wrsrc =
+      buffer_rsrc(packed + (tile0 + my_rt) * kt_count * (kTileBytes / 16),
+                  my_rt < tiles_here ? (uint32_t)(kt_count * kTileBytes) : 0u);
+  const __amdgpu_buffer_rsrc_t xrsrc = buffer_rsrc(xq + tok0 * k, (uint32_t)(rows * k));
+  const float gamma = buffer_load_f32(buffer_rsrc(gamma_ptr, 4), 0);
+  const float alpha_tok =
+      buffer_load_f32(buffer_rsrc(alpha + tok0, (uint32_t)(rows * 4)), col < rows ? (uint32_t)(col * 4) : kOutOfRange);
+
+  // chunk c: this wave's token rows into dst by DMA, its weight group into w
+  auto load_chunk = [&](int c, uint4* dst, uint4& w) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kDma; ++j) {
+      const int row = wave * kDma + j;
+      const uint32_t col_byte = (uint32_t)c * kCC + 16u * (uint32_t)(lane ^ (row & 15));
+      const uint32_t off = col_byte < kk ? (uint32_t)row * kk + col_byte : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, (__attribute__((address_space(3))) void*)(dst + row * kPieces),
+                                               16, off, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // one issue order for every chunk: the wait counts depend on it
+    w = buffer_load16_stream(wrsrc, (uint32_t)((c * 4 + my_g) * 1024 + lane * 16));
+  };
+
+  v4i acc0 = {0, 0, 0, 0}, acc1 = acc0;
+  auto compute = [&](const uint4* buf, const uint4& w) __attribute__((always_inline)) {
+    // token col, column tile sub of group my_g: pieces 16 * my_g + 4 * sub + f
+    const uint4* xt = buf + col * kPieces;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const v4i b = as_v4i(xt[(16 * my_g + 4 * sub + f) ^ col]);
+      if (f & 1)
+        acc1 = mfma_16x16x64(unpack_field(w, f), b, acc1);
+      else
+        acc0 = mfma_16x16x64(unpack_field(w, f), b, acc0);
+    }
+  };
+  // chunk c: this wave's LDS reads of chunk c - 1 have completed and its DMA
+  // and weights of chunk c (issued before those of chunks c + 1 and c + 2)
+  // have landed; after the barrier that holds for every wave, so chunk c is
+  // in LDS and the buffer of chunk c - 1 is free for chunk c + 3.  (A bare
+  // s_barrier with its own wait: __syncthreads() carries a release fence,
+  // which would wait for every DMA this wave has in flight, the later
+  // chunks' included.  The scheduling barriers keep every LDS access and
+  // MFMA on its side of it.)
+  auto step = [&](int c, const uint4* rd, const uint4& w_rd, uint4* wr, uint4& w_wr) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(2 * (kDma + 1)) & ~(15 << 8));  // and lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    __builtin_amdgcn_sched_barrier(0);
+    load_chunk(c + 3, wr, w_wr);
+    // nothing of this chunk's arithmetic moves above the barrier (its weight
+    // register would then be waited for early, with the later loads)
+    __builtin_amdgcn_sched_barrier(0);
+    compute(rd, w_rd);
+  };
+  // issue order as in the loop: each chunk's DMA, then its weights
+  uint4 w0, w1, w2, w3;
+  load_chunk(0, xs0, w0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_chunk(1, xs1, w1);
+  __builtin_amdgcn_sched_barrier(0);
+  load_chunk(2, xs2, w2);
+  __builtin_amdgcn_sched_barrier(0);
+  // chunks past the last read as zero: the ring runs in whole turns (at
+  // least one: k > 0, and the loads above stay ahead of the loop)
+  int c = 0;
+  do {
+    step(c, xs0, w0, xs3, w3);
+    step(c + 1, xs1, w1, xs0, w0);
+    step(c + 2, xs2, w2, xs1, w1);
+    step(c + 3, xs3, w3, xs2, w2);
+    c += 4;
+  } while (c < chunks);
+  __builtin_amdgcn_s_waitcnt(0);  // the last (all-zero) loads have landed before the wave can exit
+
+  add4(acc0, acc1);
+  partial[my_rt][my_g][lane] = acc0;
+  __syncthreads();
+  if (my_g != 0 || col >= rows) return;
+  auto tile_sum = [&](int rt) {
+    v4i sum = partial[rt][0][lane];
+#pragma unroll
+    for (int g = 1; g < 4; ++g) add4(sum, partial[rt][g][lane]);
+    return sum;
+  };
+  const float scale = (gamma * alpha_tok) / 127.0f;
+  if constexpr (kGlu) {
+    if (wave != 0 || tiles_here < 2) return;
+    store_glu_tile(tile_sum(0), tile_sum(1), (tile0 / 2) * kTileRows + 4 * sub, tok0 + col, n / 2, scale, y_out);
+    return;
+  }
+  if (my_rt >= tiles_here) return;
+  store_tile(tile_sum(my_rt), (tile0 + my_rt) * kTileRows + 4 * sub, tok0 + col, n, scale, acc_out, y_out);
+}
+
 }  // namespace
 
 size_t gemv_lds_bytes(int64_t m, int64_t k) { return (size_t)(m < 16 ? m : 16) * (size_t)(k + kLdsRowPad); }
@@ -852,6 +1005,8 @@ namespace {
 
 // kGlu: gate+up matrix of n rows, alternating gate/up tiles; y is h [m][n / 2]
 // and every workgroup takes an even number of row tiles.
+constexpr int64_t kRingMinK = 8192;  // rows from which 2..16 tokens take k_gemv_ring
+
 template <bool kGlu>
 hipError_t launch_gemv_impl(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
                             int64_t n, int64_t k, int32_t* acc, uint16_t* y, hipStream_t s) {
@@ -869,17 +1024,23 @@ hipError_t launch_gemv_impl(const uint8_t* packed, const float* gamma, const int
     return hipGetLastError();
   }
   if (m >= 2) {
-    // two row tiles per workgroup once there are ~2 per CU; eight waves (same
-    // 4096-column chunk, half the loads per thread) for rows of 8192 and more
-    // (measured: 70B-shaped matrices at 16 tokens 5-13% faster, 2B-shaped
-    // ones 3% slower)
+    // two row tiles per workgroup once there are ~2 per CU; rows of 8192 and
+    // more stream through the LDS ring (measured 10-25% faster on 70B-shaped
+    // matrices at 4-16 tokens; no gain on 2560- and 6912-column rows)
     const int rt = kGlu || row_tiles >= 512 ? 2 : 1;
     const dim3 grid((unsigned)((row_tiles + rt - 1) / rt), (unsigned)((m + 15) / 16));
-    if (k >= 8192) {
-      if (rt == 2)
-        hipLaunchKernelGGL((k_gemv_lds<2, 8, 2, 1, kGlu>), grid, dim3(512), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
-      else
-        hipLaunchKernelGGL((k_gemv_lds<1, 8, 2, 1>), grid, dim3(512), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
+    if (k >= kRingMinK) {
+      // four row tiles (sixteen waves) per workgroup once there are ~8 per CU:
+      // half the activation bytes per weight byte (measured 34 -> 28 us for
+      // 16 tokens on a 57344 x 8192 matrix)
+      if (!kGlu && row_tiles >= 2048) {
+        const dim3 grid4((unsigned)((row_tiles + 3) / 4), (unsigned)((m + 15) / 16));
+        hipLaunchKernelGGL((k_gemv_ring<4>), grid4, dim3(1024), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
+      } else if (rt == 2) {
+        hipLaunchKernelGGL((k_gemv_ring<2, kGlu>), grid, dim3(512), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
+      } else {
+        hipLaunchKernelGGL((k_gemv_ring<1>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
+      }
     } else if (rt == 2) {
       hipLaunchKernelGGL((k_gemv_lds<2, 4, 4, 1, kGlu>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
     } else {

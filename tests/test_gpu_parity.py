@@ -204,7 +204,10 @@ def test_linear_brute_force_shapes(m, n, k):
                                    # 17..64 tokens in one workgroup (four token blocks), ragged chunk
                                    (40, 1000, 4160), (64, 8200, 320),
                                    # the same token counts on a matrix with many row tiles: the GEMM
-                                   (20, 32784, 128)])
+                                   (20, 32784, 128),
+                                   # 2..16 tokens on rows of 8192 and more: the LDS ring with 1, 2 and 4
+                                   # row tiles per workgroup, ragged last workgroup, partial last chunk
+                                   (3, 40, 8256), (16, 8208, 9216), (5, 32784, 8256), (16, 33, 16448)])
 def test_linear_multi_tile_workgroups(m, n, k):
     """Token blocks whose activation loads serve 2 or 4 row tiles per
     workgroup, with a ragged last workgroup."""
