@@ -22,7 +22,8 @@
 //     per row block, reused for the 4 token blocks;
 //   * dy's tile (64 tokens x 256 columns x 2 bytes) is copied to LDS by DMA,
 //     double-buffered; 16-byte chunk c of token row r is stored at chunk
-//     c ^ (r % 16), so the 16 tokens of a B read fall in distinct banks.
+//     c ^ lds_row_key(r), so the B reads of 16 tokens are free of bank
+//     conflicts.
 // Tails: rows of q^T past k and tokens past m are never stored; columns past
 // n read as zero gradient (and the trits there are multiplied by zero).
 //
@@ -113,13 +114,13 @@ __global__ __launch_bounds__(256, 2) void k_bwd_x(const uint8_t* __restrict__ pa
 
   // DMA: lane i of a 1 KiB load writes LDS bytes 16i.. of it = token row
   // 2 * load + i / 32, stored chunk i % 32, which holds source chunk
-  // (i % 32) ^ (row % 16)
+  // (i % 32) ^ lds_row_key(row)
   const int dma_row0 = wave * kXDma * 2 + (lane >> 5);
   auto load_x = [&](int s, uint4* dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < kXDma; ++j) {
       const int row = dma_row0 + 2 * j;
-      const int c = (lane & 31) ^ (row & 15);
+      const int c = (lane & 31) ^ lds_row_key(row);
       const uint32_t col_byte = (uint32_t)(s * kStepK * 2 + 16 * c);
       const uint32_t off = (s < full_steps || col_byte < row_bytes) ? (uint32_t)row * row_bytes + col_byte
                                                                      : kOutOfRange;
@@ -148,15 +149,16 @@ __global__ __launch_bounds__(256, 2) void k_bwd_x(const uint8_t* __restrict__ pa
   __syncthreads();
 
   auto compute = [&](const uint4* xbuf) __attribute__((always_inline)) {
-    // token row tb*16 + col; chunk 8*sub + 2*f + h stored at that ^ col
+    // token row tb*16 + col; chunk 8*sub + 2*f + h stored at that ^ key
     const uint4* xt = xbuf + col * kChunks;
+    const int key = lds_row_key(col);
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         uint4 b[kTB];
 #pragma unroll
-        for (int tb = 0; tb < kTB; ++tb) b[tb] = xt[tb * 16 * kChunks + ((8 * sub + 2 * f + h) ^ col)];
+        for (int tb = 0; tb < kTB; ++tb) b[tb] = xt[tb * 16 * kChunks + ((8 * sub + 2 * f + h) ^ key)];
 #pragma unroll
         for (int rb = 0; rb < kRB; ++rb) {
           const uint32_t c0 = ((h ? w_cur[rb].z : w_cur[rb].x) >> (2 * f)) & 0x03030303u;

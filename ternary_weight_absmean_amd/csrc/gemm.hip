@@ -22,9 +22,9 @@
 //   * the activation tile (tokens x 256 bytes) is shared by the four waves
 //     through LDS, double-buffered, and copied there by DMA (buffer loads
 //     that write LDS directly: no registers, no LDS store instructions);
-//     16-byte chunk c of token row r is stored at chunk c ^ (r % 16) of that
-//     row, so the 16 lanes of each phase of a 128-bit read (16 tokens, one
-//     chunk) hit 16 distinct 4-bank groups;
+//     16-byte chunk c of token row r is stored at chunk c ^ lds_row_key(r)
+//     of that row, so the 128-bit reads of 16 token rows are free of bank
+//     conflicts;
 //   * the MFMA A operand is the raw code c = q + 1 of one 2-bit field
 //     ((p >> 2f) & 0x03030303), so the product is sum c*x; the token's sum of
 //     x turns it into sum q*x.  The sums come from the B operands already in
@@ -114,13 +114,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* __restrict__ pac
   // Activation tiles go global -> LDS by DMA (buffer_load ... lds): lane i of
   // a load writes LDS bytes 16i..16i+15 of that load's 1 KiB, i.e. token row
   // 4*load + i/16, stored chunk i%16.  Stored chunk p of row r holds source
-  // chunk p ^ (r % 16), so the lane fetches that one.
+  // chunk p ^ lds_row_key(r), so the lane fetches that one.
   const int dma_row0 = wave * kXDma * 4 + (lane >> 4);
   auto load_x = [&](int s, uint4* dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < kXDma; ++j) {
       const int row = dma_row0 + 4 * j;
-      const int c = (lane & 15) ^ (row & 15);
+      const int c = (lane & 15) ^ lds_row_key(row);
       const uint32_t col_byte = (uint32_t)(s * kStepK + 16 * c);
       const uint32_t off = (s < full_steps || col_byte < kk) ? (uint32_t)row * kk + col_byte : kOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -159,13 +159,14 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* __restrict__ pac
   __syncthreads();
 
   auto compute = [&](const uint4* xbuf) __attribute__((always_inline)) {
-    // token row tb*16 + col, chunk 4*sub + f, stored at chunk (4*sub + f) ^ col
+    // token row tb*16 + col, chunk 4*sub + f, stored at chunk (4*sub + f) ^ key
     const uint4* xt = xbuf + col * kXRow;
+    const int key = lds_row_key(col);
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       v4i b[kTB];
 #pragma unroll
-      for (int tb = 0; tb < kTB; ++tb) b[tb] = as_v4i(xt[tb * 16 * kXRow + ((4 * sub + f) ^ col)]);
+      for (int tb = 0; tb < kTB; ++tb) b[tb] = as_v4i(xt[tb * 16 * kXRow + ((4 * sub + f) ^ key)]);
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) {
         v4i a;
