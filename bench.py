@@ -260,7 +260,7 @@ STACK_WORKLOAD = "bitnet-b1.58-2B-shaped decode stack, M=1"
 STACK_KERNEL = "k_bitlinear_m1"
 # kernel base name -> source file whose hash marks the stored counter figures as current
 KERNEL_SOURCES = {"k_bitlinear_m1": "gemv.hip", "k_bitlinear_fused": "gemv.hip", "k_gemv_direct": "gemv.hip",
-                  "k_gemv_lds": "gemv.hip", "k_gemm": "gemm.hip", "k_quant_act": "quant.hip",
+                  "k_gemv_lds": "gemv.hip", "k_gemv_ring": "gemv.hip", "k_gemm": "gemm.hip", "k_quant_act": "quant.hip",
                   "k_bwd_x": "backward.hip", "k_bwd_w": "backward.hip", "k_bwd_w_prep": "backward.hip"}
 # operations per MFMA instruction: int8 16 x 16 x 64 (the forward kernels),
 # bf16 16 x 16 x 32 (the backward kernels), two per multiply-add
@@ -326,13 +326,26 @@ def summarize(args):
         g["total"] += float(r["TotalDurationNs"])
         g["min"] = min(g["min"], float(r["MinNs"]))
         g["max"] = max(g["max"], float(r["MaxNs"]))
+    # the later half of each kernel's dispatches (the timed steps, after the
+    # warmup and the eager passes) from the per-dispatch trace
+    late = {}
+    trace = _find(args.stats, "kernel_trace.csv") if args.stats else None
+    if trace:
+        per = collections.defaultdict(list)
+        for r in _read_csv(trace):
+            per[_base_name(r["Kernel_Name"])].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        late = {k: sum(v[len(v) // 2:]) / len(v[len(v) // 2:]) for k, v in per.items() if v}
     if grouped:
         lines += ["## Kernel durations (--kernel-trace --stats; template instances summed)", "",
-                  "| kernel | calls | avg (us) | min (us) | max (us) | share of GPU time |", "|---|---|---|---|---|---|"]
+                  "The tracer separates dispatches (each kernel runs without its neighbours); the last column "
+                  "averages the later half of a kernel's dispatches.", "",
+                  "| kernel | calls | avg (us) | min (us) | max (us) | share of GPU time | avg, later half (us) |",
+                  "|---|---|---|---|---|---|---|"]
         total = sum(g["total"] for g in grouped.values())
         for base, g in grouped.items():
+            lh = f"{late[base] / 1e3:.3f}" if base in late else "-"
             lines.append(f"| {base} | {g['calls']} | {g['total'] / g['calls'] / 1e3:.3f} | {g['min'] / 1e3:.3f} | "
-                         f"{g['max'] / 1e3:.3f} | {100 * g['total'] / total:.1f}% |")
+                         f"{g['max'] / 1e3:.3f} | {100 * g['total'] / total:.1f}% | {lh} |")
         lines.append("")
     counters = collections.OrderedDict()  # counter -> {kernel: (avg value, avg duration ns, dispatches)}
     for d in args.pmc:
@@ -410,10 +423,13 @@ def summarize(args):
 
 
 def source_hash(kernel: str) -> str:
+    """Hash of the kernel's source file and the device helpers it includes."""
     import hashlib
-    path = os.path.join(ROOT, "ternary_weight_absmean_amd", "csrc", KERNEL_SOURCES[kernel])
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in (KERNEL_SOURCES[kernel], "device_util.h"):
+        with open(os.path.join(ROOT, "ternary_weight_absmean_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def stored_traffic(workload: str, kernel: str, algorithmic_bytes: float):
