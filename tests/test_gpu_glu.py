@@ -59,6 +59,8 @@ def test_pack_glu_matches_oracle(f, k):
     (3, 4096, 2560), (5, 48, 320), (8, 160, 2560), (16, 48, 1024),
     # quantizer + LDS-staged product (16- and 64-token blocks; eight waves from k = 8192)
     (9, 96, 6912), (17, 160, 640), (40, 96, 640), (64, 1040, 320), (3, 48, 6912), (5, 48, 8256),
+    # 64-token workgroups (512 row tiles of the gate+up matrix, more than 32 tokens)
+    (40, 4096, 320),
     # quantizer + GEMM path: past the product's token limits, ragged token blocks
     (70, 96, 1088), (130, 272, 192),
     # one token given as int8 (bl_linear_glu): four row tiles per workgroup, ragged last

@@ -207,7 +207,10 @@ def test_linear_brute_force_shapes(m, n, k):
                                    (20, 32784, 128),
                                    # 2..16 tokens on rows of 8192 and more: the LDS ring with 1, 2 and 4
                                    # row tiles per workgroup, ragged last workgroup, partial last chunk
-                                   (3, 40, 8256), (16, 8208, 9216), (5, 32784, 8256), (16, 33, 16448)])
+                                   (3, 40, 8256), (16, 8208, 9216), (5, 32784, 8256), (16, 33, 16448),
+                                   # 17..64 tokens: 16-token workgroups (LDS-staged, and the ring with a
+                                   # ragged last token block), 64-token workgroups from 512 row tiles
+                                   (24, 600, 2560), (40, 100, 8256), (33, 8208, 640)])
 def test_linear_multi_tile_workgroups(m, n, k):
     """Token blocks whose activation loads serve 2 or 4 row tiles per
     workgroup, with a ragged last workgroup."""
