@@ -38,6 +38,8 @@
 // scaled by 1, 4, 16, 16 and are divided exactly at the end (20 VALU ops per
 // 1 KiB group instead of 44 for a signed table lookup).  The others convert
 // codes to signed trits with v_perm.
+#include <utility>
+
 #include "device_util.h"
 #include "internal.h"
 
@@ -819,14 +821,25 @@ __global__ __launch_bounds__(kW * 64) void k_gemv_lds(const uint4* __restrict__ 
 }
 
 
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>): a loop
+// whose index is a compile-time constant in every copy of the body.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
+
 // s_waitcnt immediate that waits until at most n vector memory operations of
 // this wave are outstanding (expcnt and lgkmcnt left at their maxima).
 constexpr int vmcnt_at_most(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
 // Product with int8 activations given, 2 <= m <= 16 tokens, long rows: the
-// token block's activations stream through a ring of four 1024-column LDS
-// buffers filled by DMA (buffer loads that write LDS, no registers) three
-// chunks ahead, so the loads of three chunks are in flight while one is
+// token block's activations stream through a ring of kS 1024-column LDS
+// buffers filled by DMA (buffer loads that write LDS, no registers) kS - 1
+// chunks ahead, so the loads of kS - 1 chunks are in flight while one is
 // multiplied; one barrier per chunk.  kW = 4 * kRT waves: wave w multiplies
 // 256-column group w % 4 of every chunk for row tile w / 4 of the workgroup
 // (one non-temporal 1 KiB weight load per chunk, in a register ring beside
@@ -839,7 +852,7 @@ constexpr int vmcnt_at_most(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((
 // ring size so that every buffer is named at compile time.
 // kGlu (kRT = 2): gate+up matrix with alternating gate/up row tiles; wave 0
 // gates the tile pair into y_out ([m][n / 2]).
-template <int kRT, bool kGlu = false>
+template <int kRT, bool kGlu = false, int kS = 4>
 __global__ __launch_bounds__(kRT * 256) void k_gemv_ring(const uint4* __restrict__ packed,
                                                         const float* __restrict__ gamma_ptr,
                                                         const int8_t* __restrict__ xq,
@@ -852,11 +865,23 @@ __global__ __launch_bounds__(kRT * 256) void k_gemv_ring(const uint4* __restrict
   constexpr int kDma = 16 / kW;      // token rows this wave copies per chunk, one 1 KiB DMA each
   static_assert(16 % kW == 0, "the 16 token rows split evenly over the waves");
   static_assert(!kGlu || kRT == 2, "a gate tile and its up tile per workgroup");
-  __shared__ uint4 xs0[16 * kPieces];  // the ring: four distinct LDS objects
-  __shared__ uint4 xs1[16 * kPieces];
-  __shared__ uint4 xs2[16 * kPieces];
-  __shared__ uint4 xs3[16 * kPieces];
+  static_assert(kS >= 3 && kS <= 8, "ring depth");
+  // the ring: kS distinct LDS objects (each named at compile time below)
+  __shared__ uint4 xs0[16 * kPieces], xs1[16 * kPieces], xs2[16 * kPieces], xs3[16 * kPieces];
+  __shared__ uint4 xs4[kS > 4 ? 16 * kPieces : 1], xs5[kS > 5 ? 16 * kPieces : 1];
+  __shared__ uint4 xs6[kS > 6 ? 16 * kPieces : 1], xs7[kS > 7 ? 16 * kPieces : 1];
   __shared__ v4i partial[kRT][4][64];
+  auto ring = [&](auto slot) -> uint4* {
+    constexpr int i = decltype(slot)::value;
+    if constexpr (i == 0) return xs0;
+    else if constexpr (i == 1) return xs1;
+    else if constexpr (i == 2) return xs2;
+    else if constexpr (i == 3) return xs3;
+    else if constexpr (i == 4) return xs4;
+    else if constexpr (i == 5) return xs5;
+    else if constexpr (i == 6) return xs6;
+    else return xs7;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -919,33 +944,31 @@ __global__ __launch_bounds__(kRT * 256) void k_gemv_ring(const uint4* __restrict
   // MFMA on its side of it.)
   auto step = [&](int c, const uint4* rd, const uint4& w_rd, uint4* wr, uint4& w_wr) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(2 * (kDma + 1)) & ~(15 << 8));  // and lgkmcnt(0)
+    __builtin_amdgcn_s_waitcnt(vmcnt_at_most((kS - 2) * (kDma + 1)) & ~(15 << 8));  // and lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     __builtin_amdgcn_sched_barrier(0);
-    load_chunk(c + 3, wr, w_wr);
+    load_chunk(c + kS - 1, wr, w_wr);
     // nothing of this chunk's arithmetic moves above the barrier (its weight
     // register would then be waited for early, with the later loads)
     __builtin_amdgcn_sched_barrier(0);
     compute(rd, w_rd);
   };
   // issue order as in the loop: each chunk's DMA, then its weights
-  uint4 w0, w1, w2, w3;
-  load_chunk(0, xs0, w0);
-  __builtin_amdgcn_sched_barrier(0);
-  load_chunk(1, xs1, w1);
-  __builtin_amdgcn_sched_barrier(0);
-  load_chunk(2, xs2, w2);
-  __builtin_amdgcn_sched_barrier(0);
+  uint4 w[kS];
+  static_for<kS - 1>([&](auto i) {
+    load_chunk(decltype(i)::value, ring(i), w[decltype(i)::value]);
+    __builtin_amdgcn_sched_barrier(0);
+  });
   // chunks past the last read as zero: the ring runs in whole turns (at
   // least one: k > 0, and the loads above stay ahead of the loop)
   int c = 0;
   do {
-    step(c, xs0, w0, xs3, w3);
-    step(c + 1, xs1, w1, xs0, w0);
-    step(c + 2, xs2, w2, xs1, w1);
-    step(c + 3, xs3, w3, xs2, w2);
-    c += 4;
+    static_for<kS>([&](auto i) {
+      constexpr int cur = decltype(i)::value, prev = (cur + kS - 1) % kS;
+      step(c + cur, ring(i), w[cur], ring(std::integral_constant<int, prev>{}), w[prev]);
+    });
+    c += kS;
   } while (c < chunks);
   __builtin_amdgcn_s_waitcnt(0);  // the last (all-zero) loads have landed before the wave can exit
 
