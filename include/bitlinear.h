@@ -72,9 +72,9 @@ typedef enum {
  * Returns 0 for an invalid shape. */
 size_t bl_packed_bytes(int64_t n, int64_t k);
 
-/* Device workspace needed by bl_ternarize_pack: a fixed 512 KiB (256
- * exponent bins of 64-bit integers for each of up to 256 workgroups of the
- * absmean pass).  Returns 0 for an invalid shape. */
+/* Device workspace needed by bl_ternarize_pack: a fixed 2 KiB (256 exponent
+ * bins of 64-bit integers, into which the absmean pass adds).  Returns 0 for
+ * an invalid shape. */
 size_t bl_ternarize_pack_workspace_bytes(int64_t n, int64_t k);
 
 /* Weight preparation [P1]: gamma = mean |w| over all n*k weights, computed

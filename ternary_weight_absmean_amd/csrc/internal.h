@@ -13,9 +13,10 @@ constexpr int kTileCols = 64;
 constexpr int kTileBytes = 256;
 
 // Weight packer (absmean exponent bins -> exact gamma -> ternarize + pack).
-// The workspace holds 256 exponent bins (u64) per absmean workgroup.
+// The workspace holds the 256 exponent bins (u64) of the whole matrix; the
+// absmean workgroups add into them with integer atomics (cleared first).
 constexpr int kAbsmeanMaxBlocks = 256;
-constexpr size_t kPackWorkspaceBytes = (size_t)kAbsmeanMaxBlocks * 256 * sizeof(unsigned long long);
+constexpr size_t kPackWorkspaceBytes = 256 * sizeof(unsigned long long);
 hipError_t launch_absmean_bins(const float* w, int64_t count, unsigned long long* ws, hipStream_t s);
 hipError_t launch_gamma_fold(const unsigned long long* ws, int64_t count, float* gamma, hipStream_t s);
 // glu_f > 0: w is [2 * glu_f][k] gate rows then up rows, packed with

@@ -17,10 +17,12 @@
 // and rounds it once to fp32 (nearest, ties to even).
 //
 // Kernels (all HBM-bound streaming passes except the fold):
+//   k_zero_bins        clear the 256 bins of the workspace
 //   k_absmean_bins     read w once; exponent bins per workgroup (registers
-//                      and LDS), written to the workspace (no global atomics)
-//   k_gamma_fold       sum the workgroups' bins, exact mean -> gamma (device
-//                      memory; no host readback)
+//                      and LDS), added into the workspace's bins (64-bit
+//                      integer atomics, 256 per workgroup)
+//   k_gamma_fold       exact mean of the binned sum -> gamma (device memory;
+//                      no host readback)
 //   k_ternarize_pack   read w again; lane per float4, 16 lanes per 64-column
 //                      row segment; IEEE fp32 divide, round-half-even, clamp
 //   k_unpack           packed -> int8 trits (inspection helper)
@@ -50,11 +52,12 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
 // wave's first values; that register equals sum sig * 2^(e - e0), i.e. the
 // bin e0 contribution of the window, and is split into its low and high 32
 // bits for bins e0 and e0 + 32.  Values outside the window (and subnormals)
-// go to LDS bins by atomic add.  Each workgroup writes its 256 bins to its
-// row of the workspace; the fold adds the rows.  All additions are of
-// integers, so the result does not depend on the grid or the order.  At
-// most 2^17 threads and count <= 2^39: at most 2^22 values per lane of at
-// most 2^39 each, and no bin total exceeds count * 2^24 + 2^49 < 2^64.
+// go to LDS bins by atomic add.  Each workgroup then adds its 256 bins into
+// the workspace's bins (cleared by k_zero_bins) with 64-bit integer atomics.
+// All additions are of integers, so the result does not depend on the grid
+// or the order.  At most 2^17 threads and count <= 2^39: at most 2^22 values
+// per lane of at most 2^39 each, and no bin total exceeds
+// count * 2^24 + 2^49 < 2^64.
 __global__ __launch_bounds__(kBinThreads) void k_absmean_bins(const float4* __restrict__ w4, int64_t n4,
                                                                unsigned long long* __restrict__ ws) {
   __shared__ unsigned long long lbins[kBins];
@@ -109,8 +112,10 @@ __global__ __launch_bounds__(kBinThreads) void k_absmean_bins(const float4* __re
     }
   }
   __syncthreads();
-  if (tid < kBins) ws[(int64_t)blockIdx.x * kBins + tid] = lbins[tid];
+  if (tid < kBins && lbins[tid]) atomicAdd(&ws[tid], lbins[tid]);
 }
+
+__global__ __launch_bounds__(kBins) void k_zero_bins(unsigned long long* __restrict__ ws) { ws[threadIdx.x] = 0ull; }
 
 // ---------------------------------------------------------------- exact fold
 
@@ -139,39 +144,19 @@ __device__ __forceinline__ uint32_t div_step(unsigned long long cur, unsigned lo
   return (uint32_t)q;
 }
 
-// One workgroup: four threads per exponent e add its bins over the absmean
-// workgroups, and thread e adds the value bins[e] * 2^(max(e,1) - 1) into 16-bit limbs
-// of X = sum |w| * 2^149 (LDS atomics; each limb sum stays below 2^25); one
-// thread then propagates the carries, divides by the element count (long
-// division by limbs) and rounds the quotient once to fp32, nearest with
-// ties to even.
-constexpr int kFoldThreads = 1024;  // four threads per exponent share the workgroup rows
-
-__global__ __launch_bounds__(kFoldThreads) void k_gamma_fold(const unsigned long long* __restrict__ ws, int blocks,
-                                                              unsigned long long count, float* __restrict__ gamma) {
+// One workgroup of 256 threads: thread e adds the value bins[e] *
+// 2^(max(e,1) - 1) into 16-bit limbs of X = sum |w| * 2^149 (LDS atomics;
+// each limb sum stays below 2^25); one thread then propagates the carries,
+// divides by the element count (long division by limbs) and rounds the
+// quotient once to fp32, nearest with ties to even.
+__global__ __launch_bounds__(kBins) void k_gamma_fold(const unsigned long long* __restrict__ ws,
+                                                      unsigned long long count, float* __restrict__ gamma) {
   __shared__ uint32_t xl[kLimbs];
-  __shared__ unsigned long long part[kFoldThreads / kBins][kBins];
-  const int e = threadIdx.x % kBins;
-  const int p = threadIdx.x / kBins;
-  constexpr int kParts = kFoldThreads / kBins;
-  if (threadIdx.x < kLimbs) xl[threadIdx.x] = 0;
-  unsigned long long v = 0;
-  {
-    int b = p;
-    for (; b + 15 * kParts < blocks; b += 16 * kParts) {  // 16 loads in flight
-      unsigned long long t[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) t[j] = ws[(int64_t)(b + j * kParts) * kBins + e];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) v += t[j];
-    }
-    for (; b < blocks; b += kParts) v += ws[(int64_t)b * kBins + e];
-  }
-  part[p][e] = v;
+  const int e = threadIdx.x;
+  if (e < kLimbs) xl[e] = 0;
+  const unsigned long long v = ws[e];
   __syncthreads();
-#pragma unroll
-  for (int q = 1; q < kParts; ++q) v += part[q][e];
-  if (p == 0 && v != 0 && e < kBins - 1) {
+  if (v != 0 && e < kBins - 1) {
     const int sh = e ? e - 1 : 0;
     const int q = sh >> 4, r = sh & 15;
     const unsigned long long lo = v << r;
@@ -336,14 +321,14 @@ int absmean_blocks(int64_t count) {
 }
 
 hipError_t launch_absmean_bins(const float* w, int64_t count, unsigned long long* ws, hipStream_t s) {
+  hipLaunchKernelGGL(k_zero_bins, dim3(1), dim3(kBins), 0, s, ws);
   hipLaunchKernelGGL(k_absmean_bins, dim3((unsigned)absmean_blocks(count)), dim3(kBinThreads), 0, s,
                      reinterpret_cast<const float4*>(w), count / 4, ws);
   return hipGetLastError();
 }
 
 hipError_t launch_gamma_fold(const unsigned long long* ws, int64_t count, float* gamma, hipStream_t s) {
-  hipLaunchKernelGGL(k_gamma_fold, dim3(1), dim3(kFoldThreads), 0, s, ws, absmean_blocks(count),
-                     (unsigned long long)count, gamma);
+  hipLaunchKernelGGL(k_gamma_fold, dim3(1), dim3(kBins), 0, s, ws, (unsigned long long)count, gamma);
   return hipGetLastError();
 }
 

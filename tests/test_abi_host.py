@@ -37,7 +37,7 @@ def test_sizes():
     assert bl.bl_packed_bytes(0, 64) == 0
     assert bl.bl_packed_bytes(16, 63) == 0
     assert bl.bl_packed_bytes(16, 1 << 23) == 0
-    WS = 256 * 256 * 8
+    WS = 256 * 8
     assert bl.bl_ternarize_pack_workspace_bytes(57344, 8192) == WS
     assert bl.bl_ternarize_pack_workspace_bytes(16, 64) == WS
     assert bl.bl_ternarize_pack_workspace_bytes(0, 64) == 0
@@ -45,7 +45,7 @@ def test_sizes():
 
 def test_ternarize_pack_validation():
     f = lib.bl_ternarize_pack
-    WS = 256 * 256 * 8
+    WS = 256 * 8
     assert f(None, 16, 64, FAKE, FAKE, FAKE, WS, None) == BL_ERR_NULL
     assert f(FAKE, 16, 64, FAKE, FAKE, None, WS, None) == BL_ERR_NULL
     assert f(FAKE, 0, 64, FAKE, FAKE, FAKE, WS, None) == BL_ERR_SHAPE
@@ -132,7 +132,7 @@ def test_bitlinear_validation():
 
 
 def test_glu_entry_points_validation():
-    WS = 256 * 256 * 8
+    WS = 256 * 8
     pack = lib.bl_ternarize_pack_glu
     assert pack(None, 16, 64, FAKE, FAKE, FAKE, WS, None) == BL_ERR_NULL
     assert pack(FAKE, 24, 64, FAKE, FAKE, FAKE, WS, None) == BL_ERR_SHAPE   # f not a multiple of 16
