@@ -329,7 +329,10 @@ def summarize(args):
     # the later half of each kernel's dispatches (the timed steps, after the
     # warmup and the eager passes) from the per-dispatch trace
     late = {}
-    trace = _find(args.stats, "kernel_trace.csv") if args.stats else None
+    try:
+        trace = _find(args.stats, "kernel_trace.csv") if args.stats else None
+    except FileNotFoundError:  # a stats directory without the per-dispatch trace
+        trace = None
     if trace:
         per = collections.defaultdict(list)
         for r in _read_csv(trace):
