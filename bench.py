@@ -103,8 +103,7 @@ def main() -> int:
     # ------------------------------------------------------------ weights, once
     ws = torch.empty(bl.bl_ternarize_pack_workspace_bytes(2560, 2560), dtype=torch.uint8, device=dev)
     linears = []
-    pack_ms = 0.0
-    w_bytes = 0
+    layer0_w = []  # fp32 weights of layer 0, kept for the packer's timing
     outliers = {k: datagen.outlier_columns(wl, k, datagen.STACK_2B_OUTLIERS) for _, k, _ in proj}
     for layer in range(args.layers):
         for pi, (name, k, n) in enumerate(proj):
@@ -112,13 +111,9 @@ def main() -> int:
             wd = torch.from_numpy(w).to(dev)
             packed = torch.empty(bl.bl_packed_bytes(n, k), dtype=torch.uint8, device=dev)
             gamma = torch.empty(1, dtype=torch.float32, device=dev)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
             bl.bl_ternarize_pack(wd, packed, gamma, ws)
-            e1.record()
-            e1.synchronize()
-            pack_ms += e0.elapsed_time(e1)
-            w_bytes += wd.numel() * 4
+            if layer == 0:
+                layer0_w.append((wd, n, k))
             del wd
             x = datagen.activations_bf16(datagen.stream_id(wl, layer, pi, datagen.TENSOR_X), m, k, outliers[k],
                                          datagen.STACK_2B_OUTLIER_MULT)
@@ -216,6 +211,27 @@ def main() -> int:
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args, outliers)
 
+    # the packer (offline for decode): layer 0's four matrices re-packed,
+    # timed as graph replays (launch gaps spread over 5 calls per replay)
+    pk_out = [(torch.empty(bl.bl_packed_bytes(n, k), dtype=torch.uint8, device=dev),
+               torch.empty(1, dtype=torch.float32, device=dev)) for _, n, k in layer0_w]
+
+    def pack_layer0():
+        s = vp(torch.cuda.current_stream().cuda_stream)
+        for (wd, n, k), (pk, gm) in zip(layer0_w, pk_out):
+            rc = lib.bl_ternarize_pack(vp(wd.data_ptr()), n, k, vp(pk.data_ptr()), vp(gm.data_ptr()),
+                                       vp(ws.data_ptr()), ws.numel(), s)
+            if rc:
+                raise RuntimeError(bl.bl_status_string(rc))
+
+    pack_ms = _graph_time_ms(torch, _repeat(pack_layer0, 5), 5) / 5
+    w0_bytes = sum(4 * n * k for _, n, k in layer0_w)
+    packer = {"matrices": len(layer0_w), "fp32_MB": round(w0_bytes / 1e6, 1), "ms": round(pack_ms, 4),
+              "us_per_matrix": round(1000 * pack_ms / len(layer0_w), 2),
+              "GBps_fp32_read": round(w0_bytes / (pack_ms * 1e-3) / 1e9, 1),
+              "note": "layer 0 of the stack; each weight is read twice (absmean pass, ternarize pass)"}
+    del layer0_w, pk_out
+
     result = {
         "metric": METRIC,
         "value": round(tokens_per_s, 2),
@@ -244,8 +260,7 @@ def main() -> int:
                      "algorithmic_bytes_per_launch": round(avg_bytes, 1),
                      "measured_hbm_reference": stream,
                      "frac_of_measured_read": round(gemv_gbps / stream["read_GBps"], 4)},
-        "packer": {"weights": len(linears), "fp32_GB": round(w_bytes / 1e9, 3), "ms": round(pack_ms, 3),
-                   "GBps_fp32_read": round(w_bytes / (pack_ms * 1e-3) / 1e9, 1)},
+        "packer": packer,
         "cpu_baseline": cpu,
         "extras": extras,
     }
