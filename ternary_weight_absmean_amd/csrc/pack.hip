@@ -24,7 +24,8 @@
 //   k_gamma_fold       exact mean of the binned sum -> gamma (device memory;
 //                      no host readback)
 //   k_ternarize_pack   read w again; lane per float4, 16 lanes per 64-column
-//                      row segment; IEEE fp32 divide, round-half-even, clamp
+//                      row segment; the rounding of w / (gamma + 1e-5) as an
+//                      exact threshold test
 //   k_unpack           packed -> int8 trits (inspection helper)
 #include "device_util.h"
 #include "internal.h"
@@ -224,44 +225,65 @@ constexpr int kPackThreads = 256;
 // four lanes j = d, d+4, d+8, d+12 of dword d are OR-combined with DPP row
 // rotations, and lanes 0..3 of each 16 store the dwords.  Rows past n get
 // code 1 (trit 0).  Code = q + 1, q = clamp(round_half_even(w / (gamma +
-// 1e-5)), -1, 1) with IEEE fp32 division.
+// 1e-5)), -1, 1) with IEEE fp32 division, evaluated as the equivalent
+// threshold test below.  Each thread handles kPackIter float4 slots, all
+// loads issued first.
 // glu_f > 0: w is a gate+up matrix [2 * glu_f][k] (gate rows first) and the
 // packed row tiles alternate gate and up: packed tile 2t holds gate rows
 // 16t..16t+15, tile 2t + 1 the up rows 16t..16t+15 (glu_f % 16 == 0).
+constexpr int kPackIter = 4;  // float4 loads per thread, issued together
 __global__ __launch_bounds__(kPackThreads) void k_ternarize_pack(const float4* __restrict__ w4, int64_t n, int64_t k,
                                                                   const float* __restrict__ gamma_ptr,
                                                                   uint32_t* __restrict__ packed, int64_t glu_f) {
   const int64_t k4 = k / 4;
   const int64_t n_pad = (n + kTileRows - 1) / kTileRows * kTileRows;
-  const int64_t idx = (int64_t)blockIdx.x * kPackThreads + threadIdx.x;  // float4 index in the padded matrix
-  if (idx >= n_pad * k4) return;  // whole 16-lane groups leave together (k4 is a multiple of 16)
-  const int64_t row = idx / k4;
-  const int64_t c4 = idx % k4;  // float4 within the row
-  const int j = (int)(c4 & 15);  // lane within the tile row
-  const int64_t kt = c4 >> 4;
-  const float denom = *gamma_ptr + 1e-5f;
-  uint32_t part = 0;
-  if (row < n) {
-    const float4 v = w4[idx];
-    const float c[4] = {v.x, v.y, v.z, v.w};
+  const int64_t total = n_pad * k4;  // float4 slots of the padded matrix
+  // q = clamp(rint(fl(w / d)), -1, 1) with d = fl(gamma + 1e-5) is +-1 exactly
+  // when fl(|w| / d) > 0.5 (0.5 itself rounds to 0, ties to even).  The fp32
+  // value above d / 2 is d / 2 + ulp(d / 2), whose quotient is 0.5 + 2^-24 / m
+  // (m in [1, 2) the significand of d): beyond the midpoint 0.5 + 2^-25, so it
+  // rounds above 0.5; and |w| <= d / 2 gives a quotient of at most 0.5.  So
+  // for finite w the code is sign(w) when |w| > d / 2 (exact in fp32) and 0
+  // otherwise -- the same bits as the correctly rounded division.
+  const float half_d = (*gamma_ptr + 1e-5f) * 0.5f;
+  int64_t idx[kPackIter];
+  float4 v[kPackIter];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float r = fminf(fmaxf(__builtin_rintf(c[i] / denom), -1.0f), 1.0f);  // IEEE division, then RNE
-      part |= (uint32_t)((int)r + 1) << (8 * i + 2 * (j >> 2));
+  for (int it = 0; it < kPackIter; ++it) {
+    idx[it] = ((int64_t)blockIdx.x * kPackIter + it) * kPackThreads + threadIdx.x;
+    const bool real = idx[it] < total && idx[it] / k4 < n;
+    v[it] = w4[real ? idx[it] : 0];
+  }
+#pragma unroll
+  for (int it = 0; it < kPackIter; ++it) {
+    if (idx[it] >= total) break;  // whole 16-lane groups leave together (k4 is a multiple of 16)
+    const int64_t row = idx[it] / k4;
+    const int64_t c4 = idx[it] % k4;  // float4 within the row
+    const int j = (int)(c4 & 15);     // lane within the tile row
+    const int64_t kt = c4 >> 4;
+    uint32_t part;
+    if (row < n) {
+      const float c[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
+      part = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t code = fabsf(c[i]) > half_d ? (c[i] < 0.0f ? 0u : 2u) : 1u;
+        part |= code << (8 * i + 2 * (j >> 2));
+      }
+    } else {
+      part = 0x01010101u << (2 * (j >> 2));
     }
-  } else {
-    part = 0x01010101u << (2 * (j >> 2));
+    // OR over the four lanes of the same dword (lane offsets 4 and 8 within the 16-lane row)
+    part |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)part, 0x124, 0xF, 0xF, false);  // row_ror:4
+    part |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)part, 0x128, 0xF, 0xF, false);  // row_ror:8
+    int64_t prow = row;  // row of the packed matrix
+    if (glu_f > 0) {
+      const bool up = row >= glu_f;
+      const int64_t r = up ? row - glu_f : row;
+      prow = (r / kTileRows) * (2 * kTileRows) + (up ? kTileRows : 0) + r % kTileRows;
+    }
+    if (j < 4) packed[(((prow / kTileRows) * (k / kTileCols) + kt) * kTileRows + (prow % kTileRows)) * 4 + j] = part;
   }
-  // OR over the four lanes of the same dword (lane offsets 4 and 8 within the 16-lane row)
-  part |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)part, 0x124, 0xF, 0xF, false);  // row_ror:4
-  part |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)part, 0x128, 0xF, 0xF, false);  // row_ror:8
-  int64_t prow = row;  // row of the packed matrix
-  if (glu_f > 0) {
-    const bool up = row >= glu_f;
-    const int64_t r = up ? row - glu_f : row;
-    prow = (r / kTileRows) * (2 * kTileRows) + (up ? kTileRows : 0) + r % kTileRows;
-  }
-  if (j < 4) packed[(((prow / kTileRows) * (k / kTileCols) + kt) * kTileRows + (prow % kTileRows)) * 4 + j] = part;
 }
 
 // Packed q^T ([k][n]) from packed q ([n][k]), n % 64 == 0.  A workgroup
@@ -336,7 +358,7 @@ hipError_t launch_ternarize_pack(const float* w, int64_t n, int64_t k, const flo
                                  hipStream_t s, int64_t glu_f) {
   const int64_t n_pad = (n + kTileRows - 1) / kTileRows * kTileRows;
   const int64_t threads = n_pad * (k / 4);
-  const int64_t blocks = (threads + kPackThreads - 1) / kPackThreads;
+  const int64_t blocks = (threads + kPackThreads * kPackIter - 1) / (kPackThreads * kPackIter);
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_ternarize_pack, dim3((unsigned)blocks), dim3(kPackThreads), 0, s,
                      reinterpret_cast<const float4*>(w), n, k, gamma, reinterpret_cast<uint32_t*>(packed), glu_f);

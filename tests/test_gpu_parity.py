@@ -96,6 +96,35 @@ def test_pack_small_and_ragged(n, k):
     check_pack(w)
 
 
+def test_pack_rounding_boundary_at_final_gamma():
+    """Weights at and next to the rounding boundary d / 2 (d = gamma + 1e-5)
+    of the matrix's own final gamma: the inserted values change gamma, so
+    they are placed again until gamma no longer moves.  The oracle divides
+    and rounds; the packed codes must agree bit for bit."""
+    rng = np.random.default_rng(77)
+    n, k = 64, 1024
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    pos = rng.choice(n * k, size=208, replace=False)
+    near = rng.uniform(0.999, 1.001, size=200)
+    signs = np.where(rng.random(200) < 0.5, -1.0, 1.0)
+    g = None
+    for _ in range(20):
+        g = oracle.absmean(w)
+        d = np.float32(np.float32(g) + np.float32(1e-5))
+        h = np.float32(d * np.float32(0.5))
+        up, down = np.nextafter(h, np.float32(np.inf)), np.nextafter(h, np.float32(0))
+        vals = np.concatenate([[h, -h, up, -up, down, -down, d, np.float32(1.5) * d],
+                               (h * near * signs).astype(np.float32)]).astype(np.float32)
+        w.ravel()[pos] = vals
+        if oracle.absmean(w) == g:
+            break
+    assert oracle.absmean(w) == g, "gamma did not settle"
+    q = oracle.ternarize(w, g).ravel()[pos]
+    assert (q == 0).any() and (q != 0).any()  # the inserted values straddle the boundary
+    assert list(q[:6]) == [0, 0, 1, -1, 0, 0]
+    check_pack(w)
+
+
 def test_pack_gamma_exotic_values():
     rng = np.random.default_rng(4)
     cases = [
