@@ -1156,9 +1156,10 @@ M1Config m1_config_glu(int64_t m, int64_t groups, int64_t row_tiles) {
 
 M1Config m1_config(int64_t m, int64_t groups, int64_t row_tiles) {
   // Several tokens: every workgroup quantizes all of them, which pays off
-  // only for short rows and few row tiles (measured: rows of 2560 with 160
-  // or 240 row tiles; not 6912-column rows or 864+ row tiles).
-  if (m > 1 && (m > 4 || row_tiles >= 512)) return M1Config{};
+  // for short rows (measured: rows of 2560 with 160 or 240 row tiles, and
+  // with 864 row tiles at 3-4 tokens, 7.3 -> 6.8 us; not at 2 tokens, where
+  // the block-quantizing kernel is faster, nor on 6912-column rows).
+  if (m > 1 && (m > 4 || (row_tiles >= 512 && m < 3))) return M1Config{};
   // two row tiles per workgroup (the quantized tokens are reused) for short
   // rows once there are more than ~2 tiles per CU, for longer rows once there
   // are ~4 (measured on 8192-column rows: 5.6 TB/s against 5.1 with one)
