@@ -1173,13 +1173,19 @@ M1Config m1_config(int64_t m, int64_t groups, int64_t row_tiles) {
 }  // namespace
 
 // Every workgroup of k_bitlinear_fused quantizes its whole token block, so
-// it pays off while m * k is small (up to 8 tokens of 2560, 4 of 6912);
-// larger blocks go through the quantizer and k_gemv_lds.  k_bitlinear_m1
+// it pays off while m * k is small (up to 8 tokens of 2560, 4 of 6912) and
+// the matrix has few row tiles; larger blocks go through the quantizer and
+// k_gemv_lds.  k_bitlinear_m1
 // takes one token, and up to 4 on small matrices, whenever it applies.
 bool gemv_fused_applies(int64_t m, int64_t n, int64_t k) {
   if (m < 1 || m > 16) return false;
-  if (m1_config(m, (k / kTileCols + 3) / 4, (n + kTileRows - 1) / kTileRows).kernel) return true;
+  const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
+  if (m1_config(m, (k / kTileCols + 3) / 4, row_tiles).kernel) return true;
   if (m > 1 && m * k > kFusedMaxTokenColumns) return false;
+  // the quantizer + product launch pair is faster for more than 8 tokens
+  // (rows of 2560, 160-240 row tiles: 5.7 against 7.9 us at 10-12 tokens),
+  // and from 5 tokens on matrices of 512+ row tiles (7.5 against 8.8 us)
+  if (m > 8 || (m > 4 && row_tiles >= 512)) return false;
   return fused_plan(m, 1, k).rt > 0;
 }
 

@@ -375,7 +375,9 @@ def test_linear_is_deterministic():
                                    # single-token (k > 10240) with two row tiles, ragged last workgroup and group
                                    (1, 530, 16384), (7, 70, 16448), (16, 40, 32768), (1, 16400, 10304),
                                    (3, 48, 2560), (4, 3840, 2560), (5, 40, 6912), (16, 64, 1024), (16, 31, 2560),
-                                   (17, 40, 2560), (64, 100, 2560), (4, 16, 28672)])
+                                   (17, 40, 2560), (64, 100, 2560), (4, 16, 28672),
+                                   # block-quantizing kernel up to 8 tokens on few row tiles; past it
+                                   (6, 240, 2560), (8, 160, 2560), (10, 240, 2560), (6, 1040, 2560)])
 def test_bitlinear_matches_oracle(m, n, k):
     """bl_bitlinear (fused quantize + product where it fits, two kernels
     otherwise) against the oracle's quantizer, product and rescale."""
