@@ -74,7 +74,7 @@ def main() -> int:
             return 2
         return PROFILE_CASES[args.profile](args)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the BitLinear path runs on a single MI355X).", file=sys.stderr)
         return 2
 
