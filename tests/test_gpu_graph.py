@@ -92,3 +92,38 @@ def test_graph_replays_match_eager():
             a, b = eager[name].view(torch.uint8), static[name].view(torch.uint8)
             assert torch.equal(a, b), f"replay {r}: {name} differs in {(a != b).sum().item()} bytes"
         assert float(junk) > 0
+
+
+def test_two_streams_do_not_interfere():
+    """The library keeps no state between calls (workspaces are the caller's):
+    the packer and the products running on two streams at once give the
+    results of running them one after the other."""
+    rng = np.random.default_rng(22)
+    n, k = 3840, 2560
+    ws = [f32((rng.standard_normal((n, k)) * 0.02).astype(np.float32)) for _ in range(2)]
+    xs = [bf16(datagen.activations_bf16(int(rng.integers(1 << 40)), m, k)) for m in (1, 16)]
+
+    def chain(w, x1, x16):
+        packed, gamma = bl.bl_ternarize_pack(w)
+        out = [packed, gamma]
+        for _ in range(3):
+            acc1, y1, _, _ = bl.bl_bitlinear(packed, gamma, x1, n)
+            acc16, y16, _, _ = bl.bl_bitlinear(packed, gamma, x16, n)
+            out += [acc1, y1, acc16, y16]
+        return out
+
+    say("streams: one after the other")
+    want = [chain(w, xs[0], xs[1]) for w in ws]
+    torch.cuda.synchronize()
+    say("streams: two at once")
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    got = [None, None]
+    for i in (0, 1):
+        streams[i].wait_stream(torch.cuda.current_stream())
+    for i in (0, 1):
+        with torch.cuda.stream(streams[i]):
+            got[i] = chain(ws[i], xs[0], xs[1])
+    torch.cuda.synchronize()
+    for i in (0, 1):
+        for a, b in zip(want[i], got[i]):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
