@@ -817,6 +817,17 @@ def measure_extras(args, linears, lib):
             entry["frac_of_int8_mfma_peak"] = round(ops / (ms * 1e-3) / 1e12 / MFMA_I8_PEAK_TOPS, 4)
         else:
             entry["frac_of_hbm_peak"] = round(layer_bytes * n_layers / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+            # each projection alone over the 80 copies (same launches, same copies)
+            per = {}
+            for name_p, k_p, n_p, packed_p, _ in layer:
+                sel = [it for c in copies for it, (nm, _, _, _, _) in
+                       zip([(packed, gamma, xs[k], n, k, *scratch[(n, k)]) for (_, k, n, packed, gamma) in c], c)
+                       if nm == name_p]
+                ms_p = _graph_time_ms(torch, layer_fn(sel, m), 10)
+                gbps = packed_p.numel() * n_layers / (ms_p * 1e-3) / 1e9
+                per[name_p] = {"us_per_layer": round(1000.0 * ms_p / n_layers, 2), "weight_GBps": round(gbps, 1),
+                               "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+            entry["per_projection"] = per
         r70[f"M={m}"] = entry
         del items, scratch
     out["layer_70b"] = r70
