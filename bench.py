@@ -201,10 +201,21 @@ def main() -> int:
     avg_bytes = sum(layer_bytes) / len(layer_bytes)
     gemv_gbps = avg_bytes / (avg_us * 1e-6) / 1e9
 
+    # each projection's launches alone (30 of one shape back to back in a graph)
+    per_projection = {}
+    for name, k, n in proj:
+        sel = {i for i, l in enumerate(linears) if l["name"] == name}
+        us = 1000.0 * time_graph(capture(sel), max(args.steps, 20)) / len(sel)
+        wb = bl.bl_packed_bytes(n, k)
+        per_projection[name] = {"KxN": f"{k}x{n}", "us_per_launch": round(us, 3),
+                                "weight_GBps": round(wb / (us * 1e-6) / 1e9, 1)}
+
     extras = None
     if not args.no_extras:
         extras = measure_extras(args, linears, lib)
     stream = stream_reference(torch)
+    floor_us = graph_node_floor_us(torch, len(linears))
+    ceiling_us = floor_us + avg_bytes / (stream["read_GBps"] * 1e3)
 
     # ------------------------------------------------------------ CPU oracle baseline
     cpu = None
@@ -259,7 +270,12 @@ def main() -> int:
                      "avg_launch_us": round(avg_us, 3),
                      "algorithmic_bytes_per_launch": round(avg_bytes, 1),
                      "measured_hbm_reference": stream,
-                     "frac_of_measured_read": round(gemv_gbps / stream["read_GBps"], 4)},
+                     "frac_of_measured_read": round(gemv_gbps / stream["read_GBps"], 4),
+                     "graph_node_floor_us": floor_us,
+                     # per-launch lower bound: the node floor plus the weight bytes at the measured read rate
+                     "launch_bound_ceiling_us": round(ceiling_us, 3),
+                     "frac_of_launch_bound_ceiling": round(ceiling_us / avg_us, 4),
+                     "per_projection": per_projection},
         "packer": packer,
         "cpu_baseline": cpu,
         "extras": extras,
@@ -892,6 +908,15 @@ def cpu_baseline(args, outliers):
                       f"{all_threads} threads; tokens/s = layers/s / {args.layers}",
             "value_1_thread": round(done1 / elapsed1 / args.layers, 4),
             "cpu_model": _cpu_model(), "nproc": os.cpu_count(), "affinity_cpus": affinity}
+
+
+def graph_node_floor_us(torch, nodes):
+    """Time per node of a captured graph of `nodes` one-element kernels (torch's
+    in-place add on a single int32), replayed back to back: the launch cost that
+    each kernel node of the decode step pays before it moves any data."""
+    t = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ms = _graph_time_ms(torch, _repeat(lambda: t.add_(1), nodes), 20)
+    return round(1000.0 * ms / nodes, 3)
 
 
 def stream_reference(torch):
