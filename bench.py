@@ -514,6 +514,37 @@ def _profile_prefill_2b(args):
     return 0
 
 
+def _profile_batched_2b(args, m):
+    """The first 16 layers of the 2B-shaped stack (64 linears, 278 MB packed:
+    more than the 256 MB Infinity Cache, so each pass streams from HBM) at M
+    tokens: bl_bitlinear on every linear in order, --reps passes."""
+    import numpy as np
+    import torch
+    import datagen
+    import ternary_weight_absmean_amd as bl
+
+    dev = torch.device("cuda", 0)
+    wl = datagen.WORKLOAD_STACK_2B
+    linears = []
+    for layer in range(16):
+        for pi, (name, k, n) in enumerate(datagen.STACK_2B_PROJ):
+            w = torch.from_numpy(datagen.weights(datagen.stream_id(wl, layer, pi, datagen.TENSOR_W), n, k)).to(dev)
+            packed, gamma = bl.bl_ternarize_pack(w)
+            del w
+            cols = datagen.outlier_columns(wl, k, datagen.STACK_2B_OUTLIERS)
+            x = datagen.activations_bf16(datagen.stream_id(wl, layer, pi, datagen.TENSOR_X) + m, m, k, cols,
+                                         datagen.STACK_2B_OUTLIER_MULT)
+            linears.append((packed, gamma, torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16), n))
+    torch.cuda.synchronize()
+    print(f"[profile] batched_2b M={m}: {len(linears)} linears packed", flush=True)
+    for r in range(args.reps):
+        for packed, gamma, xd, n in linears:
+            bl.bl_bitlinear(packed, gamma, xd, n, acc=False)
+        torch.cuda.synchronize()
+        print(f"[profile] batched_2b M={m} pass {r + 1}/{args.reps}", flush=True)
+    return 0
+
+
 def _profile_70b(args, ms):
     import numpy as np
     import torch
@@ -581,6 +612,9 @@ PROFILE_CASES = {
     "training_2b": _profile_training_2b,
     "decode_70b": lambda args: _profile_70b(args, (1, 16)),
     "prefill_70b": lambda args: _profile_70b(args, (1024,)),
+    "batched_2b_m4": lambda args: _profile_batched_2b(args, 4),
+    "batched_2b_m16": lambda args: _profile_batched_2b(args, 16),
+    "batched_2b_m64": lambda args: _profile_batched_2b(args, 64),
 }
 
 
