@@ -28,9 +28,11 @@
  *   - Tensors are dense and row-major.  W is [n][k] (n output features,
  *     k input features), activations are [m][k] (m tokens), outputs [m][n].
  *   - k must be a positive multiple of 64 and at most BL_MAX_K (2^22);
- *     m <= BL_MAX_M (2^24) and n <= BL_MAX_N (2^30); m and n may be 0
+ *     m <= BL_MAX_M (2^23) and n <= BL_MAX_N (2^26); m and n may be 0
  *     (nothing is enqueued) except where stated; n * k, m * k and m * n must
- *     stay below 2^40.
+ *     stay below 2^40.  A shape inside these limits whose launch grid would
+ *     still exceed the device's 2^32 work-items (a very large m * n product)
+ *     returns BL_ERR_SHAPE as well, before anything is enqueued.
  *   - Pointers that are read or written with 128-bit accesses (w, packed, x,
  *     xq, workspace) must be 16-byte aligned; alpha, gamma and acc 4-byte,
  *     y 2-byte aligned.
@@ -54,8 +56,8 @@ extern "C" {
 #endif
 
 #define BL_MAX_K (1 << 22)
-#define BL_MAX_M (1 << 24)
-#define BL_MAX_N (1 << 30)
+#define BL_MAX_M (1 << 23)
+#define BL_MAX_N (1 << 26)
 #define BL_MAX_BACKWARD_N (1 << 24)
 
 typedef enum {
@@ -91,9 +93,9 @@ size_t bl_ternarize_pack_workspace_bytes(int64_t n, int64_t k);
  *   gamma     out, one fp32 on the device (gamma, without eps).
  *   workspace device scratch of workspace_bytes >= the size above; its
  *             contents on entry do not matter and are clobbered.
- * Errors: BL_ERR_NULL, BL_ERR_SHAPE (n < 1, bad k, or n*k > 2^39, beyond
- *         which the exact integer sum could overflow), BL_ERR_ALIGN,
- *         BL_ERR_WORKSPACE, BL_ERR_HIP. */
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE (n < 1, bad k, or n*k > 2^35: 34 G
+ *         weights, 137 GB of fp32 input), BL_ERR_ALIGN, BL_ERR_WORKSPACE,
+ *         BL_ERR_HIP. */
 bl_status bl_ternarize_pack(const float* w, int64_t n, int64_t k, uint8_t* packed, float* gamma,
                             void* workspace, size_t workspace_bytes, void* stream);
 
@@ -115,18 +117,20 @@ bl_status bl_quant_act(const uint16_t* x, int64_t m, int64_t k, int8_t* xq, floa
  *   xq/alpha as written by bl_quant_act for [m][k] activations.
  *   acc    out [m][n] int32, or NULL to skip it.
  *   y      out [m][n] bf16 bit patterns, or NULL to skip it (not both NULL).
- * Kernel choice depends on m only (GEMV for m <= 16, tiled GEMM above);
- * results do not depend on it.
+ * The kernel is chosen from m, n and k: decode kernels that stream the
+ * weights once per block of 16 (or 64) tokens for up to 64 tokens, the tiled
+ * int8 matrix-core GEMM beyond; results do not depend on the choice.
  * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_HIP. */
 bl_status bl_linear(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha,
                     int64_t m, int64_t n, int64_t k, int32_t* acc, uint16_t* y, void* stream);
 
 /* The whole layer in one call [P1, P2, P3]: per-token absmax int8
  * quantization of x followed by the ternary product and rescale, with exactly
- * the results of bl_quant_act followed by bl_linear.  For m <= 16 tokens whose
- * int8 rows fit on chip (m * (k + 16) <= 33024 bytes) a single kernel does
- * both steps (each workgroup quantizes the token block it multiplies);
- * otherwise the two kernels run back to back on `stream`.
+ * the results of bl_quant_act followed by bl_linear.  For one token, and for
+ * up to 8 tokens with short rows (m * k below 32768), a single kernel does
+ * both steps (each workgroup quantizes the tokens it multiplies); otherwise
+ * the two kernels run back to back on `stream`.  Results do not depend on
+ * the choice.
  *   x      [m][k] bf16 (raw 16-bit patterns), read only.
  *   xq     out [m][k] int8 (the quantized activations; also used as staging).
  *   alpha  out [m] fp32 (per-token absmax).
@@ -154,7 +158,7 @@ bl_status bl_bitlinear(const uint8_t* packed, const float* gamma, const uint16_t
  * bl_packed_bytes(2f, k) bytes; bl_unpack_ternary(packed, 2f, k) returns the
  * rows in that packed order.
  * Errors: BL_ERR_NULL, BL_ERR_SHAPE (f not a positive multiple of 16, bad k,
- *         2f*k > 2^39), BL_ERR_ALIGN, BL_ERR_WORKSPACE, BL_ERR_HIP. */
+ *         2f*k > 2^35), BL_ERR_ALIGN, BL_ERR_WORKSPACE, BL_ERR_HIP. */
 bl_status bl_ternarize_pack_glu(const float* w, int64_t f, int64_t k, uint8_t* packed, float* gamma,
                                 void* workspace, size_t workspace_bytes, void* stream);
 

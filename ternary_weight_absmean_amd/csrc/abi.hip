@@ -13,7 +13,14 @@ bool valid_k(int64_t k) { return k >= 64 && k <= BL_MAX_K && k % 64 == 0; }
 
 bool product_ok(int64_t a, int64_t b) { return a == 0 || b < kLimit40 / a; }
 
-bl_status from_hip(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_HIP; }
+// A launch grid beyond the device's work-item limit is a shape error (the
+// launchers detect it before any HIP call); any other failure is the runtime's.
+bl_status from_hip(hipError_t e) {
+  return e == hipSuccess ? BL_OK : e == bl::kErrGridTooLarge ? BL_ERR_SHAPE : BL_ERR_HIP;
+}
+
+// Largest weight count the packer takes: its grid covers n * k / 16 work-items.
+constexpr int64_t kMaxPackWeights = (int64_t)1 << 35;
 
 }  // namespace
 
@@ -32,7 +39,7 @@ size_t bl_ternarize_pack_workspace_bytes(int64_t n, int64_t k) {
 bl_status bl_ternarize_pack(const float* w, int64_t n, int64_t k, uint8_t* packed, float* gamma, void* workspace,
                             size_t workspace_bytes, void* stream) {
   if (!w || !packed || !gamma || !workspace) return BL_ERR_NULL;
-  if (n < 1 || n > BL_MAX_N || !valid_k(k) || !product_ok(n + 16, k) || n * k > (1LL << 39)) return BL_ERR_SHAPE;
+  if (n < 1 || n > BL_MAX_N || !valid_k(k) || !product_ok(n + 16, k) || n * k > kMaxPackWeights) return BL_ERR_SHAPE;
   if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(gamma, 4) || !aligned(workspace, 16)) return BL_ERR_ALIGN;
   if (workspace_bytes < bl_ternarize_pack_workspace_bytes(n, k)) return BL_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
@@ -76,6 +83,7 @@ bl_status bl_bitlinear(const uint8_t* packed, const float* gamma, const uint16_t
   if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(alpha, 4) || (n > 0 && (!aligned(packed, 16) ||
       !aligned(gamma, 4) || (acc && !aligned(acc, 4)) || (y && !aligned(y, 2)))))
     return BL_ERR_ALIGN;
+  if (n > 0 && !bl::gemv_serves(m, n) && !bl::gemm_fits(m, n)) return BL_ERR_SHAPE;  // before the quantizer runs
   hipStream_t s = (hipStream_t)stream;
   if (n > 0 && m <= 16 && bl::gemv_fused_applies(m, n, k))
     return from_hip(bl::launch_gemv_fused(packed, gamma, x, m, n, k, xq, alpha, acc, y, s));
@@ -89,7 +97,7 @@ bl_status bl_ternarize_pack_glu(const float* w, int64_t f, int64_t k, uint8_t* p
                                 size_t workspace_bytes, void* stream) {
   if (!w || !packed || !gamma || !workspace) return BL_ERR_NULL;
   if (f < 16 || f % 16 != 0 || 2 * f > BL_MAX_N || !valid_k(k) || !product_ok(2 * f + 16, k) ||
-      2 * f * k > (1LL << 39))
+      2 * f * k > kMaxPackWeights)
     return BL_ERR_SHAPE;
   if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(gamma, 4) || !aligned(workspace, 16)) return BL_ERR_ALIGN;
   if (workspace_bytes < bl_ternarize_pack_workspace_bytes(2 * f, k)) return BL_ERR_WORKSPACE;
@@ -132,6 +140,7 @@ bl_status bl_bitlinear_glu(const uint8_t* packed, const float* gamma, const uint
   if (!aligned(packed, 16) || !aligned(x, 16) || !aligned(xq, 16) || !aligned(gamma, 4) || !aligned(alpha, 4) ||
       !aligned(h, 2))
     return BL_ERR_ALIGN;
+  if (!bl::gemv_serves(m, 2 * f) && !bl::gemm_fits(m, 2 * f)) return BL_ERR_SHAPE;  // before the quantizer runs
   hipStream_t s = (hipStream_t)stream;
   if (bl::gemv_fused_glu_applies(m, f, k))
     return from_hip(bl::launch_gemv_fused_glu(packed, gamma, x, m, f, k, xq, alpha, h, s));

@@ -391,7 +391,7 @@ hipError_t launch_backward_x(const uint8_t* packed_t, const float* gamma, const 
                              int64_t k, float* dx, hipStream_t s) {
   // 128 rows of q^T x 64 tokens per workgroup (measured faster than 256 x 64)
   const int64_t blocks_n = (k + 127) / 128, blocks = blocks_n * ((m + 63) / 64);
-  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (!grid_fits(blocks, 256)) return kErrGridTooLarge;
   hipLaunchKernelGGL((k_bwd_x<4, 2>), dim3((unsigned)blocks), dim3(256), 0, s, packed_t, gamma, dy, m, n, k,
                      blocks_n, dx);
   return hipGetLastError();
@@ -409,7 +409,7 @@ __global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ p, int64_
 hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t s) {
   if (count == 0) return hipSuccess;
   const int64_t blocks = (count + 255) / 256;
-  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (!grid_fits(blocks, 256)) return kErrGridTooLarge;
   hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(256), 0, s, p, count);
   return hipGetLastError();
 }
@@ -427,7 +427,7 @@ hipError_t launch_backward_w(const uint16_t* dy, const int8_t* xq, const float* 
   uint16_t* x_t = a_lo + n * m_pad;
   const int64_t prep_blocks = (n / kPrepTile + k / kPrepTile) * (m_pad / kPrepTile);
   const int64_t blocks_t = (k + 127) / 128, blocks = ((n + 127) / 128) * blocks_t;
-  if (prep_blocks > 0x7FFFFFFF || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (!grid_fits(prep_blocks, 256) || !grid_fits(blocks, 256)) return kErrGridTooLarge;
   hipLaunchKernelGGL(k_bwd_w_prep, dim3((unsigned)prep_blocks), dim3(256), 0, s, dy, xq, alpha, m, n, k, m_pad, a_hi,
                      a_lo, x_t);
   hipLaunchKernelGGL(k_bwd_w, dim3((unsigned)blocks), dim3(256), 0, s, a_hi, a_lo, x_t, m_pad, n, k, blocks_t, dw);

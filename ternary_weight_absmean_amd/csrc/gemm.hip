@@ -1,4 +1,5 @@
-// Prefill product for BitLinear W1.58A8 (m > 16 tokens): packed ternary W x int8 x.
+// Prefill product for BitLinear W1.58A8 (more tokens than the decode kernels
+// take): packed ternary W x int8 x.
 //
 // deepmox.com chapter 8, "A low-bit model is a whole-stack design": the packed
 // weights move on chip, are unpacked there and multiplied with the 8-bit
@@ -298,28 +299,44 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint8_t* __restrict__ pac
 
 namespace {
 
+// Tile of the GEMM for an m x n product: the largest that still gives the
+// chip enough workgroups -- 256 rows x 128 tokens with >= 4 per CU, else
+// 256 x 64 with >= 2 per CU, else 128 x 64.
+struct GemmTile {
+  int64_t rows, toks;
+};
+GemmTile gemm_tile(int64_t m, int64_t n) {
+  auto count = [&](int64_t rows, int64_t toks) { return ((n + rows - 1) / rows) * ((m + toks - 1) / toks); };
+  if (count(256, 128) >= 1024) return {256, 128};
+  if (count(256, 64) >= 512) return {256, 64};
+  return {128, 64};
+}
+
+int64_t gemm_blocks(int64_t m, int64_t n) {
+  const GemmTile t = gemm_tile(m, n);
+  return ((n + t.rows - 1) / t.rows) * ((m + t.toks - 1) / t.toks);
+}
+
 template <bool kGlu>
 hipError_t launch_gemm_impl(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
                             int64_t n, int64_t k, int32_t* acc, uint16_t* y, hipStream_t s) {
-  // Largest tile that still gives the chip enough workgroups: 256 rows x 128
-  // tokens with >= 4 per CU, else 256 x 64 with >= 2 per CU, else 128 x 64.
   // Fixed buffers (unrolled steps, more registers) where they measured
   // faster: always for 128 x 64 tiles (same occupancy either way), for
   // 256 x 64 tiles only with long rows (the extra registers cost a
   // workgroup per CU, which the short-row shapes need more); the 256 x 128
   // tile does not fit its registers unrolled.
-  auto count = [&](int64_t rows, int64_t toks) { return ((n + rows - 1) / rows) * ((m + toks - 1) / toks); };
   const uint8_t* p = packed;
   auto launch = [&](auto kern, int64_t rows, int64_t toks) {
-    const int64_t blocks_n = (n + rows - 1) / rows, blocks = count(rows, toks);
-    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const int64_t blocks_n = (n + rows - 1) / rows, blocks = ((m + toks - 1) / toks) * blocks_n;
+    if (!grid_fits(blocks, 256)) return kErrGridTooLarge;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, blocks_n, acc, y);
     return hipSuccess;
   };
   hipError_t e;
-  if (count(256, 128) >= 1024)
+  const GemmTile t = gemm_tile(m, n);
+  if (t.toks == 128)
     e = launch(k_gemm<8, 4, false, kGlu>, 256, 128);
-  else if (count(256, 64) >= 512)
+  else if (t.rows == 256)
     e = k >= 8192 ? launch(k_gemm<4, 4, true, kGlu>, 256, 64) : launch(k_gemm<4, 4, false, kGlu>, 256, 64);
   else
     e = launch(k_gemm<4, 2, true, kGlu>, 128, 64);
@@ -328,6 +345,8 @@ hipError_t launch_gemm_impl(const uint8_t* packed, const float* gamma, const int
 }
 
 }  // namespace
+
+bool gemm_fits(int64_t m, int64_t n) { return grid_fits(gemm_blocks(m, n), 256); }
 
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
                        int64_t n, int64_t k, int32_t* acc, uint16_t* y, hipStream_t s) {

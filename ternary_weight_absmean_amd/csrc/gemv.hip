@@ -1,4 +1,4 @@
-// Decode products for BitLinear W1.58A8 (m <= 16 tokens): packed ternary W x int8 x.
+// Decode products for BitLinear W1.58A8 (up to 64 tokens): packed ternary W x int8 x.
 //
 // deepmox.com chapter 8, "A low-bit model is a whole-stack design": decode
 // time goes to moving the weights; the GPU path keeps them packed at four
@@ -1034,8 +1034,9 @@ constexpr int64_t kRingMinK = 8192;  // rows from which 2..16 tokens take k_gemv
 template <bool kGlu>
 hipError_t launch_gemv_impl(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
                             int64_t n, int64_t k, int32_t* acc, uint16_t* y, hipStream_t s) {
-  if ((m + 15) / 16 > 65535) return hipErrorInvalidValue;
   const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
+  // at most one workgroup of up to 1024 threads per row tile, at most 4 token blocks
+  if (!grid_fits(row_tiles, 1024) || (m + 15) / 16 > 65535) return kErrGridTooLarge;
   const uint4* p = reinterpret_cast<const uint4*>(packed);
   if (m > 32 && row_tiles >= 512) {
     // up to 64 tokens per workgroup: the unpacked weights serve 4 token blocks

@@ -12,6 +12,15 @@ constexpr int kTileRows = 16;
 constexpr int kTileCols = 64;
 constexpr int kTileBytes = 256;
 
+// A launch of `blocks` workgroups of `threads` work-items fits the device:
+// the grid's total work-item count must stay below 2^32.  Launchers return
+// kErrGridTooLarge (before any HIP call) for a shape that would not fit; the
+// C ABI reports it as BL_ERR_SHAPE.
+constexpr hipError_t kErrGridTooLarge = hipErrorInvalidConfiguration;
+inline bool grid_fits(int64_t blocks, int64_t threads) {
+  return blocks >= 1 && blocks <= ((int64_t)1 << 32) / threads - 1;
+}
+
 // Weight packer (absmean exponent bins -> exact gamma -> ternarize + pack).
 // The workspace holds the 256 exponent bins (u64) of the whole matrix; the
 // absmean workgroups add into them with integer atomics (cleared first).
@@ -51,6 +60,8 @@ hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const ui
                              int64_t k, int8_t* xq, float* alpha, int32_t* acc, uint16_t* y, hipStream_t s);
 hipError_t launch_gemm(const uint8_t* packed, const float* gamma, const int8_t* xq, const float* alpha, int64_t m,
                        int64_t n, int64_t k, int32_t* acc, uint16_t* y, hipStream_t s);
+// The GEMM's grid fits the device for an m x n product.
+bool gemm_fits(int64_t m, int64_t n);
 
 // Squared-ReLU gated products from gate+up weights packed with alternating
 // gate/up row tiles (n = 2f rows): h[i][j] = bf16(relu(g)^2 * u), g and u the

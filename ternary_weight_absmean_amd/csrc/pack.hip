@@ -359,7 +359,7 @@ hipError_t launch_ternarize_pack(const float* w, int64_t n, int64_t k, const flo
   const int64_t n_pad = (n + kTileRows - 1) / kTileRows * kTileRows;
   const int64_t threads = n_pad * (k / 4);
   const int64_t blocks = (threads + kPackThreads * kPackIter - 1) / (kPackThreads * kPackIter);
-  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (!grid_fits(blocks, kPackThreads)) return kErrGridTooLarge;
   hipLaunchKernelGGL(k_ternarize_pack, dim3((unsigned)blocks), dim3(kPackThreads), 0, s,
                      reinterpret_cast<const float4*>(w), n, k, gamma, reinterpret_cast<uint32_t*>(packed), glu_f);
   return hipGetLastError();
@@ -367,7 +367,7 @@ hipError_t launch_ternarize_pack(const float* w, int64_t n, int64_t k, const flo
 
 hipError_t launch_pack_transposed(const uint8_t* packed, int64_t n, int64_t k, uint8_t* packed_t, hipStream_t s) {
   const int64_t blocks = (n / 64) * (k / 64);
-  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (!grid_fits(blocks, 256)) return kErrGridTooLarge;
   hipLaunchKernelGGL(k_pack_transposed, dim3((unsigned)blocks), dim3(256), 0, s,
                      reinterpret_cast<const uint32_t*>(packed), n, k, reinterpret_cast<uint32_t*>(packed_t));
   return hipGetLastError();
@@ -376,6 +376,7 @@ hipError_t launch_pack_transposed(const uint8_t* packed, int64_t n, int64_t k, u
 hipError_t launch_unpack(const uint8_t* packed, int64_t n, int64_t k, int8_t* q, hipStream_t s) {
   const int64_t threads = n * (k / kTileCols);
   const int64_t blocks = (threads + kPackThreads - 1) / kPackThreads;
+  if (!grid_fits(blocks, kPackThreads)) return kErrGridTooLarge;
   hipLaunchKernelGGL(k_unpack, dim3((unsigned)blocks), dim3(kPackThreads), 0, s,
                      reinterpret_cast<const uint4*>(packed), n, k, q);
   return hipGetLastError();

@@ -72,6 +72,7 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t m, int64_t k, int8_t* xq,
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   uint2* q = reinterpret_cast<uint2*>(xq);
   const int64_t chunks = (k / 8 + kQuantThreads - 1) / kQuantThreads;  // per thread
+  if (!grid_fits(m, kQuantThreads)) return kErrGridTooLarge;
   if (chunks <= 2)
     hipLaunchKernelGGL(k_quant_act<2>, dim3((unsigned)m), dim3(kQuantThreads), 0, s, xv, k, q, alpha);
   else if (chunks <= 4)

@@ -52,8 +52,8 @@ def test_ternarize_pack_validation():
     assert f(FAKE, 16, 96, FAKE, FAKE, FAKE, WS, None) == BL_ERR_SHAPE
     assert f(FAKE, 16, 0, FAKE, FAKE, FAKE, WS, None) == BL_ERR_SHAPE
     assert f(FAKE, 1 << 31, 64, FAKE, FAKE, FAKE, WS, None) == BL_ERR_SHAPE
-    # more than 2^39 weights: the exact integer sum of |w| could overflow
-    assert f(FAKE, (1 << 17) + 16, 1 << 22, FAKE, FAKE, FAKE, WS, None) == BL_ERR_SHAPE
+    # more than 2^35 weights (the packer's grid would pass 2^32 work-items)
+    assert f(FAKE, (1 << 13) + 16, 1 << 22, FAKE, FAKE, FAKE, WS, None) == BL_ERR_SHAPE
     assert f(FAKE + 4, 16, 64, FAKE, FAKE, FAKE, WS, None) == BL_ERR_ALIGN
     assert f(FAKE, 16, 64, FAKE + 8, FAKE, FAKE, WS, None) == BL_ERR_ALIGN
     assert f(FAKE, 16, 64, FAKE, FAKE, FAKE, WS - 1, None) == BL_ERR_WORKSPACE
@@ -65,7 +65,7 @@ def test_quant_act_validation():
     assert f(None, 0, 64, None, None, None) == BL_OK  # empty: pointers may be NULL
     assert f(FAKE, -1, 64, FAKE, FAKE, None) == BL_ERR_SHAPE
     assert f(FAKE, 1, 100, FAKE, FAKE, None) == BL_ERR_SHAPE
-    assert f(FAKE, (1 << 24) + 1, 64, FAKE, FAKE, None) == BL_ERR_SHAPE
+    assert f(FAKE, (1 << 23) + 1, 64, FAKE, FAKE, None) == BL_ERR_SHAPE  # past BL_MAX_M
     assert f(FAKE + 2, 1, 64, FAKE, FAKE, None) == BL_ERR_ALIGN
     assert f(FAKE, 1, 64, FAKE, FAKE + 2, None) == BL_ERR_ALIGN
     assert f(FAKE, 0, 64, FAKE, FAKE, None) == BL_OK  # empty: nothing enqueued
@@ -92,6 +92,20 @@ def test_linear_validation():
     assert call(m=0) == BL_OK
     assert call(n=0) == BL_OK
     assert call(m=0, packed=None, xq=None) == BL_OK
+
+
+def test_grid_limits_are_shape_errors():
+    """Shapes inside the argument limits whose launch grid would pass the
+    device's 2^32 work-items are rejected on the host, before anything runs:
+    2^21 tokens x 2^18 outputs (m * n = 2^39 < 2^40) needs 2^24 GEMM
+    workgroups of 256 work-items."""
+    m, n, k = 1 << 21, 1 << 18, 64
+    assert lib.bl_linear(FAKE, FAKE, FAKE, FAKE, m, n, k, FAKE, FAKE, None) == BL_ERR_SHAPE
+    assert lib.bl_bitlinear(FAKE, FAKE, FAKE, m, n, k, FAKE, FAKE, FAKE, FAKE, None) == BL_ERR_SHAPE
+    assert lib.bl_linear_glu(FAKE, FAKE, FAKE, FAKE, m, n // 2, k, FAKE, None) == BL_ERR_SHAPE
+    assert lib.bl_bitlinear_glu(FAKE, FAKE, FAKE, m, n // 2, k, FAKE, FAKE, FAKE, None) == BL_ERR_SHAPE
+    # past the row limit (2^26)
+    assert lib.bl_linear(FAKE, FAKE, FAKE, FAKE, 1, (1 << 26) + 1, k, FAKE, FAKE, None) == BL_ERR_SHAPE
 
 
 def test_unpack_validation():
@@ -138,7 +152,7 @@ def test_glu_entry_points_validation():
     assert pack(FAKE, 24, 64, FAKE, FAKE, FAKE, WS, None) == BL_ERR_SHAPE   # f not a multiple of 16
     assert pack(FAKE, 0, 64, FAKE, FAKE, FAKE, WS, None) == BL_ERR_SHAPE
     assert pack(FAKE, 16, 96, FAKE, FAKE, FAKE, WS, None) == BL_ERR_SHAPE
-    assert pack(FAKE, 1 << 17, 1 << 22, FAKE, FAKE, FAKE, WS, None) == BL_ERR_SHAPE  # 2f*k > 2^39
+    assert pack(FAKE, 1 << 13, 1 << 22, FAKE, FAKE, FAKE, WS, None) == BL_ERR_SHAPE  # 2f*k > 2^35
     assert pack(FAKE + 4, 16, 64, FAKE, FAKE, FAKE, WS, None) == BL_ERR_ALIGN
     assert pack(FAKE, 16, 64, FAKE, FAKE, FAKE, WS - 1, None) == BL_ERR_WORKSPACE
 

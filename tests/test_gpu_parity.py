@@ -4,8 +4,18 @@ Bar: bytes, trits, int8 activations and int32 accumulators bit-exact; gamma
 and alpha bit-exact (fp32 values the method rounds once); bf16 outputs within
 one bf16 ulp of the oracle's (relative <= 7.8e-3), with exact zeros kept.
 Shapes span several 16x64 tiles, ragged row counts and K tails that do not
-fill a 1 KiB group; the workload cases use the BitNet b1.58 2B- and 70B-shaped
-layers at full size (sampled outputs where the oracle would take minutes).
+fill a 1 KiB group.  The workload cases use the BitNet b1.58 2B- and 70B-shaped
+layers at full size:
+  * the single 2560 x 2560 decode and every one of the 120 matrices of the
+    30-layer 2B-shaped stack (each has its own gamma): packed bytes and gamma
+    bit for bit, then the decode call at one token with the benchmark's seeded
+    input, every output;
+  * batched decode (4, 16, 64 tokens) on the 2B layer-0 shapes, every output;
+  * the 2B prefill (2048 tokens) of gate+up and down, every output, through
+    both bl_linear and the benchmark's bl_bitlinear;
+  * the 70B-shaped layer at 1 and 16 tokens, every output; at 1024 tokens,
+    every output row of 64 sampled tokens (the oracle would take minutes for
+    all 1024).
 """
 import numpy as np
 import pytest
@@ -291,7 +301,8 @@ def test_linear_empty_is_a_noop():
 
 def workload_case(workload, proj, k, n, m, outliers, mult, layer=0, sample=None):
     """Pack seeded weights on the GPU (gamma and bytes checked against the
-    oracle), quantize seeded activations on the GPU, and compare the product."""
+    oracle), quantize seeded activations on the GPU, and compare the product.
+    sample: (tokens, rows) to compare, either None for all of them."""
     w = datagen.weights(datagen.stream_id(workload, layer, proj, datagen.TENSOR_W), n, k)
     packed_dev = check_pack(w)
     gamma = oracle.absmean(w)
@@ -302,8 +313,10 @@ def workload_case(workload, proj, k, n, m, outliers, mult, layer=0, sample=None)
     rows = toks = None
     if sample is not None:
         rng = np.random.default_rng(m + n)
-        toks = np.sort(rng.choice(m, size=min(m, sample[0]), replace=False))
-        rows = np.sort(rng.choice(n, size=min(n, sample[1]), replace=False))
+        if sample[0] is not None:
+            toks = np.sort(rng.choice(m, size=min(m, sample[0]), replace=False))
+        if sample[1] is not None:
+            rows = np.sort(rng.choice(n, size=min(n, sample[1]), replace=False))
     gamma_dev = f32(np.array([gamma]))
     check_linear(packed_dev, gamma_dev, qw, gamma, x_bits=x, rows=rows, toks=toks)
 
@@ -327,16 +340,20 @@ def test_linear_workload_2b_stack_last_layer_decode():
 
 @pytest.mark.parametrize("proj", [2, 3])
 def test_linear_workload_2b_prefill_2048(proj):
+    """The 2B prefill shapes (gate+up 2560 -> 13824, down 6912 -> 2560) at
+    2048 tokens: every output of the GEMM."""
     name, k, n = datagen.STACK_2B_PROJ[proj]
     workload_case(datagen.WORKLOAD_STACK_2B, proj, k, n, 2048, datagen.STACK_2B_OUTLIERS,
-                  datagen.STACK_2B_OUTLIER_MULT, sample=(96, 512))
+                  datagen.STACK_2B_OUTLIER_MULT)
 
 
 @pytest.mark.parametrize("proj", [0, 1])
 @pytest.mark.parametrize("m", [1, 16, 1024])
 def test_linear_workload_70b(proj, m):
+    """The 70B-shaped layer: every output at 1 and 16 tokens; at 1024 tokens
+    every output row of 64 sampled tokens."""
     name, k, n = datagen.LAYER_70B_PROJ[proj]
-    sample = None if m == 1 else (16, 2048) if m == 16 else (48, 512)
+    sample = (64, None) if m == 1024 else None
     workload_case(datagen.WORKLOAD_70B, proj, k, n, m, datagen.n_outliers_70b(k), datagen.LAYER_70B_OUTLIER_MULT,
                   sample=sample)
 
@@ -361,8 +378,15 @@ def test_linear_is_deterministic():
                                    (1, 8200, 320), (1, 16400, 2560), (1, 16400, 6912), (1, 17000, 7168),
                                    # single-token kernel: partial last column group, both slot counts
                                    (1, 40, 192), (1, 1000, 2624), (1, 9000, 4160), (1, 8200, 28672),
-                                   # block-quantizing kernel with 2 and 4 row tiles per workgroup
-                                   (1, 16400, 8192), (3, 8200, 2560), (16, 16400, 1024), (2, 17, 320),
+                                   # single-token kernel, two row tiles per workgroup (1025 row tiles);
+                                   # its 4-token form with two row tiles (513) and with one; 16 tokens
+                                   # on 1025 row tiles: quantizer + LDS-staged product, two tiles per workgroup
+                                   (1, 16400, 8192), (3, 8200, 2560), (2, 17, 320), (16, 16400, 1024),
+                                   # block-quantizing kernel with two row tiles and four waves (2 tokens on
+                                   # 513 row tiles, k <= 4096); its activation path that re-reads the rows
+                                   # instead of holding them in registers: 1 token on rows too long for
+                                   # the single-token kernel, 3 tokens of 10240 and 5 of 5120 columns
+                                   (2, 8200, 2560), (1, 40, 32832), (3, 48, 10240), (5, 48, 5120),
                                    # several tokens: quantizer + product with shared activation loads
                                    (8, 16400, 2560), (16, 32800, 320), (5, 2000, 6912),
                                    # block-quantizing kernel with eight waves, one and two row tiles
@@ -401,21 +425,45 @@ def test_bitlinear_matches_oracle(m, n, k):
     assert torch.equal(y2.view(torch.int16), y.view(torch.int16))
 
 
-def test_bitlinear_2b_stack_layer_decode():
-    """The benchmark's own step on one layer: seeded inputs, M = 1."""
+@pytest.mark.parametrize("layer", range(datagen.STACK_2B_LAYERS))
+def test_bitlinear_2b_stack_every_matrix(layer):
+    """The benchmark's own step, on every matrix of the 30-layer 2B-shaped
+    stack (each has its own gamma): the packer's gamma and bytes bit for bit,
+    then bl_bitlinear at one token on the benchmark's seeded input (int8
+    activations, alpha and int32 exact; bf16 within one ulp), every output."""
     wl = datagen.WORKLOAD_STACK_2B
     for pi, (name, k, n) in enumerate(datagen.STACK_2B_PROJ):
-        w = datagen.weights(datagen.stream_id(wl, 3, pi, datagen.TENSOR_W), n, k)
+        w = datagen.weights(datagen.stream_id(wl, layer, pi, datagen.TENSOR_W), n, k)
         cols = datagen.outlier_columns(wl, k, datagen.STACK_2B_OUTLIERS)
-        x = datagen.activations_bf16(datagen.stream_id(wl, 3, pi, datagen.TENSOR_X), 1, k, cols,
+        x = datagen.activations_bf16(datagen.stream_id(wl, layer, pi, datagen.TENSOR_X), 1, k, cols,
                                      datagen.STACK_2B_OUTLIER_MULT)
-        say(f"bl_bitlinear 2B layer 3 {name}")
-        packed, gamma = bl.bl_ternarize_pack(f32(w))
-        acc, y, _, _ = bl.bl_bitlinear(packed, gamma, bf16(x), n)
+        say(f"bl_ternarize_pack + bl_bitlinear 2B layer {layer} {name}")
+        packed = check_pack(w)
         want_packed, want_gamma = oracle.ternarize_pack(w)
-        want_y, want_acc, _, _ = oracle.bitlinear_forward(want_packed, want_gamma, x, n)
+        del w
+        gamma = f32(np.array([want_gamma]))
+        acc, y, xq, alpha = bl.bl_bitlinear(packed, gamma, bf16(x), n)
+        want_y, want_acc, want_xq, want_alpha = oracle.bitlinear_forward(want_packed, want_gamma, x, n)
+        np.testing.assert_array_equal(host(xq), want_xq)
+        np.testing.assert_array_equal(host(alpha).view(np.uint32), want_alpha.view(np.uint32))
         np.testing.assert_array_equal(host(acc), want_acc)
         assert_bf16_within_one_ulp(host(y), want_y)
+
+
+@pytest.mark.parametrize("proj", [2, 3])
+def test_bitlinear_2b_prefill_full(proj):
+    """The benchmark's prefill call (bl_bitlinear: quantizer + GEMM) on the 2B
+    layer-0 gate+up and down at 2048 tokens, with the benchmark's seeded
+    input: every output."""
+    wl = datagen.WORKLOAD_STACK_2B
+    name, k, n = datagen.STACK_2B_PROJ[proj]
+    m = 2048
+    w = datagen.weights(datagen.stream_id(wl, 0, proj, datagen.TENSOR_W), n, k)
+    cols = datagen.outlier_columns(wl, k, datagen.STACK_2B_OUTLIERS)
+    x = datagen.activations_bf16(datagen.stream_id(wl, 0, proj, datagen.TENSOR_X) + m, m, k, cols,
+                                 datagen.STACK_2B_OUTLIER_MULT)
+    say(f"bl_bitlinear 2B prefill {name} m={m}")
+    check_bitlinear_sampled(w, x)
 
 
 def check_bitlinear_sampled(w, x, rows=None):
@@ -451,13 +499,12 @@ def test_bitlinear_2b_stack_batched_decode(m):
 @pytest.mark.parametrize("proj", [0, 1])
 @pytest.mark.parametrize("m", [1, 16])
 def test_bitlinear_70b_decode(proj, m):
-    """The benchmark's 70B-shaped decode call (full shapes, sampled rows)."""
+    """The benchmark's 70B-shaped decode call (full shapes, every output)."""
     wl = datagen.WORKLOAD_70B
     name, k, n = datagen.LAYER_70B_PROJ[proj]
     w = datagen.weights(datagen.stream_id(wl, 0, proj, datagen.TENSOR_W), n, k)
     cols = datagen.outlier_columns(wl, k, datagen.n_outliers_70b(k))
     x = datagen.activations_bf16(datagen.stream_id(wl, 0, proj, datagen.TENSOR_X) + m, m, k, cols,
                                  datagen.LAYER_70B_OUTLIER_MULT)
-    rows = np.sort(np.random.default_rng(proj + m).choice(n, size=1024, replace=False))
     say(f"bl_bitlinear 70B {name} m={m}")
-    check_bitlinear_sampled(w, x, rows)
+    check_bitlinear_sampled(w, x)
