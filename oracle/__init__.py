@@ -25,6 +25,13 @@ Parity status of each function (what pins it, see ``tests/test_oracle_*.py``):
   equals the addition-only form.
 * ``rescale``      -- pinned: exact rational product rounded to bf16 by an
   independent Python routine.
+* ``b3_encode/b3_decode``, ``pack_b3/unpack_b3`` (five trits per byte) --
+  pinned: all 243 five-trit patterns round-trip to 243 distinct bytes, the 13
+  other bytes are rejected; hand-worked bytes; every code also decodes by the
+  multiply-and-carry route; the documented digit/column property read back
+  from random buffers; the 2-bit packing of the same trits unpacks equal.
+* ``bitlinear_forward_b3`` -- pinned: equals ``bitlinear_forward`` on the
+  2-bit packing of the same trits.
 """
 from __future__ import annotations
 
@@ -99,6 +106,18 @@ def _load():
         lib.orc_backward_w.restype = None
         lib.orc_pack_transposed.argtypes = [p, i64, i64, p]
         lib.orc_pack_transposed.restype = ctypes.c_int
+        lib.orc_packed_bytes_b3.argtypes = [i64, i64]
+        lib.orc_packed_bytes_b3.restype = i64
+        lib.orc_b3_encode.argtypes = [p]
+        lib.orc_b3_encode.restype = ctypes.c_uint8
+        lib.orc_b3_decode.argtypes = [ctypes.c_uint8, p]
+        lib.orc_b3_decode.restype = ctypes.c_int
+        lib.orc_pack_b3.argtypes = [p, i64, i64, p]
+        lib.orc_pack_b3.restype = ctypes.c_int
+        lib.orc_unpack_b3.argtypes = [p, i64, i64, p]
+        lib.orc_unpack_b3.restype = ctypes.c_int
+        lib.orc_bitlinear_forward_b3.argtypes = [p, ctypes.c_float, p, i64, i64, i64, p, p, p, p]
+        lib.orc_bitlinear_forward_b3.restype = ctypes.c_int
         lib.orc_set_threads.argtypes = [ctypes.c_int]
         lib.orc_set_threads.restype = ctypes.c_int
         _lib = lib
@@ -316,6 +335,70 @@ def pack_transposed(packed: np.ndarray, n: int, k: int) -> np.ndarray:
     if rc != 0:
         raise ValueError(f"orc_pack_transposed failed ({rc})")
     return out
+
+
+def packed_bytes_b3(n: int, k: int) -> int:
+    """Size of the five-trits-per-byte buffer: ceil(n/16)*16 rows of ceil(k/320)*64 bytes."""
+    return int(_load().orc_packed_bytes_b3(n, k))
+
+
+def b3_encode(trits) -> int:
+    """The byte of five trits (t_0 most significant base-3 digit)."""
+    t = _c(trits, np.int8)
+    assert t.shape == (5,)
+    return int(_load().orc_b3_encode(_p(t)))
+
+
+def b3_decode(byte: int):
+    """The five trits of a byte, or None if the byte is no code."""
+    t = np.empty(5, np.int8)
+    if _load().orc_b3_decode(int(byte), _p(t)) != 0:
+        return None
+    return t
+
+
+def pack_b3(q: np.ndarray) -> np.ndarray:
+    """Pack a ternary matrix ``[n][k]`` (k % 64 == 0) five trits per byte."""
+    q = _c(q, np.int8)
+    n, k = q.shape
+    out = np.empty(packed_bytes_b3(n, k), np.uint8)
+    rc = _load().orc_pack_b3(_p(q), n, k, _p(out))
+    if rc != 0:
+        raise ValueError(f"orc_pack_b3 failed ({rc})")
+    return out
+
+
+def unpack_b3(packed: np.ndarray, n: int, k: int) -> np.ndarray:
+    packed = _c(packed, np.uint8)
+    if packed.size != packed_bytes_b3(n, k):
+        raise ValueError("packed buffer has the wrong size")
+    q = np.empty((n, k), np.int8)
+    rc = _load().orc_unpack_b3(_p(packed), n, k, _p(q))
+    if rc != 0:
+        raise ValueError(f"orc_unpack_b3 failed ({rc})")
+    return q
+
+
+def ternarize_pack_b3(w: np.ndarray):
+    """Full weight preparation in the five-trits-per-byte code: (packed, gamma)."""
+    g = absmean(w)
+    return pack_b3(ternarize(w, g)), g
+
+
+def bitlinear_forward_b3(packed: np.ndarray, gamma, x_bf16: np.ndarray, n: int):
+    """Whole layer from five-trits-per-byte weights: (y bf16 bits, acc, xq, alpha)."""
+    packed = _c(packed, np.uint8)
+    x = _c(x_bf16, np.uint16)
+    m, k = x.shape
+    xq = np.empty((m, k), np.int8)
+    alpha = np.empty(m, np.float32)
+    acc = np.empty((m, n), np.int32)
+    y = np.empty((m, n), np.uint16)
+    rc = _load().orc_bitlinear_forward_b3(_p(packed), float(np.float32(gamma)), _p(x), m, n, k,
+                                          _p(xq), _p(alpha), _p(acc), _p(y))
+    if rc != 0:
+        raise ValueError("k must be a multiple of 64")
+    return y, acc, xq, alpha
 
 
 def set_threads(n: int = 0) -> int:

@@ -256,6 +256,110 @@ int orc_unpack(const uint8_t* packed, int64_t n, int64_t k, int8_t* q) {
 }
 
 /* ------------------------------------------------------------------------ */
+/* Denser code: five trits per byte (base 3).                                */
+/* ------------------------------------------------------------------------ */
+/*
+ * Sources: bako.co, "BitNet b1.58 and the 1-Bit AI Architecture Revolution",
+ * section "The Information Theory of 1.58 Bits": a weight with three states
+ * carries log2(3), about 1.58, bits.  deepmox.com chapter 1, "Why Smaller
+ * Weights Are Not the Whole Story", section "A different place to make
+ * efficiency decisions": the 2B4T model's non-embedding weights take 0.4 GB,
+ * less than two bits per weight.
+ * Readings (the pages give no format):
+ *  - five trits t_0..t_4 share one byte (3^5 = 243 <= 256): 1.6 bits per
+ *    weight.  With codes c_d = t_d + 1 the byte holds v = sum_d c_d * 3^(4-d)
+ *    (t_0 the most significant base-3 digit) as b = ceil(256 * v / 243), the
+ *    base-3 fraction v / 243 scaled to a byte and rounded up; decoding takes
+ *    v = floor(243 * b / 256) and its base-3 digits.  (Rounding up keeps
+ *    b / 256 inside [v / 243, (v + 1) / 243), so each digit also equals
+ *    floor(3 * ((b * 3^d) mod 256) / 256), which a decoder can use instead.)
+ *    13 byte values are no code.
+ *  - layout: 16-row x 320-column super-tiles of 1024 bytes, column
+ *    super-tile fastest (super-tile (i, s) at byte 1024 * (i * ceil(k/320) + s));
+ *    inside one, the 320 columns form four groups of 80; group g of row r
+ *    owns bytes 256 g + 16 r .. + 15, and its column 80 g + 16 d + j sits in
+ *    byte j (0..15) as digit d (0..4).  So digit d of the 16 bytes of (g, r)
+ *    is 16 consecutive columns.  Columns past k (the last super-tile is
+ *    partial unless 320 divides k) and rows past n hold trit 0.
+ */
+
+int64_t orc_packed_bytes_b3(int64_t n, int64_t k) {
+    return ((n + 15) / 16) * 16 * ((k + 319) / 320) * 64;
+}
+
+static const int pow3[5] = {81, 27, 9, 3, 1};   /* 3^(4 - d) */
+
+/* byte of the five trits t[0..4] (each in {-1, 0, 1}) */
+uint8_t orc_b3_encode(const int8_t* t) {
+    int v = 0;
+    for (int d = 0; d < 5; ++d) v += (t[d] + 1) * pow3[d];
+    return (uint8_t)((256 * v + 242) / 243);    /* ceil(256 v / 243) */
+}
+
+/* the five trits of byte b; returns 0, or -1 if b is not the code of any
+ * five trits */
+int orc_b3_decode(uint8_t b, int8_t* t) {
+    int v = (243 * (int)b) / 256;               /* floor(243 b / 256) */
+    for (int d = 0; d < 5; ++d) t[d] = (int8_t)((v / pow3[d]) % 3 - 1);
+    return orc_b3_encode(t) == b ? 0 : -1;
+}
+
+static void b3_position(int64_t row, int64_t col, int64_t k, int64_t* byte, int* digit) {
+    int64_t supers = (k + 319) / 320;
+    int64_t s = col / 320, t = col % 320;
+    int64_t g = t / 80, u = t % 80;
+    *digit = (int)(u / 16);
+    *byte = ((row / 16) * supers + s) * 1024 + g * 256 + (row % 16) * 16 + u % 16;
+}
+
+/* q [n][k] with values in {-1, 0, 1}, k a multiple of 64.  Returns 0, -1 on a
+ * bad shape, -2 if a value is not a trit. */
+int orc_pack_b3(const int8_t* q, int64_t n, int64_t k, uint8_t* packed) {
+    if (k % 64 != 0 || n < 0) return -1;
+    int64_t total = orc_packed_bytes_b3(n, k);
+    int8_t* trits = (int8_t*)malloc((size_t)(total > 0 ? 5 * total : 1));
+    if (!trits) return -1;
+    memset(trits, 0, (size_t)(5 * total));     /* padding: trit 0 */
+    for (int64_t row = 0; row < n; ++row)
+        for (int64_t col = 0; col < k; ++col) {
+            int8_t v = q[row * k + col];
+            if (v < -1 || v > 1) {
+                free(trits);
+                return -2;
+            }
+            int64_t byte;
+            int digit;
+            b3_position(row, col, k, &byte, &digit);
+            trits[5 * byte + digit] = v;
+        }
+    for (int64_t b = 0; b < total; ++b) packed[b] = orc_b3_encode(trits + 5 * b);
+    free(trits);
+    return 0;
+}
+
+/* Inverse of orc_pack_b3 for the n real rows.  Returns 0, -1 on a bad k, or
+ * -3 if any byte of the buffer (padding included) is no code. */
+int orc_unpack_b3(const uint8_t* packed, int64_t n, int64_t k, int8_t* q) {
+    if (k % 64 != 0 || n < 0) return -1;
+    int64_t total = orc_packed_bytes_b3(n, k);
+    int8_t t[5];
+    for (int64_t b = 0; b < total; ++b)
+        if (orc_b3_decode(packed[b], t) != 0) return -3;
+#pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < n; ++row) {
+        int8_t tt[5];
+        for (int64_t col = 0; col < k; ++col) {
+            int64_t byte;
+            int digit;
+            b3_position(row, col, k, &byte, &digit);
+            orc_b3_decode(packed[byte], tt);
+            q[row * k + col] = tt[digit];
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Per-token absmax 8-bit activation quantization.                          */
 /* ------------------------------------------------------------------------ */
 
@@ -379,6 +483,31 @@ int orc_bitlinear_forward(const uint8_t* packed, float gamma, const uint16_t* x,
                 trit_position(j, t, k, &byte, &bit);
                 int w = (int)((packed[byte] >> bit) & 3u) - 1;
                 s += (int64_t)w * xq[i * k + t];
+            }
+            acc[i * n + j] = (int32_t)s;
+        }
+    }
+    orc_rescale(acc, m, n, gamma, alpha, y);
+    return 0;
+}
+
+/* y = BitLinear(x) with base-3 packed ternary weights (orc_pack_b3): the same
+ * steps as orc_bitlinear_forward, reading each trit from the base-3 buffer. */
+int orc_bitlinear_forward_b3(const uint8_t* packed, float gamma, const uint16_t* x, int64_t m, int64_t n,
+                             int64_t k, int8_t* xq, float* alpha, int32_t* acc, uint16_t* y) {
+    if (k % 64 != 0) return -1;
+    orc_quant_act(x, m, k, xq, alpha);
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < n; ++j) {
+        for (int64_t i = 0; i < m; ++i) {
+            int64_t s = 0;
+            int8_t t[5];
+            for (int64_t c = 0; c < k; ++c) {
+                int64_t byte;
+                int digit;
+                b3_position(j, c, k, &byte, &digit);
+                orc_b3_decode(packed[byte], t);
+                s += (int64_t)t[digit] * xq[i * k + c];
             }
             acc[i * n + j] = (int32_t)s;
         }

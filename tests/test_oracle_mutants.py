@@ -16,7 +16,8 @@ SRC = os.path.join(ROOT, "oracle", "oracle.c")
 PINS = [os.path.join(ROOT, "tests", "test_oracle_absmean.py"),
         os.path.join(ROOT, "tests", "test_oracle_act_linear.py"),
         os.path.join(ROOT, "tests", "test_oracle_glu.py"),
-        os.path.join(ROOT, "tests", "test_oracle_backward.py")]
+        os.path.join(ROOT, "tests", "test_oracle_backward.py"),
+        os.path.join(ROOT, "tests", "test_oracle_b3.py")]
 
 MUTANTS = {
     "ternarize_round_half_away": ("float r = rintf(scaled);", "float r = roundf(scaled);"),
@@ -59,6 +60,13 @@ MUTANTS = {
     "backward_w_128": ("dw[j * k + t] = (float)(s / 127.0);", "dw[j * k + t] = (float)(s / 128.0);"),
     "pack_transposed_not_transposed": ("for (int64_t t = 0; t < k; ++t) qt[t * n + j] = q[j * k + t];",
                                        "for (int64_t t = 0; t < k; ++t) qt[j * k + t] = q[j * k + t];"),
+    "b3_floor_encoding": ("return (uint8_t)((256 * v + 242) / 243);", "return (uint8_t)((256 * v) / 243);"),
+    "b3_digit_order_reversed": ("*digit = (int)(u / 16);", "*digit = 4 - (int)(u / 16);"),
+    "b3_group_row_swapped": ("g * 256 + (row % 16) * 16 + u % 16;", "(row % 16) * 64 + g * 16 + u % 16;"),
+    "b3_padding_not_zero": ("memset(trits, 0, (size_t)(5 * total));     /* padding: trit 0 */",
+                            "memset(trits, 1, (size_t)(5 * total));     /* padding: trit 0 */"),
+    "b3_forward_digit_off_by_one": ("s += (int64_t)t[digit] * xq[i * k + c];",
+                                    "s += (int64_t)t[(digit + 1) % 5] * xq[i * k + c];"),
     "unpack_codes_not_trits": ("q[row * k + col] = (int8_t)((int)((packed[byte] >> bit) & 3u) - 1);",
                                "q[row * k + col] = (int8_t)((int)((packed[byte] >> bit) & 3u));"),
 }
