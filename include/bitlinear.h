@@ -41,8 +41,9 @@
  *     an empty problem (m or n = 0) then returns BL_OK at once, so empty
  *     tensors may pass NULL pointers.  A failed kernel launch
  *     returns BL_ERR_HIP.  Faults inside kernels surface at the caller's next
- *     synchronization.  Entry points are thread-safe (no global mutable
- *     state); calls on one stream execute in order.
+ *     synchronization.  Entry points are thread-safe; the only global
+ *     mutable state is the device array of bl_ternarize_pack_noalloc (see
+ *     there).  Calls on one stream execute in order.
  *   - Inputs must be finite (no Inf or NaN).
  */
 #ifndef BITLINEAR_H
@@ -98,6 +99,23 @@ size_t bl_ternarize_pack_workspace_bytes(int64_t n, int64_t k);
  *         BL_ERR_HIP. */
 bl_status bl_ternarize_pack(const float* w, int64_t n, int64_t k, uint8_t* packed, float* gamma,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): exactly
+ * bl_ternarize_pack (same gamma, same packed bytes), without a workspace
+ * argument.  The 2 KiB of exponent bins live in a static device array of the
+ * library, one per GPU, held until the process ends; it covers every shape
+ * bl_ternarize_pack takes (n*k <= 2^35), and larger shapes are rejected with
+ * BL_ERR_SHAPE.  The first call on a device looks the array's address up
+ * (hipGetSymbolAddress, with that device current); later calls allocate and
+ * free nothing.  Each call clears the bins on `stream` (with a kernel) before
+ * using them, so leftovers of an earlier call do not matter, but two calls
+ * that overlap on one GPU (on different streams, or from different host
+ * threads) share the array and race: serialize them.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_HIP (also when the
+ *         array's address cannot be obtained). */
+bl_status bl_ternarize_pack_noalloc(const float* w, int64_t n, int64_t k, uint8_t* packed, float* gamma,
+                                    void* stream);
 
 /* Per-token absmax int8 activation quantization [P2, P3]: for each row i,
  * a = max_j |x[i][j]|, s = fl32(127 / max(a, 1e-5f)),

@@ -22,7 +22,7 @@ __all__ = [
     "BitLinearError", "bl_packed_bytes", "bl_ternarize_pack_workspace_bytes", "bl_ternarize_pack",
     "bl_quant_act", "bl_linear", "bl_bitlinear", "bl_unpack_ternary", "bl_status_string", "library", "declared_symbols",
     "bl_ternarize_pack_glu", "bl_linear_glu", "bl_bitlinear_glu", "bl_pack_transposed", "bl_bitlinear_backward_x",
-    "bl_backward_w_workspace_bytes", "bl_bitlinear_backward_w",
+    "bl_backward_w_workspace_bytes", "bl_bitlinear_backward_w", "bl_ternarize_pack_noalloc",
 ]
 
 
@@ -45,6 +45,8 @@ _lib.bl_ternarize_pack_workspace_bytes.argtypes = [_I64, _I64]
 _lib.bl_ternarize_pack_workspace_bytes.restype = _SZ
 _lib.bl_ternarize_pack.argtypes = [_P, _I64, _I64, _P, _P, _P, _SZ, _P]
 _lib.bl_ternarize_pack.restype = ctypes.c_int
+_lib.bl_ternarize_pack_noalloc.argtypes = [_P, _I64, _I64, _P, _P, _P]
+_lib.bl_ternarize_pack_noalloc.restype = ctypes.c_int
 _lib.bl_quant_act.argtypes = [_P, _I64, _I64, _P, _P, _P]
 _lib.bl_quant_act.restype = ctypes.c_int
 _lib.bl_linear.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P]
@@ -135,6 +137,20 @@ def bl_ternarize_pack(w: torch.Tensor, packed: torch.Tensor | None = None, gamma
         workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=w.device)
     _check("bl_ternarize_pack", _lib.bl_ternarize_pack(_ptr(w), n, k, _ptr(packed), _ptr(gamma), _ptr(workspace),
                                                        workspace.numel(), _stream(w.device)))
+    return packed, gamma
+
+
+def bl_ternarize_pack_noalloc(w: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor):
+    """bl_ternarize_pack into caller-provided outputs, with the library's static
+    device bins instead of a workspace (the call itself allocates nothing)."""
+    _need(w, "w", torch.float32)
+    n, k = w.shape
+    _need(packed, "packed", torch.uint8)
+    _need(gamma, "gamma", torch.float32)
+    if packed.numel() < bl_packed_bytes(n, k) or gamma.numel() < 1:
+        raise ValueError("packed or gamma buffer too small")
+    _check("bl_ternarize_pack_noalloc", _lib.bl_ternarize_pack_noalloc(_ptr(w), n, k, _ptr(packed), _ptr(gamma),
+                                                                       _stream(w.device)))
     return packed, gamma
 
 

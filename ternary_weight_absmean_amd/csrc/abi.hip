@@ -50,6 +50,20 @@ bl_status bl_ternarize_pack(const float* w, int64_t n, int64_t k, uint8_t* packe
   return from_hip(e);
 }
 
+bl_status bl_ternarize_pack_noalloc(const float* w, int64_t n, int64_t k, uint8_t* packed, float* gamma,
+                                    void* stream) {
+  if (!w || !packed || !gamma) return BL_ERR_NULL;
+  if (n < 1 || n > BL_MAX_N || !valid_k(k) || !product_ok(n + 16, k) || n * k > kMaxPackWeights) return BL_ERR_SHAPE;
+  if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(gamma, 4)) return BL_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  unsigned long long* bins = nullptr;  // the static array's device address, never its host-side name
+  hipError_t e = bl::static_pack_bins(s, &bins);
+  if (e == hipSuccess) e = bl::launch_absmean_bins(w, n * k, bins, s);
+  if (e == hipSuccess) e = bl::launch_gamma_fold(bins, n * k, gamma, s);
+  if (e == hipSuccess) e = bl::launch_ternarize_pack(w, n, k, gamma, packed, s);
+  return from_hip(e);
+}
+
 bl_status bl_quant_act(const uint16_t* x, int64_t m, int64_t k, int8_t* xq, float* alpha, void* stream) {
   if (m < 0 || m > BL_MAX_M || !valid_k(k) || !product_ok(m, k)) return BL_ERR_SHAPE;
   if (m == 0) return BL_OK;  // empty tensors may carry NULL pointers

@@ -28,6 +28,10 @@ constexpr int kAbsmeanMaxBlocks = 256;
 constexpr size_t kPackWorkspaceBytes = 256 * sizeof(unsigned long long);
 hipError_t launch_absmean_bins(const float* w, int64_t count, unsigned long long* ws, hipStream_t s);
 hipError_t launch_gamma_fold(const unsigned long long* ws, int64_t count, float* gamma, hipStream_t s);
+// Device address of the library's static 2 KiB bin array (kPackWorkspaceBytes)
+// on the device of stream `s`, for the allocation-free packer; looked up once
+// per device (thread-safe), then cached.
+hipError_t static_pack_bins(hipStream_t s, unsigned long long** bins);
 // glu_f > 0: w is [2 * glu_f][k] gate rows then up rows, packed with
 // alternating gate/up 16-row tiles (n == 2 * glu_f, glu_f % 16 == 0).
 hipError_t launch_ternarize_pack(const float* w, int64_t n, int64_t k, const float* gamma, uint8_t* packed,

@@ -27,8 +27,19 @@
 //                      row segment; the rounding of w / (gamma + 1e-5) as an
 //                      exact threshold test
 //   k_unpack           packed -> int8 trits (inspection helper)
+//
+// The allocation-free form of the packer keeps its bins in `scratch`, a
+// static device array of this file (one copy per GPU, at its own address on
+// each); the host side looks its address up once per device.
+#include <mutex>
+
 #include "device_util.h"
 #include "internal.h"
+
+// The packer's 256 exponent bins for callers that cannot allocate a
+// workspace.  In host code this name is a stand-in for the symbol, not a
+// device address: kernels receive the address static_pack_bins() looked up.
+static __device__ __align__(256) unsigned long long scratch[256];
 
 namespace bl {
 namespace {
@@ -334,6 +345,39 @@ __global__ __launch_bounds__(kPackThreads) void k_unpack(const uint4* __restrict
 }
 
 }  // namespace
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+unsigned long long* g_scratch_ptr[kMaxDevices];  // address of `scratch` on each device, once looked up
+
+}  // namespace
+
+hipError_t static_pack_bins(hipStream_t s, unsigned long long** bins) {
+  int dev = 0;
+  hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    // the array's address on `dev`: looked up with that device current
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    void* p = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e == hipSuccess && p == nullptr) e = hipErrorInvalidSymbol;
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<unsigned long long*>(p);
+  }
+  *bins = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 int absmean_blocks(int64_t count) {
   const int64_t n4 = count / 4;

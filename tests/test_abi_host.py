@@ -59,6 +59,17 @@ def test_ternarize_pack_validation():
     assert f(FAKE, 16, 64, FAKE, FAKE, FAKE, WS - 1, None) == BL_ERR_WORKSPACE
 
 
+def test_ternarize_pack_noalloc_validation():
+    f = lib.bl_ternarize_pack_noalloc
+    assert f(None, 16, 64, FAKE, FAKE, None) == BL_ERR_NULL
+    assert f(FAKE, 16, 64, None, FAKE, None) == BL_ERR_NULL
+    assert f(FAKE, 0, 64, FAKE, FAKE, None) == BL_ERR_SHAPE
+    assert f(FAKE, 16, 96, FAKE, FAKE, None) == BL_ERR_SHAPE
+    assert f(FAKE, (1 << 13) + 16, 1 << 22, FAKE, FAKE, None) == BL_ERR_SHAPE  # past 2^35 weights
+    assert f(FAKE + 4, 16, 64, FAKE, FAKE, None) == BL_ERR_ALIGN
+    assert f(FAKE, 16, 64, FAKE, FAKE + 2, None) == BL_ERR_ALIGN
+
+
 def test_quant_act_validation():
     f = lib.bl_quant_act
     assert f(None, 1, 64, FAKE, FAKE, None) == BL_ERR_NULL
