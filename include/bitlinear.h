@@ -157,6 +157,55 @@ bl_status bl_linear(const uint8_t* packed, const float* gamma, const int8_t* xq,
 bl_status bl_bitlinear(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t n, int64_t k,
                        int8_t* xq, float* alpha, int32_t* acc, uint16_t* y, void* stream);
 
+/* ---- Five trits per byte ----
+ * The denser weight code: [P4] bako.co, "BitNet b1.58 and the 1-Bit AI
+ * Architecture Revolution", section "The Information Theory of 1.58 Bits" (a
+ * three-state weight carries log2(3), about 1.58, bits) and [P5] deepmox.com
+ * chapter 1, "Why Smaller Weights Are Not the Whole Story", section "A
+ * different place to make efficiency decisions" (the 2B4T model keeps its
+ * non-embedding weights below two bits per weight).  3^5 = 243 <= 256, so
+ * five trits share one byte: 1.6 bits per weight, 20% fewer bytes to move
+ * per decoded token than the 2-bit code, for the same gamma, trits and
+ * results. */
+
+#define BL_B3_MAX_K 64000
+#define BL_B3_MAX_M 64
+
+/* Size in bytes of the five-trits-per-byte buffer for an [n][k] matrix:
+ * ceil(n/16)*16 rows of ceil(k/320)*64 bytes.  Returns 0 for an invalid shape. */
+size_t bl_packed_bytes_b3(int64_t n, int64_t k);
+
+/* Weight preparation in the five-trits-per-byte code [P1, P4, P5]: the same
+ * gamma and trits as bl_ternarize_pack, stored as follows.  Five trits t_0..t_4
+ * with codes c_d = t_d + 1 form v = sum_d c_d * 3^(4-d); the byte is
+ * ceil(256 * v / 243) (so v = floor(243 * b / 256), and digit d is also
+ * floor(3 * ((b * 3^d) mod 256) / 256)).  The matrix is cut into super-tiles
+ * of 16 rows x 320 columns, 1024 bytes each, column super-tile fastest
+ * (super-tile (i, s) at byte 1024 * (i * ceil(k/320) + s)); inside one,
+ * column 80 g + 16 d + j (g < 4, d < 5, j < 16) of row r sits in byte
+ * 256 g + 16 r + j as digit d.  Columns past k and rows past n hold trit 0.
+ *   w, gamma, workspace as for bl_ternarize_pack; packed has
+ *   bl_packed_bytes_b3(n, k) bytes.
+ * Errors: as bl_ternarize_pack. */
+bl_status bl_ternarize_pack_b3(const float* w, int64_t n, int64_t k, uint8_t* packed, float* gamma,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* The whole layer from five-trits-per-byte weights, for decoding [P1, P2, P3,
+ * P4]: per-token absmax int8 quantization of x (xq, alpha written exactly as
+ * bl_quant_act would) and the ternary product with the bf16 rescale, with
+ * exactly the results of bl_quant_act followed by bl_linear on the 2-bit
+ * packing of the same trits.  One kernel per call; every token is its own
+ * pass over the weights, so the call is meant for few tokens (m up to
+ * BL_B3_MAX_M) and rows up to BL_B3_MAX_K columns (a row's activations are
+ * held on chip).
+ *   packed/gamma from bl_ternarize_pack_b3 for an [n][k] matrix;
+ *   x [m][k] bf16; xq out [m][k] int8; alpha out [m] fp32;
+ *   acc, y as in bl_linear (either may be NULL, not both).
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE (m > BL_B3_MAX_M, k > BL_B3_MAX_K, or
+ *         as bl_bitlinear), BL_ERR_ALIGN, BL_ERR_HIP. */
+bl_status bl_bitlinear_b3(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t n,
+                          int64_t k, int8_t* xq, float* alpha, int32_t* acc, uint16_t* y, void* stream);
+
 /* ---- Gated feed-forward front half: gate+up BitLinear + squared ReLU ----
  * A feed-forward block with f hidden units has one gate+up BitLinear of 2f
  * output rows (rows 0..f-1 the gate, rows f..2f-1 the up projection; one

@@ -23,6 +23,7 @@ __all__ = [
     "bl_quant_act", "bl_linear", "bl_bitlinear", "bl_unpack_ternary", "bl_status_string", "library", "declared_symbols",
     "bl_ternarize_pack_glu", "bl_linear_glu", "bl_bitlinear_glu", "bl_pack_transposed", "bl_bitlinear_backward_x",
     "bl_backward_w_workspace_bytes", "bl_bitlinear_backward_w", "bl_ternarize_pack_noalloc",
+    "bl_packed_bytes_b3", "bl_ternarize_pack_b3", "bl_bitlinear_b3",
 ]
 
 
@@ -47,6 +48,12 @@ _lib.bl_ternarize_pack.argtypes = [_P, _I64, _I64, _P, _P, _P, _SZ, _P]
 _lib.bl_ternarize_pack.restype = ctypes.c_int
 _lib.bl_ternarize_pack_noalloc.argtypes = [_P, _I64, _I64, _P, _P, _P]
 _lib.bl_ternarize_pack_noalloc.restype = ctypes.c_int
+_lib.bl_packed_bytes_b3.argtypes = [_I64, _I64]
+_lib.bl_packed_bytes_b3.restype = _SZ
+_lib.bl_ternarize_pack_b3.argtypes = [_P, _I64, _I64, _P, _P, _P, _SZ, _P]
+_lib.bl_ternarize_pack_b3.restype = ctypes.c_int
+_lib.bl_bitlinear_b3.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]
+_lib.bl_bitlinear_b3.restype = ctypes.c_int
 _lib.bl_quant_act.argtypes = [_P, _I64, _I64, _P, _P, _P]
 _lib.bl_quant_act.restype = ctypes.c_int
 _lib.bl_linear.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P]
@@ -152,6 +159,58 @@ def bl_ternarize_pack_noalloc(w: torch.Tensor, packed: torch.Tensor, gamma: torc
     _check("bl_ternarize_pack_noalloc", _lib.bl_ternarize_pack_noalloc(_ptr(w), n, k, _ptr(packed), _ptr(gamma),
                                                                        _stream(w.device)))
     return packed, gamma
+
+
+def bl_packed_bytes_b3(n: int, k: int) -> int:
+    return int(_lib.bl_packed_bytes_b3(n, k))
+
+
+def bl_ternarize_pack_b3(w: torch.Tensor, packed: torch.Tensor | None = None, gamma: torch.Tensor | None = None,
+                         workspace: torch.Tensor | None = None):
+    """fp32 weights ``[n][k]`` -> (five-trits-per-byte uint8 [bl_packed_bytes_b3], gamma fp32 [1])."""
+    _need(w, "w", torch.float32)
+    n, k = w.shape
+    if packed is None:
+        packed = torch.empty(max(bl_packed_bytes_b3(n, k), 1), dtype=torch.uint8, device=w.device)
+    if gamma is None:
+        gamma = torch.empty(1, dtype=torch.float32, device=w.device)
+    if workspace is None:
+        workspace = torch.empty(max(bl_ternarize_pack_workspace_bytes(n, k), 16), dtype=torch.uint8, device=w.device)
+    _check("bl_ternarize_pack_b3", _lib.bl_ternarize_pack_b3(_ptr(w), n, k, _ptr(packed), _ptr(gamma),
+                                                             _ptr(workspace), workspace.numel(), _stream(w.device)))
+    return packed, gamma
+
+
+def bl_bitlinear_b3(packed: torch.Tensor, gamma: torch.Tensor, x: torch.Tensor, n: int,
+                    xq: torch.Tensor | None = None, alpha: torch.Tensor | None = None,
+                    acc: torch.Tensor | None | bool = True, y: torch.Tensor | None | bool = True):
+    """bf16 activations ``[m][k]`` through the layer with five-trits-per-byte
+    weights: returns (acc or None, y or None, xq, alpha)."""
+    _need(x, "x", torch.bfloat16)
+    m, k = x.shape
+    dev = x.device
+    if xq is None:
+        xq = torch.empty((m, k), dtype=torch.int8, device=dev)
+    if alpha is None:
+        alpha = torch.empty(m, dtype=torch.float32, device=dev)
+    _need(xq, "xq", torch.int8, (m, k))
+    _need(alpha, "alpha", torch.float32, (m,))
+    if acc is True:
+        acc = torch.empty((m, n), dtype=torch.int32, device=dev)
+    if y is True:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    acc = acc if isinstance(acc, torch.Tensor) else None
+    y = y if isinstance(y, torch.Tensor) else None
+    if acc is not None:
+        _need(acc, "acc", torch.int32, (m, n))
+    if y is not None:
+        _need(y, "y", torch.bfloat16, (m, n))
+    _need(packed, "packed", torch.uint8)
+    if packed.numel() < bl_packed_bytes_b3(n, k):
+        raise ValueError("packed buffer is smaller than bl_packed_bytes_b3(n, k)")
+    _check("bl_bitlinear_b3", _lib.bl_bitlinear_b3(_ptr(packed), _ptr(gamma), _ptr(x), m, n, k, _ptr(xq),
+                                                   _ptr(alpha), _ptr(acc), _ptr(y), _stream(dev)))
+    return acc, y, xq, alpha
 
 
 def bl_quant_act(x: torch.Tensor, xq: torch.Tensor | None = None, alpha: torch.Tensor | None = None):

@@ -1,4 +1,5 @@
-"""Build ``libbitlinear.so`` (the C-ABI HIP library) for gfx950 with hipcc."""
+"""Build ``libbitlinear.so`` (the C-ABI HIP library) and ``libblmeasure.so`` (the
+benchmark's reference kernels) for gfx950 with hipcc."""
 from __future__ import annotations
 
 import os
@@ -10,7 +11,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libbitlinear.so")
-SOURCES = ["abi.hip", "pack.hip", "quant.hip", "gemv.hip", "gemm.hip", "backward.hip"]
+SOURCES = ["abi.hip", "pack.hip", "quant.hip", "gemv.hip", "gemm.hip", "backward.hip", "b3.hip"]
+MEASURE_LIB_PATH = os.path.join(HERE, "libblmeasure.so")
+MEASURE_SOURCES = ["measure.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -49,43 +52,49 @@ def kernel_resources(compiler_output: str) -> dict:
     return kernels
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source in parallel and link the shared library.
-    Every kernel must run from registers: a kernel with scratch memory (a
-    spill, or a register array indexed at run time) fails the build."""
-    with tempfile.TemporaryDirectory(prefix="bitlinear_build_") as tmp:
-        procs, objs = [], []
-        for src in SOURCES:
-            obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
-            cmd = [HIPCC, *FLAGS, RESOURCE_REMARKS, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj]
+def _build_lib(sources, lib_path, tmp, verbose):
+    """Compile `sources` in parallel and link them into `lib_path`.  Every
+    kernel must run from registers: a kernel with scratch memory (a spill, or
+    a register array indexed at run time) fails the build."""
+    procs, objs = [], []
+    for src in sources:
+        obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
+        cmd = [HIPCC, *FLAGS, RESOURCE_REMARKS, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd))
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+        objs.append(obj)
+    failed, scratch = [], []
+    for src, p in procs:
+        out, _ = p.communicate()
+        lines = [ln for ln in out.splitlines() if "packed-fp32-ops" not in ln and "remark:" not in ln
+                 and "kernel-resource-usage" not in ln]
+        if lines and (verbose or p.returncode):
+            print("\n".join(lines))
+        if p.returncode:
+            failed.append(src)
+            continue
+        for name, res in kernel_resources(out).items():
             if verbose:
-                print(" ".join(cmd))
-            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
-            objs.append(obj)
-        failed, scratch = [], []
-        for src, p in procs:
-            out, _ = p.communicate()
-            lines = [ln for ln in out.splitlines() if "packed-fp32-ops" not in ln and "remark:" not in ln
-                     and "kernel-resource-usage" not in ln]
-            if lines and (verbose or p.returncode):
-                print("\n".join(lines))
-            if p.returncode:
-                failed.append(src)
-                continue
-            for name, res in kernel_resources(out).items():
-                if verbose:
-                    print(f"{src}: {name}: VGPRs {res.get('VGPRs')} AGPRs {res.get('AGPRs')} "
-                          f"scratch {res.get('ScratchSize [bytes/lane]')} LDS {res.get('LDS Size [bytes/block]')}")
-                if res.get("ScratchSize [bytes/lane]", "0") != "0":
-                    scratch.append(f"{src}: {name} ({res['ScratchSize [bytes/lane]']} bytes/lane)")
-        if failed:
-            raise RuntimeError(f"hipcc failed for {failed}")
-        if scratch:
-            raise RuntimeError("kernels using scratch memory: " + "; ".join(scratch))
-        tmp_lib = LIB_PATH + ".tmp"
-        subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", *objs, "-o", tmp_lib],
-                       check=True)
-        os.replace(tmp_lib, LIB_PATH)
+                print(f"{src}: {name}: VGPRs {res.get('VGPRs')} AGPRs {res.get('AGPRs')} "
+                      f"scratch {res.get('ScratchSize [bytes/lane]')} LDS {res.get('LDS Size [bytes/block]')}")
+            if res.get("ScratchSize [bytes/lane]", "0") != "0":
+                scratch.append(f"{src}: {name} ({res['ScratchSize [bytes/lane]']} bytes/lane)")
+    if failed:
+        raise RuntimeError(f"hipcc failed for {failed}")
+    if scratch:
+        raise RuntimeError("kernels using scratch memory: " + "; ".join(scratch))
+    tmp_lib = lib_path + ".tmp"
+    subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", *objs, "-o", tmp_lib],
+                   check=True)
+    os.replace(tmp_lib, lib_path)
+
+
+def build(verbose: bool = False) -> str:
+    """Build both libraries; returns the path of libbitlinear.so."""
+    with tempfile.TemporaryDirectory(prefix="bitlinear_build_") as tmp:
+        _build_lib(SOURCES, LIB_PATH, tmp, verbose)
+        _build_lib(MEASURE_SOURCES, MEASURE_LIB_PATH, tmp, verbose)
     return LIB_PATH
 
 

@@ -64,6 +64,37 @@ bl_status bl_ternarize_pack_noalloc(const float* w, int64_t n, int64_t k, uint8_
   return from_hip(e);
 }
 
+size_t bl_packed_bytes_b3(int64_t n, int64_t k) {
+  if (n < 0 || n > BL_MAX_N || !valid_k(k) || !product_ok(n + 16, k)) return 0;
+  return bl::packed_bytes_b3(n, k);
+}
+
+bl_status bl_ternarize_pack_b3(const float* w, int64_t n, int64_t k, uint8_t* packed, float* gamma, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (!w || !packed || !gamma || !workspace) return BL_ERR_NULL;
+  if (n < 1 || n > BL_MAX_N || !valid_k(k) || !product_ok(n + 16, k) || n * k > kMaxPackWeights) return BL_ERR_SHAPE;
+  if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(gamma, 4) || !aligned(workspace, 16)) return BL_ERR_ALIGN;
+  if (workspace_bytes < bl_ternarize_pack_workspace_bytes(n, k)) return BL_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  unsigned long long* bins = (unsigned long long*)workspace;
+  hipError_t e = bl::launch_absmean_bins(w, n * k, bins, s);
+  if (e == hipSuccess) e = bl::launch_gamma_fold(bins, n * k, gamma, s);
+  if (e == hipSuccess) e = bl::launch_ternarize_pack_b3(w, n, k, gamma, packed, s);
+  return from_hip(e);
+}
+
+bl_status bl_bitlinear_b3(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t n,
+                          int64_t k, int8_t* xq, float* alpha, int32_t* acc, uint16_t* y, void* stream) {
+  if (m < 0 || m > BL_B3_MAX_M || n < 0 || n > BL_MAX_N || !valid_k(k) || k > BL_B3_MAX_K || !product_ok(n + 16, k))
+    return BL_ERR_SHAPE;
+  if (m == 0 || n == 0) return BL_OK;  // empty tensors may carry NULL pointers
+  if (!packed || !gamma || !x || !xq || !alpha || (!acc && !y)) return BL_ERR_NULL;
+  if (!aligned(packed, 16) || !aligned(x, 16) || !aligned(xq, 16) || !aligned(gamma, 4) || !aligned(alpha, 4) ||
+      (acc && !aligned(acc, 4)) || (y && !aligned(y, 2)))
+    return BL_ERR_ALIGN;
+  return from_hip(bl::launch_bitlinear_b3(packed, gamma, x, m, n, k, xq, alpha, acc, y, (hipStream_t)stream));
+}
+
 bl_status bl_quant_act(const uint16_t* x, int64_t m, int64_t k, int8_t* xq, float* alpha, void* stream) {
   if (m < 0 || m > BL_MAX_M || !valid_k(k) || !product_ok(m, k)) return BL_ERR_SHAPE;
   if (m == 0) return BL_OK;  // empty tensors may carry NULL pointers

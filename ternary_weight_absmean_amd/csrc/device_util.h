@@ -181,4 +181,37 @@ __device__ __forceinline__ v4i mfma_16x16x64(const v4i& a, const v4i& b, const v
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ void add4(v4i& a, const v4i& b) {
+  a.x += b.x;
+  a.y += b.y;
+  a.z += b.z;
+  a.w += b.w;
+}
+
+// Epilogue of a 16-row tile product: the lane holds the int32 sums of rows
+// row0 .. row0 + 3 for token `tok`; writes acc (if non-NULL) and y = bf16(acc
+// * scale) (if non-NULL), rows past n skipped.
+__device__ __forceinline__ void store_tile(const v4i& acc, int64_t row0, int64_t tok, int64_t n, float scale,
+                                           int32_t* __restrict__ acc_out, uint16_t* __restrict__ y_out) {
+  const int vals[4] = {acc.x, acc.y, acc.z, acc.w};
+  // four consecutive outputs of one token: one 16-byte and one 8-byte store when aligned
+  uint16_t* yp = y_out ? y_out + tok * n + row0 : nullptr;
+  int32_t* ap = acc_out ? acc_out + tok * n + row0 : nullptr;
+  if (row0 + 3 < n && (!yp || ((uintptr_t)yp & 7) == 0) && (!ap || ((uintptr_t)ap & 15) == 0)) {
+    if (ap) *reinterpret_cast<int4*>(ap) = make_int4(vals[0], vals[1], vals[2], vals[3]);
+    if (yp)
+      *reinterpret_cast<uint2*>(yp) = make_uint2(f32x2_to_bf16x2((float)vals[0] * scale, (float)vals[1] * scale),
+                                                 f32x2_to_bf16x2((float)vals[2] * scale, (float)vals[3] * scale));
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = row0 + i;
+    if (row < n) {
+      if (acc_out) acc_out[tok * n + row] = vals[i];
+      if (y_out) y_out[tok * n + row] = f32_to_bf16_rne((float)vals[i] * scale);
+    }
+  }
+}
+
 }  // namespace bl

@@ -60,37 +60,6 @@ __device__ __forceinline__ v4i mask4(const uint4& a, uint32_t mask, int shift) {
   return r;
 }
 
-__device__ __forceinline__ void add4(v4i& a, const v4i& b) {
-  a.x += b.x;
-  a.y += b.y;
-  a.z += b.z;
-  a.w += b.w;
-}
-
-// Epilogue for wave 0: lane holds rows 4*(lane/16) + i of the tile, token `tok`.
-__device__ __forceinline__ void store_tile(const v4i& acc, int64_t row0, int64_t tok, int64_t n, float scale,
-                                           int32_t* __restrict__ acc_out, uint16_t* __restrict__ y_out) {
-  const int vals[4] = {acc.x, acc.y, acc.z, acc.w};
-  // four consecutive outputs of one token: one 16-byte and one 8-byte store when aligned
-  uint16_t* yp = y_out ? y_out + tok * n + row0 : nullptr;
-  int32_t* ap = acc_out ? acc_out + tok * n + row0 : nullptr;
-  if (row0 + 3 < n && (!yp || ((uintptr_t)yp & 7) == 0) && (!ap || ((uintptr_t)ap & 15) == 0)) {
-    if (ap) *reinterpret_cast<int4*>(ap) = make_int4(vals[0], vals[1], vals[2], vals[3]);
-    if (yp)
-      *reinterpret_cast<uint2*>(yp) = make_uint2(f32x2_to_bf16x2((float)vals[0] * scale, (float)vals[1] * scale),
-                                                 f32x2_to_bf16x2((float)vals[2] * scale, (float)vals[3] * scale));
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t row = row0 + i;
-    if (row < n) {
-      if (acc_out) acc_out[tok * n + row] = vals[i];
-      if (y_out) y_out[tok * n + row] = f32_to_bf16_rne((float)vals[i] * scale);
-    }
-  }
-}
-
 // Gated outputs h[tok][col0 .. col0 + 3] = bf16(relu(g)^2 * u) from the exact
 // products of four gate rows (g) and the four matching up rows (u).
 __device__ __forceinline__ void store_glu_tile(const v4i& g, const v4i& u, int64_t col0, int64_t tok, int64_t f,

@@ -47,6 +47,17 @@ hipError_t launch_backward_w(const uint16_t* dy, const int8_t* xq, const float* 
                              float* dw, void* workspace, hipStream_t s);
 hipError_t launch_unpack(const uint8_t* packed, int64_t n, int64_t k, int8_t* q, hipStream_t s);
 
+// Five trits per byte (base 3): 16-row x 320-column super-tiles of 1 KiB.
+// The fused single-token decode holds a row's activations on chip: k up to
+// kB3MaxK (25 super-tiles per wave of eight); m tokens run as m passes.
+constexpr int64_t kB3MaxK = 64000;
+constexpr int64_t kB3MaxM = 64;
+size_t packed_bytes_b3(int64_t n, int64_t k);
+hipError_t launch_ternarize_pack_b3(const float* w, int64_t n, int64_t k, const float* gamma, uint8_t* packed,
+                                    hipStream_t s);
+hipError_t launch_bitlinear_b3(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t n,
+                               int64_t k, int8_t* xq, float* alpha, int32_t* acc, uint16_t* y, hipStream_t s);
+
 // Per-token absmax int8 quantizer.
 hipError_t launch_quant_act(const uint16_t* x, int64_t m, int64_t k, int8_t* xq, float* alpha, hipStream_t s);
 

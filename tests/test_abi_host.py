@@ -25,6 +25,30 @@ def test_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def test_measurement_library_exports_and_validates():
+    """libblmeasure.so (the benchmark's reference kernels) exports every
+    function include/blmeasure.h declares and rejects bad arguments on the host."""
+    import os
+    import re
+    from ternary_weight_absmean_amd._build import INCLUDE, MEASURE_LIB_PATH
+
+    with open(os.path.join(INCLUDE, "blmeasure.h")) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(blmeasure_\w+)\s*\(", text)))
+    assert names == ["blmeasure_stream_read", "blmeasure_stream_read_sink_words"]
+    m = ctypes.CDLL(MEASURE_LIB_PATH)
+    for name in names:
+        assert hasattr(m, name), name
+    m.blmeasure_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    m.blmeasure_stream_read_sink_words.argtypes = [ctypes.c_size_t]
+    m.blmeasure_stream_read_sink_words.restype = ctypes.c_size_t
+    assert m.blmeasure_stream_read_sink_words(1 << 30) >= 1
+    assert m.blmeasure_stream_read(None, 1 << 20, FAKE, None) == 1
+    assert m.blmeasure_stream_read(FAKE, 0, FAKE, None) == 1
+    assert m.blmeasure_stream_read(FAKE, 1000, FAKE, None) == 1       # not whole 32 KiB steps
+    assert m.blmeasure_stream_read(FAKE + 8, 1 << 20, FAKE, None) == 1  # misaligned
+
+
 def test_status_strings():
     for code in range(6):
         assert bl.bl_status_string(code).startswith("BL_")
@@ -68,6 +92,34 @@ def test_ternarize_pack_noalloc_validation():
     assert f(FAKE, (1 << 13) + 16, 1 << 22, FAKE, FAKE, None) == BL_ERR_SHAPE  # past 2^35 weights
     assert f(FAKE + 4, 16, 64, FAKE, FAKE, None) == BL_ERR_ALIGN
     assert f(FAKE, 16, 64, FAKE, FAKE + 2, None) == BL_ERR_ALIGN
+
+
+def test_b3_entry_points_validation():
+    assert bl.bl_packed_bytes_b3(16, 320) == 1024
+    assert bl.bl_packed_bytes_b3(2560, 2560) == 2560 * 512
+    assert bl.bl_packed_bytes_b3(17, 64) == 32 * 64
+    assert bl.bl_packed_bytes_b3(16, 100) == 0
+    WS = 256 * 8
+    pack = lib.bl_ternarize_pack_b3
+    assert pack(None, 16, 64, FAKE, FAKE, FAKE, WS, None) == BL_ERR_NULL
+    assert pack(FAKE, 0, 64, FAKE, FAKE, FAKE, WS, None) == BL_ERR_SHAPE
+    assert pack(FAKE, 16, 96, FAKE, FAKE, FAKE, WS, None) == BL_ERR_SHAPE
+    assert pack(FAKE + 4, 16, 64, FAKE, FAKE, FAKE, WS, None) == BL_ERR_ALIGN
+    assert pack(FAKE, 16, 64, FAKE, FAKE, FAKE, WS - 1, None) == BL_ERR_WORKSPACE
+    f = lib.bl_bitlinear_b3
+
+    def call(packed=FAKE, gamma=FAKE, x=FAKE, m=1, n=16, k=64, xq=FAKE, alpha=FAKE, acc=FAKE, y=FAKE):
+        return f(packed, gamma, x, m, n, k, xq, alpha, acc, y, None)
+
+    assert call(x=None) == BL_ERR_NULL
+    assert call(acc=None, y=None) == BL_ERR_NULL
+    assert call(m=65) == BL_ERR_SHAPE           # more tokens than the decode call takes
+    assert call(k=64064) == BL_ERR_SHAPE        # row longer than the on-chip activations
+    assert call(k=100) == BL_ERR_SHAPE
+    assert call(x=FAKE + 4) == BL_ERR_ALIGN
+    assert call(y=FAKE + 1) == BL_ERR_ALIGN
+    assert call(m=0, x=None, xq=None) == BL_OK
+    assert call(n=0) == BL_OK
 
 
 def test_quant_act_validation():
