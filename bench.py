@@ -208,7 +208,10 @@ def main() -> int:
         us = 1000.0 * time_graph(capture(sel), max(args.steps, 20)) / len(sel)
         wb = bl.bl_packed_bytes(n, k)
         per_projection[name] = {"KxN": f"{k}x{n}", "us_per_launch": round(us, 3),
-                                "weight_GBps": round(wb / (us * 1e-6) / 1e9, 1)}
+                                "weight_GBps": round(wb / (us * 1e-6) / 1e9, 1),
+                                "weights_MB": round(wb * len(sel) / 1e6, 1),
+                                # the 30 matrices of one shape: below 256 MB the Infinity Cache can hold them
+                                "cache_resident": wb * len(sel) <= INFINITY_CACHE_BYTES}
 
     extras = None
     if not args.no_extras:
@@ -264,6 +267,9 @@ def main() -> int:
         "eager": {"ms_per_step": round(eager_ms, 4), "tokens_per_s": round(m * 1000.0 / eager_ms, 2)},
         "wall_s_timed": round(wall, 4),
         "roofline": {"bound": "hbm", "kernel": f"{STACK_KERNEL} (bl_bitlinear, all {len(linears)} launches)",
+                     "time_source": (f"HIP events around {args.steps} replays of the captured step ({len(linears)} "
+                                     "launches back to back on one stream); per launch = step time / launches, "
+                                     "the gap between dependent launches included"),
                      "achieved": round(gemv_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gemv_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": stored_traffic(STACK_WORKLOAD, STACK_KERNEL, avg_bytes),
@@ -285,6 +291,7 @@ def main() -> int:
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+INFINITY_CACHE_BYTES = 256 * 1000 ** 2  # MI355X last-level (MALL) cache
 MFMA_I8_PEAK_TOPS = 5000.0
 CALIB_BYTES = 1 << 30
 STACK_WORKLOAD = "bitnet-b1.58-2B-shaped decode stack, M=1"
@@ -364,22 +371,39 @@ def summarize(args):
         trace = _find(args.stats, "kernel_trace.csv") if args.stats else None
     except FileNotFoundError:  # a stats directory without the per-dispatch trace
         trace = None
+    s2s = {}
     if trace:
         per = collections.defaultdict(list)
-        for r in _read_csv(trace):
+        rows = sorted(_read_csv(trace), key=lambda r: int(r["Start_Timestamp"]))
+        for r in rows:
             per[_base_name(r["Kernel_Name"])].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
         late = {k: sum(v[len(v) // 2:]) / len(v[len(v) // 2:]) for k, v in per.items() if v}
+        # start-to-start interval of consecutive dispatches of the same kernel
+        # (graph replays: one launch after the other), gaps over 100 us
+        # (between replays, or host work) left out
+        gaps = collections.defaultdict(list)
+        for a, b in zip(rows, rows[1:]):
+            ka, kb = _base_name(a["Kernel_Name"]), _base_name(b["Kernel_Name"])
+            d = int(b["Start_Timestamp"]) - int(a["Start_Timestamp"])
+            if ka == kb and d < 100000:
+                gaps[ka].append(d)
+        for k, v in gaps.items():
+            v = sorted(v)
+            s2s[k] = (sum(v) / len(v), v[len(v) // 2], len(v))
     if grouped:
         lines += ["## Kernel durations (--kernel-trace --stats; template instances summed)", "",
-                  "The tracer separates dispatches (each kernel runs without its neighbours); the last column "
-                  "averages the later half of a kernel's dispatches.", "",
-                  "| kernel | calls | avg (us) | min (us) | max (us) | share of GPU time | avg, later half (us) |",
-                  "|---|---|---|---|---|---|---|"]
+                  "avg, later half: the later half of a kernel's dispatches.  start-to-start: the interval between "
+                  "the starts of consecutive dispatches of the same kernel (launches back to back, e.g. within a "
+                  "graph replay; intervals over 100 us left out), mean and median, and how many.", "",
+                  "| kernel | calls | avg (us) | min (us) | max (us) | share of GPU time | avg, later half (us) "
+                  "| start-to-start mean / median (us), intervals |",
+                  "|---|---|---|---|---|---|---|---|"]
         total = sum(g["total"] for g in grouped.values())
         for base, g in grouped.items():
             lh = f"{late[base] / 1e3:.3f}" if base in late else "-"
+            ss = f"{s2s[base][0] / 1e3:.3f} / {s2s[base][1] / 1e3:.3f}, {s2s[base][2]}" if base in s2s else "-"
             lines.append(f"| {base} | {g['calls']} | {g['total'] / g['calls'] / 1e3:.3f} | {g['min'] / 1e3:.3f} | "
-                         f"{g['max'] / 1e3:.3f} | {100 * g['total'] / total:.1f}% | {lh} |")
+                         f"{g['max'] / 1e3:.3f} | {100 * g['total'] / total:.1f}% | {lh} | {ss} |")
         lines.append("")
     counters = collections.OrderedDict()  # counter -> {kernel: (avg value, avg duration ns, dispatches)}
     for d in args.pmc:
@@ -484,6 +508,68 @@ def stored_traffic(workload: str, kernel: str, algorithmic_bytes: float):
 
 
 # ---------------------------------------------------------------- short programs for rocprofv3
+
+
+def _profile_stack_2b_m1(args):
+    """The benchmark's step alone: the 30-layer 2B-shaped stack packed, the
+    step captured as a HIP graph (120 bl_bitlinear launches at one token),
+    5 warm replays, then --reps timed replays back to back."""
+    import numpy as np
+    import torch
+    import datagen
+    import ternary_weight_absmean_amd as bl
+
+    dev = torch.device("cuda", 0)
+    wl = datagen.WORKLOAD_STACK_2B
+    vp = ctypes.c_void_p
+    lib = bl.library()
+    calls, keep = [], []
+    for layer in range(datagen.STACK_2B_LAYERS):
+        for pi, (name, k, n) in enumerate(datagen.STACK_2B_PROJ):
+            w = torch.from_numpy(datagen.weights(datagen.stream_id(wl, layer, pi, datagen.TENSOR_W), n, k)).to(dev)
+            packed, gamma = bl.bl_ternarize_pack(w)
+            del w
+            cols = datagen.outlier_columns(wl, k, datagen.STACK_2B_OUTLIERS)
+            x = datagen.activations_bf16(datagen.stream_id(wl, layer, pi, datagen.TENSOR_X), 1, k, cols,
+                                         datagen.STACK_2B_OUTLIER_MULT)
+            xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+            xq = torch.empty((1, k), dtype=torch.int8, device=dev)
+            alpha = torch.empty(1, dtype=torch.float32, device=dev)
+            y = torch.empty((1, n), dtype=torch.bfloat16, device=dev)
+            keep.append((packed, gamma, xd, xq, alpha, y))
+            calls.append((vp(packed.data_ptr()), vp(gamma.data_ptr()), vp(xd.data_ptr()), n, k, vp(xq.data_ptr()),
+                          vp(alpha.data_ptr()), vp(y.data_ptr())))
+    torch.cuda.synchronize()
+    print(f"[profile] stack_2b_m1: {len(calls)} linears packed", flush=True)
+
+    def step():
+        s = vp(torch.cuda.current_stream().cuda_stream)
+        for packed, gamma, x, n, k, xq, alpha, y in calls:
+            rc = lib.bl_bitlinear(packed, gamma, x, 1, n, k, xq, alpha, None, y, s)
+            if rc:
+                raise RuntimeError(bl.bl_status_string(rc))
+
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(5):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.reps
+    print(f"[profile] stack_2b_m1: {args.reps} replays, {ms:.4f} ms per step, "
+          f"{1000 * ms / len(calls):.3f} us per launch (HIP events)", flush=True)
+    return 0
 
 
 def _profile_prefill_2b(args):
@@ -608,6 +694,7 @@ def _profile_training_2b(args):
 
 
 PROFILE_CASES = {
+    "stack_2b_m1": _profile_stack_2b_m1,
     "prefill_2b": _profile_prefill_2b,
     "training_2b": _profile_training_2b,
     "decode_70b": lambda args: _profile_70b(args, (1, 16)),
@@ -755,6 +842,8 @@ def measure_extras(args, linears, lib):
         e = {"gate_up_glu_us": round(ms_glu * 1e3, 2), "ffn_gate_up_glu_down_us": round(ms_chain * 1e3, 2)}
         if m == 1:
             e["gate_up_glu_weight_GBps"] = round(packed_glu.numel() / (ms_glu * 1e-3) / 1e9, 1)
+            # one 8.8 MB matrix re-read by every call: served by the caches, not an HBM figure
+            e["cache_resident"] = True
         else:
             e["gate_up_glu_TOPS"] = round(ops / (ms_glu * 1e-3) / 1e12, 1)
             e["gate_up_glu_frac_of_int8_mfma_peak"] = round(ops / (ms_glu * 1e-3) / 1e12 / MFMA_I8_PEAK_TOPS, 4)
@@ -762,6 +851,16 @@ def measure_extras(args, linears, lib):
         del x, xq, alpha, h, xq2, alpha2, y2
     out["ffn_glu_2b_layer0"] = ffn
     del packed_glu, gamma_glu
+
+    # ---- chained feed-forward through the 30 layers: h = bl_bitlinear_glu(x)
+    # with layer l's gate+up (squared-ReLU gated), then x' = bl_bitlinear(h)
+    # with its down projection feeding layer l + 1 (60 dependent launches per
+    # token; 398 MB of weights, more than the Infinity Cache)
+    out["ffn_chain_2b"] = measure_ffn_chain(args, linears, lib)
+
+    # ---- config-1 decode (2560 x 2560, one token) over 320 distinct copies
+    # of the packed matrix (524 MB), so that each launch streams from HBM
+    out["single_2560_rotated"] = measure_single_rotated(args, lib)
 
     # ---- training side, 2B layer 0 gate+up and down at M = 2048: the
     # straight-through gradients and the per-step re-ternarization
@@ -883,6 +982,193 @@ def measure_extras(args, linears, lib):
     out["layer_70b"] = r70
     del copies, layer
     torch.cuda.empty_cache()
+
+    # ---- the same decode with five-trits-per-byte weights
+    out["b3"] = measure_b3(args, linears, lib)
+    return out
+
+
+def measure_ffn_chain(args, linears, lib):
+    import numpy as np
+    import torch
+
+    import datagen
+    import ternary_weight_absmean_amd as bl
+
+    dev = torch.device("cuda", 0)
+    vp = ctypes.c_void_p
+    wl = datagen.WORKLOAD_STACK_2B
+    gus = [l for l in linears if l["name"] == "gate_up"]
+    dns = [l for l in linears if l["name"] == "down"]
+    f = gus[0]["n"] // 2
+    k_in = gus[0]["k"]
+    glu = []
+    for layer, gu in enumerate(gus):
+        w = torch.from_numpy(datagen.weights(datagen.stream_id(wl, layer, 2, datagen.TENSOR_W), gu["n"], gu["k"])).to(dev)
+        glu.append(bl.bl_ternarize_pack_glu(w))
+        del w
+    torch.cuda.synchronize()
+    weight_bytes = sum(p.numel() for p, _ in glu) + sum(d["packed"].numel() for d in dns)
+    res = {"layers": len(gus), "weights_MB": round(weight_bytes / 1e6, 1),
+           "launch": "per layer: bl_bitlinear_glu (gate+up, squared ReLU) then bl_bitlinear (down), chained"}
+    for m in (1, 16):
+        cols = datagen.outlier_columns(wl, k_in, datagen.STACK_2B_OUTLIERS)
+        x0 = datagen.activations_bf16(datagen.stream_id(wl, 0, 2, datagen.TENSOR_X) + 9000 + m, m, k_in, cols,
+                                      datagen.STACK_2B_OUTLIER_MULT)
+        xs = [torch.from_numpy(x0.view(np.int16)).to(dev).view(torch.bfloat16)]
+        xs += [torch.empty((m, k_in), dtype=torch.bfloat16, device=dev) for _ in gus]
+        h = torch.empty((m, f), dtype=torch.bfloat16, device=dev)
+        xq1 = torch.empty((m, k_in), dtype=torch.int8, device=dev)
+        xq2 = torch.empty((m, f), dtype=torch.int8, device=dev)
+        a1 = torch.empty(m, dtype=torch.float32, device=dev)
+        a2 = torch.empty(m, dtype=torch.float32, device=dev)
+
+        def chain():
+            s = vp(torch.cuda.current_stream().cuda_stream)
+            for layer, ((pk, gm), dn) in enumerate(zip(glu, dns)):
+                rc = lib.bl_bitlinear_glu(vp(pk.data_ptr()), vp(gm.data_ptr()), vp(xs[layer].data_ptr()), m, f, k_in,
+                                          vp(xq1.data_ptr()), vp(a1.data_ptr()), vp(h.data_ptr()), s)
+                rc = rc or lib.bl_bitlinear(vp(dn["packed"].data_ptr()), vp(dn["gamma"].data_ptr()), vp(h.data_ptr()),
+                                            m, dn["n"], dn["k"], vp(xq2.data_ptr()), vp(a2.data_ptr()), None,
+                                            vp(xs[layer + 1].data_ptr()), s)
+                if rc:
+                    raise RuntimeError(bl.bl_status_string(rc))
+
+        ms = _graph_time_ms(torch, chain, max(5, args.steps // 10))
+        res[f"M={m}"] = {"ms_per_token_pass": round(ms, 4), "tokens_per_s": round(m * 1000.0 / ms, 1),
+                         "weight_GBps": round(weight_bytes / (ms * 1e-3) / 1e9, 1),
+                         "frac_of_hbm_peak": round(weight_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "us_per_launch": round(1000.0 * ms / (2 * len(gus)), 3)}
+        del xs, h, xq1, xq2, a1, a2
+    del glu
+    torch.cuda.empty_cache()
+    return res
+
+
+def measure_single_rotated(args, lib, copies=320):
+    """The single 2560 x 2560 BitLinear at one token (config 1): one
+    bl_bitlinear per launch, each on its own copy of the packed matrix
+    (320 x 1.64 MB = 524 MB, twice the Infinity Cache), replayed as a graph."""
+    import numpy as np
+    import torch
+
+    import datagen
+    import ternary_weight_absmean_amd as bl
+
+    dev = torch.device("cuda", 0)
+    vp = ctypes.c_void_p
+    n = k = 2560
+    w = torch.from_numpy(datagen.weights(datagen.stream_id(datagen.WORKLOAD_SINGLE, 0, 0, datagen.TENSOR_W), n, k)).to(dev)
+    packed, gamma = bl.bl_ternarize_pack(w)
+    del w
+    bank = packed.repeat(copies)  # copies back to back
+    nb = packed.numel()
+    x = datagen.activations_bf16(datagen.stream_id(datagen.WORKLOAD_SINGLE, 0, 0, datagen.TENSOR_X), 1, k)
+    xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    xq = torch.empty((1, k), dtype=torch.int8, device=dev)
+    alpha = torch.empty(1, dtype=torch.float32, device=dev)
+    y = torch.empty((1, n), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def run():
+        s = vp(torch.cuda.current_stream().cuda_stream)
+        base = bank.data_ptr()
+        for c in range(copies):
+            rc = lib.bl_bitlinear(vp(base + c * nb), vp(gamma.data_ptr()), vp(xd.data_ptr()), 1, n, k,
+                                  vp(xq.data_ptr()), vp(alpha.data_ptr()), None, vp(y.data_ptr()), s)
+            if rc:
+                raise RuntimeError(bl.bl_status_string(rc))
+
+    ms = _graph_time_ms(torch, run, max(5, args.steps // 10))
+    us = 1000.0 * ms / copies
+    total = nb + 2 * k + k + 4 + 4 + 2 * n
+    res = {"copies": copies, "weights_MB": round(nb * copies / 1e6, 1), "us_per_launch": round(us, 3),
+           "weight_GBps": round(nb / (us * 1e-6) / 1e9, 1),
+           "frac_of_hbm_peak": round(total / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+           "algorithmic_bytes_per_launch": total}
+    del bank, packed
+    torch.cuda.empty_cache()
+    return res
+
+
+def measure_b3(args, linears, lib):
+    """Five-trits-per-byte weights (bl_ternarize_pack_b3 / bl_bitlinear_b3)
+    against the 2-bit code on the same matrices: the 2B-shaped stack at one
+    token (120 launches in a graph) and the 70B-shaped layer at one token
+    (80 distinct copies, looped)."""
+    import numpy as np
+    import torch
+
+    import datagen
+    import ternary_weight_absmean_amd as bl
+
+    dev = torch.device("cuda", 0)
+    vp = ctypes.c_void_p
+    wl = datagen.WORKLOAD_STACK_2B
+    out = {}
+
+    def run_fn(items):
+        def fn():
+            s = vp(torch.cuda.current_stream().cuda_stream)
+            for packed, gamma, x, n, k, xq, alpha, y in items:
+                rc = lib.bl_bitlinear_b3(vp(packed.data_ptr()), vp(gamma.data_ptr()), vp(x.data_ptr()), 1, n, k,
+                                         vp(xq.data_ptr()), vp(alpha.data_ptr()), None, vp(y.data_ptr()), s)
+                if rc:
+                    raise RuntimeError(bl.bl_status_string(rc))
+        return fn
+
+    items = []
+    for i, lin in enumerate(linears):
+        layer, pi = i // 4, i % 4
+        w = torch.from_numpy(datagen.weights(datagen.stream_id(wl, layer, pi, datagen.TENSOR_W), lin["n"], lin["k"])).to(dev)
+        p3, g3 = bl.bl_ternarize_pack_b3(w)
+        del w
+        items.append((p3, g3, lin["x"], lin["n"], lin["k"], lin["xq"], lin["alpha"], lin["y"]))
+    torch.cuda.synchronize()
+    b3_bytes = sum(it[0].numel() for it in items)
+    two_bit = sum(lin["packed"].numel() for lin in linears)
+    ms = _graph_time_ms(torch, run_fn(items), max(10, args.steps // 4))
+    out["decode_stack_2b_m1"] = {"ms_per_step": round(ms, 4), "tokens_per_s": round(1000.0 / ms, 1),
+                                 "weights_MB": round(b3_bytes / 1e6, 1), "weights_MB_2bit": round(two_bit / 1e6, 1),
+                                 "weight_GBps": round(b3_bytes / (ms * 1e-3) / 1e9, 1),
+                                 "us_per_launch": round(1000.0 * ms / len(items), 3)}
+    del items
+    torch.cuda.empty_cache()
+
+    wl70 = datagen.WORKLOAD_70B
+    layer = []
+    for pi, (name, k, n) in enumerate(datagen.LAYER_70B_PROJ):
+        w = torch.from_numpy(datagen.weights(datagen.stream_id(wl70, 0, pi, datagen.TENSOR_W), n, k)).to(dev)
+        p3, g3 = bl.bl_ternarize_pack_b3(w)
+        del w
+        cols = datagen.outlier_columns(wl70, k, datagen.n_outliers_70b(k))
+        x = datagen.activations_bf16(datagen.stream_id(wl70, 0, pi, datagen.TENSOR_X) + 1, 1, k, cols,
+                                     datagen.LAYER_70B_OUTLIER_MULT)
+        xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        layer.append((name, n, k, p3, g3, xd, torch.empty((1, k), dtype=torch.int8, device=dev),
+                      torch.empty(1, dtype=torch.float32, device=dev), torch.empty((1, n), dtype=torch.bfloat16, device=dev)))
+    n_layers = datagen.LAYER_70B_LAYERS
+    copies = [[p3.clone() for (_, _, _, p3, _, _, _, _, _) in layer] for _ in range(n_layers)]
+    torch.cuda.synchronize()
+    lb = sum(l[3].numel() for l in layer)
+    r70 = {"packed_bytes_per_layer": lb, "packed_bytes_per_layer_2bit": sum(
+        bl.bl_packed_bytes(n, k) for _, k, n in datagen.LAYER_70B_PROJ), "layers": n_layers}
+    allitems = [(c[i], l[4], l[5], l[1], l[2], l[6], l[7], l[8]) for c in copies for i, l in enumerate(layer)]
+    ms = _graph_time_ms(torch, run_fn(allitems), 10)
+    r70["M=1"] = {"ms_per_80_layers": round(ms, 3), "tokens_per_s": round(1000.0 / ms, 1),
+                  "weight_GBps": round(lb * n_layers / (ms * 1e-3) / 1e9, 1),
+                  "frac_of_hbm_peak": round(lb * n_layers / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                  "trits_per_ns": round(sum(n * k for _, k, n in datagen.LAYER_70B_PROJ) * n_layers / (ms * 1e6), 1)}
+    per = {}
+    for i, l in enumerate(layer):
+        sel = [it for j, it in enumerate(allitems) if j % len(layer) == i]
+        ms_p = _graph_time_ms(torch, run_fn(sel), 10)
+        per[l[0]] = {"us_per_layer": round(1000.0 * ms_p / n_layers, 2),
+                     "weight_GBps": round(l[3].numel() * n_layers / (ms_p * 1e-3) / 1e9, 1)}
+    r70["M=1"]["per_projection"] = per
+    out["layer_70b"] = r70
+    del copies, layer, allitems
+    torch.cuda.empty_cache()
     return out
 
 
@@ -955,22 +1241,41 @@ def graph_node_floor_us(torch, nodes):
 
 def stream_reference(torch):
     """Measured HBM ceilings on this machine for context: a 1 GiB device copy
-    (read + write) and a sum over 1 GiB (read), each timed over 3 runs."""
+    (read + write, torch) and a 1 GiB read by blmeasure_stream_read (the
+    library's reference kernel: non-temporal 16-byte loads, a wave's load
+    1 KiB contiguous, eight in flight per lane, as the decode kernels read
+    weights), each timed over 5 runs after one warm run."""
+    from ternary_weight_absmean_amd._build import MEASURE_LIB_PATH
+
+    mlib = ctypes.CDLL(MEASURE_LIB_PATH)
+    mlib.blmeasure_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    mlib.blmeasure_stream_read_sink_words.argtypes = [ctypes.c_size_t]
+    mlib.blmeasure_stream_read_sink_words.restype = ctypes.c_size_t
     dev = torch.device("cuda", 0)
-    src = torch.ones(1 << 27, dtype=torch.int64, device=dev)  # 1 GiB
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 8, dtype=torch.int64, device=dev)
     dst = torch.empty_like(src)
+    sink = torch.empty(mlib.blmeasure_stream_read_sink_words(nbytes), dtype=torch.int32, device=dev)
+
+    def read():
+        rc = mlib.blmeasure_stream_read(ctypes.c_void_p(src.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()),
+                                        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc:
+            raise RuntimeError(f"blmeasure_stream_read failed ({rc})")
+
     out = {}
-    for name, fn, nbytes in (("copy_GBps", lambda: dst.copy_(src), 2 << 30), ("read_GBps", lambda: src.sum(), 1 << 30)):
+    for name, fn, moved in (("copy_GBps", lambda: dst.copy_(src), 2 * nbytes), ("read_GBps", read, nbytes)):
         fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(3):
+        for _ in range(5):
             fn()
         e1.record()
         torch.cuda.synchronize()
-        out[name] = round(nbytes * 3 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
-    del src, dst
+        out[name] = round(moved * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    out["read_kernel"] = "blmeasure_stream_read (non-temporal 16-byte loads, 1 GiB)"
+    del src, dst, sink
     torch.cuda.empty_cache()
     return out
 
