@@ -61,14 +61,17 @@ extern "C" {
 #define BL_MAX_N (1 << 26)
 #define BL_MAX_BACKWARD_N (1 << 24)
 
-typedef enum {
+/* Status codes.  bl_status is a plain int, so that any value a caller
+ * passes back (bl_status_string) is well defined in C and C++ alike. */
+typedef int bl_status;
+enum {
     BL_OK = 0,
     BL_ERR_NULL = 1,      /* a required pointer is NULL                          */
     BL_ERR_SHAPE = 2,     /* m, n or k outside the supported range               */
     BL_ERR_ALIGN = 3,     /* a pointer is not aligned as required                */
     BL_ERR_WORKSPACE = 4, /* workspace smaller than bl_ternarize_pack_workspace_bytes */
     BL_ERR_HIP = 5        /* the HIP runtime rejected a launch                   */
-} bl_status;
+};
 
 /* Size in bytes of the packed ternary buffer for an [n][k] weight matrix:
  * ceil(n/16)*16 * k/4 (four trits per byte [P2]; rows padded to 16).

@@ -35,10 +35,13 @@ class BitLinearError(RuntimeError):
         self.status = status
 
 
-if not os.path.exists(LIB_PATH):
-    raise ImportError(f"libbitlinear.so is not built ({LIB_PATH}); run __graft_entry__.build()")
+# BITLINEAR_LIB may name another build of the same library (the test suite
+# loads a host-sanitizer build this way); by default the in-tree build.
+_LIB_FILE = os.environ.get("BITLINEAR_LIB") or LIB_PATH
+if not os.path.exists(_LIB_FILE):
+    raise ImportError(f"libbitlinear.so is not built ({_LIB_FILE}); run __graft_entry__.build()")
 
-_lib = ctypes.CDLL(LIB_PATH)
+_lib = ctypes.CDLL(_LIB_FILE)
 _P, _I64, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
 _lib.bl_packed_bytes.argtypes = [_I64, _I64]
 _lib.bl_packed_bytes.restype = _SZ

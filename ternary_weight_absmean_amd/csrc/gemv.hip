@@ -146,7 +146,6 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_fused(const uint4* __rest
   const bool row_ok = my_row < rows;
   const int64_t k8 = k / 8;
   const int64_t ldx = k + kLdsRowPad;
-  const uint4* xb = x + (tok0 + (row_ok ? my_row : 0)) * k8;
   const __amdgpu_buffer_rsrc_t xrsrc = buffer_rsrc(x + tok0 * k8, (uint32_t)(rows * k8 * 16));
   const bool cached = (k8 + tpr - 1) / tpr <= kXC;
   uint4 xr[kXC];
@@ -173,12 +172,28 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_fused(const uint4* __rest
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- quantize the token block into LDS
+  // Longer rows are read twice, kBatchX chunks per thread at a time (loads
+  // issued together; offsets past the row, or of rows past the block, read
+  // as zero): one dependent load per chunk measured several times slower.
+  constexpr int kBatchX = 8;
+  auto load_batch = [&](int64_t i0, uint4 (&v)[kBatchX]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kBatchX; ++u) {
+      const int64_t i = i0 + (int64_t)u * tpr;
+      v[u] = buffer_load16(xrsrc, i < k8 ? (uint32_t)((my_row * k8 + i) * 16) : kOutOfRange);
+    }
+  };
   u16x2 m2 = {0, 0};
   if (cached) {
 #pragma unroll
     for (int c = 0; c < kXC; ++c) m2 = absmax_step(m2, xr[c]);
-  } else if (row_ok) {
-    for (int64_t i = j0; i < k8; i += tpr) m2 = absmax_step(m2, xb[i]);
+  } else {
+    for (int64_t i0 = j0; i0 < k8; i0 += (int64_t)kBatchX * tpr) {
+      uint4 v[kBatchX];
+      load_batch(i0, v);
+#pragma unroll
+      for (int u = 0; u < kBatchX; ++u) m2 = absmax_step(m2, v[u]);
+    }
   }
   group_partial<true>((int)max(m2.x, m2.y), tpr, red_max);
   __syncthreads();
@@ -198,14 +213,25 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_fused(const uint4* __rest
           if (gdst) gdst[i] = q;
         }
       }
-    } else {
-      for (int64_t i = j0; i < k8; i += tpr) {
-        const uint2 q = act_codes8(xb[i], s, sum);
-        dst[i] = q;
-        if (gdst) gdst[i] = q;
-      }
     }
     if (j0 == 0 && first_block && alpha) alpha[tok0 + my_row] = amax;
+  }
+  if (!cached) {
+    uint2* dst = reinterpret_cast<uint2*>(xs + (int64_t)my_row * ldx);
+    uint2* gdst = (first_block && xq_out && row_ok) ? reinterpret_cast<uint2*>(xq_out + (tok0 + my_row) * k) : nullptr;
+    for (int64_t i0 = j0; i0 < k8; i0 += (int64_t)kBatchX * tpr) {
+      uint4 v[kBatchX];
+      load_batch(i0, v);
+#pragma unroll
+      for (int u = 0; u < kBatchX; ++u) {
+        const int64_t i = i0 + (int64_t)u * tpr;
+        if (row_ok && i < k8) {
+          const uint2 q = act_codes8(v[u], s, sum);
+          dst[i] = q;
+          if (gdst) gdst[i] = q;
+        }
+      }
+    }
   }
   group_partial<false>(sum, tpr, red_sum);
   __syncthreads();
@@ -1153,8 +1179,9 @@ bool gemv_fused_applies(int64_t m, int64_t n, int64_t k) {
   if (m1_config(m, (k / kTileCols + 3) / 4, row_tiles).kernel) return true;
   if (m > 1 && m * k > kFusedMaxTokenColumns) return false;
   // the quantizer + product launch pair is faster for more than 8 tokens
-  // (rows of 2560, 160-240 row tiles: 5.7 against 7.9 us at 10-12 tokens),
-  // and from 5 tokens on matrices of 512+ row tiles (7.5 against 8.8 us)
+  // (rows of 2560, 160-240 row tiles: 5.7 against 7.9 us at 10-12 tokens;
+  // at 16 tokens, with every workgroup quantizing the block, 9.6 against
+  // 6.7 us), and from 5 tokens on matrices of 512+ row tiles (7.5 against 8.8 us)
   if (m > 8 || (m > 4 && row_tiles >= 512)) return false;
   return fused_plan(m, 1, k).rt > 0;
 }
