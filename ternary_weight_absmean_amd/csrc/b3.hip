@@ -281,6 +281,139 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_b3(const uint4* __restric
   }
 }
 
+// The same product for matrices with many row bands: wave w of the kW owns
+// the whole row band blockIdx.x * kW + w (all its super-tiles), so the
+// stream needs no cross-wave sums and no barrier after the quantization;
+// the workgroup quantizes the token once, into one expanded copy in LDS
+// that every wave reads.  Chunk c of the row goes to thread c % (64 kW),
+// slot c / (64 kW); the token's absmax and activation sum are reduced over
+// the workgroup through LDS (two barriers, both before the stream).
+template <int kW, int kC>
+__global__ __launch_bounds__(kW * 64) void k_bitlinear_b3_band(const uint4* __restrict__ packed,
+                                                               const float* __restrict__ gamma_ptr,
+                                                               const uint4* __restrict__ x, float* __restrict__ alpha,
+                                                               int8_t* __restrict__ xq_out, int n, int k,
+                                                               int32_t* __restrict__ acc_out,
+                                                               uint16_t* __restrict__ y_out) {
+  constexpr int kT = kW * 64;
+  constexpr int kB = 4;  // super-tiles per prefetch batch
+  extern __shared__ uint4 xe_raw[];  // [super-tile][640 bytes]
+  __shared__ int red[2][kW];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tok = blockIdx.y;
+  const int bands = (n + kTileRows - 1) / kTileRows;
+  const int band = blockIdx.x * kW + wave;
+  const int supers = (k + kSuperCols - 1) / kSuperCols;
+  const int g = lane >> 4;
+  const int col = lane & 15;
+  const int k8 = k / 8;
+
+  const __amdgpu_buffer_rsrc_t xrsrc = buffer_rsrc(x + (int64_t)tok * k8, (uint32_t)(k * 2));
+  uint4 xr[kC];
+#pragma unroll
+  for (int i = 0; i < kC; ++i) {
+    const int c = (int)threadIdx.x + kT * i;
+    xr[i] = buffer_load16(xrsrc, c < k8 ? (uint32_t)c * 16u : kOutOfRange);
+  }
+  // this wave's band: one resource (a band past n reads zero bytes, whose
+  // codes 0 add nothing), super-tiles in order
+  const __amdgpu_buffer_rsrc_t wrsrc =
+      buffer_rsrc(packed + (size_t)band * supers * (kSuperBytes / 16), band < bands ? (uint32_t)supers * kSuperBytes : 0u);
+  auto w_off = [&](int st) { return (uint32_t)(st * kSuperBytes + lane * 16); };
+  uint4 a_cur[kB];
+#pragma unroll
+  for (int u = 0; u < kB; ++u) a_cur[u] = buffer_load16_stream(wrsrc, w_off(u));
+  const float gamma = buffer_load_f32(buffer_rsrc(gamma_ptr, 4), 0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  u16x2 m2 = {0, 0};
+#pragma unroll
+  for (int i = 0; i < kC; ++i) m2 = absmax_step(m2, xr[i]);
+  int v = wave_reduce<true>((int)max(m2.x, m2.y));
+  if (lane == 0) red[0][wave] = v;
+  __syncthreads();
+  int mx = red[0][0];
+#pragma unroll
+  for (int w = 1; w < kW; ++w) mx = max(mx, red[0][w]);
+  const float amax = __uint_as_float((uint32_t)mx << 16);
+  const float s = 127.0f / fmaxf(amax, 1e-5f);  // IEEE division, as in bl_quant_act
+
+  uint8_t* region = reinterpret_cast<uint8_t*>(xe_raw);
+  const bool first_block = blockIdx.x == 0;
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < kC; ++i) {
+    const int c = (int)threadIdx.x + kT * i;
+    if (c < supers * 40) {  // chunks of the padded last super-tile are zero codes
+      const uint2 q = act_codes8(xr[i], s, sum);
+      const int st = c / 40, e = c % 40;
+      uint8_t* dst = region + st * kExpBytes + (e / 2) * 32 + (e % 2) * 8;
+      const uint2 lo = make_uint2(__builtin_amdgcn_perm(q.x, 0u, 0x060c040cu), __builtin_amdgcn_perm(q.y, 0u, 0x060c040cu));
+      const uint2 hi = make_uint2(__builtin_amdgcn_perm(q.x, 0u, 0x070c050cu), __builtin_amdgcn_perm(q.y, 0u, 0x070c050cu));
+      *reinterpret_cast<uint2*>(dst) = lo;
+      *reinterpret_cast<uint2*>(dst + 16) = hi;
+      if (first_block && xq_out && c < k8) reinterpret_cast<uint2*>(xq_out + (int64_t)tok * k)[c] = q;
+    }
+  }
+  v = wave_reduce<false>(sum);
+  if (lane == 0) red[1][wave] = v;
+  if (first_block && wave == 0 && lane == 0 && alpha) alpha[tok] = amax;
+  __syncthreads();
+  int xsum = red[1][0];
+#pragma unroll
+  for (int w = 1; w < kW; ++w) xsum += red[1][w];
+
+  v4i acc0 = {0, 0, 0, 0}, acc1 = acc0;
+  for (int st = 0; st < supers; st += kB) {
+    uint4 a_nxt[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) a_nxt[u] = buffer_load16_stream(wrsrc, w_off(st + kB + u));  // past the row: zero
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int sl = min(st + u, supers - 1);  // past the row: zero codes, any operands
+      const uint8_t* xb = region + sl * kExpBytes + g * 5 * 32;
+      const uint4 a = a_cur[u];
+      uint32_t plo[4] = {even_bytes(a.x), even_bytes(a.y), even_bytes(a.z), even_bytes(a.w)};
+      uint32_t phi[4] = {odd_bytes(a.x), odd_bytes(a.y), odd_bytes(a.z), odd_bytes(a.w)};
+#pragma unroll
+      for (int d = 0; d < 5; ++d) {
+        v4i tlo, thi;
+        tlo.x = (int)(plo[0] + (plo[0] << 1));
+        tlo.y = (int)(plo[1] + (plo[1] << 1));
+        tlo.z = (int)(plo[2] + (plo[2] << 1));
+        tlo.w = (int)(plo[3] + (plo[3] << 1));
+        thi.x = (int)(phi[0] + (phi[0] << 1));
+        thi.y = (int)(phi[1] + (phi[1] << 1));
+        thi.z = (int)(phi[2] + (phi[2] << 1));
+        thi.w = (int)(phi[3] + (phi[3] << 1));
+        acc0 = mfma_16x16x64(tlo, as_v4i(*reinterpret_cast<const uint4*>(xb + d * 32)), acc0);
+        acc1 = mfma_16x16x64(thi, as_v4i(*reinterpret_cast<const uint4*>(xb + d * 32 + 16)), acc1);
+        if (d < 4) {
+          plo[0] = (uint32_t)tlo.x & 0x00FF00FFu;
+          plo[1] = (uint32_t)tlo.y & 0x00FF00FFu;
+          plo[2] = (uint32_t)tlo.z & 0x00FF00FFu;
+          plo[3] = (uint32_t)tlo.w & 0x00FF00FFu;
+          phi[0] = (uint32_t)thi.x & 0x00FF00FFu;
+          phi[1] = (uint32_t)thi.y & 0x00FF00FFu;
+          phi[2] = (uint32_t)thi.z & 0x00FF00FFu;
+          phi[3] = (uint32_t)thi.w & 0x00FF00FFu;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kB; ++u) a_cur[u] = a_nxt[u];
+  }
+  if (col != 0 || band >= bands) return;
+  add4(acc0, acc1);
+  acc0.x -= xsum;
+  acc0.y -= xsum;
+  acc0.z -= xsum;
+  acc0.w -= xsum;
+  store_tile(acc0, (int64_t)band * kTileRows + 4 * g, tok, n, (gamma * amax) / 127.0f, acc_out, y_out);
+}
+
 }  // namespace
 }  // namespace bl
 
@@ -319,6 +452,18 @@ hipError_t launch_bitlinear_b3(const uint8_t* packed, const float* gamma, const 
                                int64_t k, int8_t* xq, float* alpha, int32_t* acc, uint16_t* y, hipStream_t s) {
   if (k > kB3MaxK || m > 65535) return kErrGridTooLarge;
   const int64_t supers = (k + 319) / 320, bands = (n + kTileRows - 1) / kTileRows;
+  if (bands >= 2048 && supers <= 51) {
+    // a whole band per wave, eight waves per workgroup: on the 70B-shaped
+    // gate+up (3584 bands of 26 super-tiles) 29.4 against 33.6 us for the
+    // split-row kernel below
+    const int64_t slots = (supers * 40 + 511) / 512;
+    auto kern = slots <= 2 ? k_bitlinear_b3_band<8, 2> : k_bitlinear_b3_band<8, 4>;
+    const dim3 grid((unsigned)((bands + 7) / 8), (unsigned)m);
+    if (!grid_fits(grid.x, 512)) return kErrGridTooLarge;
+    hipLaunchKernelGGL(kern, grid, dim3(512), (size_t)supers * kExpBytes, s, reinterpret_cast<const uint4*>(packed),
+                       gamma, reinterpret_cast<const uint4*>(x), alpha, xq, (int)n, (int)k, acc, y);
+    return hipGetLastError();
+  }
   // four waves for short rows, eight (each quantizing and streaming half as
   // many super-tiles) for longer ones; two row bands per workgroup (sharing
   // the quantized token) once there are ~2-4 per CU

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace bl {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -180,6 +182,21 @@ __device__ __forceinline__ int wave_reduce(int v) {
 __device__ __forceinline__ v4i mfma_16x16x64(const v4i& a, const v4i& b, const v4i& c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>): a loop
+// whose index is a compile-time constant in every copy of the body.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
+
+// s_waitcnt immediate that waits until at most n vector memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_at_most(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
 __device__ __forceinline__ void add4(v4i& a, const v4i& b) {
   a.x += b.x;

@@ -816,21 +816,6 @@ __global__ __launch_bounds__(kW * 64) void k_gemv_lds(const uint4* __restrict__ 
 }
 
 
-// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>): a loop
-// whose index is a compile-time constant in every copy of the body.
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_seq(f, std::make_integer_sequence<int, N>{});
-}
-
-// s_waitcnt immediate that waits until at most n vector memory operations of
-// this wave are outstanding (expcnt and lgkmcnt left at their maxima).
-constexpr int vmcnt_at_most(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
-
 // Product with int8 activations given, 2 <= m <= 16 tokens, long rows: the
 // token block's activations stream through a ring of kS 1024-column LDS
 // buffers filled by DMA (buffer loads that write LDS, no registers) kS - 1

@@ -78,6 +78,9 @@ def check_bitlinear_b3(w, x):
     (1, 40, 3904), (1, 2560, 6912), (1, 48, 8192), (1, 100, 28672), (1, 24, 64000),
     # two row bands per workgroup (>= 512 bands with short rows, >= 1024 any), ragged last band
     (1, 8200, 2560), (1, 16400, 704), (1, 17000, 8192),
+    # a whole band per wave (>= 2048 bands): ragged last workgroup, partial last super-tile,
+    # up to 2 quantization slots per thread (4 slots: the 70B gate+up below), two tokens
+    (1, 32784, 704), (1, 40000, 2560), (1, 32768, 6912), (2, 32784, 320),
     # several tokens: one pass per token
     (2, 70, 2624), (5, 48, 6912), (16, 33, 320), (64, 40, 2560)])
 def test_bitlinear_b3_matches_oracle(m, n, k):
