@@ -461,6 +461,36 @@ def summarize(args):
             lines.append(f"| {k} | {100 * util:.1f}% | {n_inst:.0f} | {ops:.4g} | "
                          f"{ops / (insts.get(k, (0, dur, 0))[1] * 1e-9) / 1e12 if n_inst else 0:.1f} |")
         lines.append("")
+    if "SQ_INSTS_VALU" in counters or "SQ_WAIT_INST_ANY" in counters:
+        lines += ["## Where the waves' time goes", "",
+                  "VALU issue = SQ_INSTS_VALU x 4 cycles (a wave64 instruction on a 16-lane SIMD) / (dispatch "
+                  "duration x 2.4 GHz x 1024 SIMDs); MFMA busy as above; waiting = SQ_WAIT_INST_ANY / "
+                  "SQ_WAVE_CYCLES (share of resident wave time spent waiting on a dependency or counter); LDS "
+                  "conflict cycles per LDS instruction = SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS.", "",
+                  "| kernel | VALU issue | MFMA busy | waiting | VALU per MFMA | LDS conflict cycles per LDS instr |",
+                  "|---|---|---|---|---|---|"]
+        def avg(c, k):
+            v = counters.get(c, {}).get(k)
+            return (v[0], v[1]) if v else (None, None)
+        for k in kernels:
+            valu, dur = avg("SQ_INSTS_VALU", k)
+            mfma, _ = avg("SQ_INSTS_MFMA", k)
+            busy, dur_b = avg("SQ_VALU_MFMA_BUSY_CYCLES", k)
+            wait, _ = avg("SQ_WAIT_INST_ANY", k)
+            wave, _ = avg("SQ_WAVE_CYCLES", k)
+            lds, _ = avg("SQ_INSTS_LDS", k)
+            conf, _ = avg("SQ_LDS_BANK_CONFLICT", k)
+            dur = dur or dur_b
+            if not dur:
+                continue
+            cyc = dur * 1e-9 * CLOCK_GHZ * 1e9
+            cells = [f"{100 * valu * 4 / (cyc * CU_SIMDS):.1f}%" if valu is not None else "-",
+                     f"{100 * busy / (cyc * CU_SIMDS):.1f}%" if busy is not None else "-",
+                     f"{100 * wait / wave:.1f}%" if wait is not None and wave else "-",
+                     f"{valu / mfma:.2f}" if valu is not None and mfma else "-",
+                     f"{conf / lds:.3f}" if conf is not None and lds else "-"]
+            lines.append(f"| {k} | " + " | ".join(cells) + " |")
+        lines.append("")
     os.makedirs(args.out_dir, exist_ok=True)
     if traffic and args.workload:
         path = os.path.join(args.out_dir, "traffic.json")
