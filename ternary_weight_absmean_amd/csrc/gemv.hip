@@ -25,7 +25,10 @@
 // Kernels:
 //   k_bitlinear_m1     one token, quantization fused; each wave quantizes only
 //                      the columns it multiplies (single-token decode)
-//   k_bitlinear_fused  a few tokens (m * k small), block quantization fused
+//   k_bitlinear_tok    2..16 tokens (m * k small), one wave per token
+//                      quantizes the block, quantization fused
+//   k_bitlinear_fused  a few tokens of rows past 8192 (m * k small), or one
+//                      of rows past 28672, block quantization fused
 //   k_gemv_lds         2..64 tokens, int8 activations given, staged in LDS
 //                      (16 tokens per workgroup, or 64 on large matrices)
 //   k_gemv_ring        2..16 tokens on rows of 8192 and more, int8
@@ -312,10 +315,178 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_fused(const uint4* __rest
   }
 }
 
+// Whole BitLinear for a block of up to 16 tokens on rows of up to 8192
+// columns, in one launch of sixteen waves.  Wave r quantizes token r of the
+// block from registers (kXC 16-byte bf16 chunks per lane: the row's absmax
+// and activation sum are whole-wave reductions, no LDS round) and writes its
+// int8 codes into LDS row r.  Every weight load of the workgroup (kRT row
+// tiles x the 1 KiB groups w, w + 16, ... of wave w) is issued right after
+// the activation loads, so the HBM latency of the weights overlaps the
+// quantization.  After one barrier each wave multiplies its groups with B
+// operands read from LDS (four scaled accumulators per row tile, as in
+// k_bitlinear_fused); the sixteen partial sums of a row tile then meet in
+// LDS.  kGlu (kRT even): gate+up matrix with alternating gate/up row tiles,
+// y_out is h ([m][n / 2]).
+template <int kRT, int kXC, int kW, bool kGlu = false>
+__global__ __launch_bounds__(kW * 64) void k_bitlinear_tok(const uint4* __restrict__ packed,
+                                                         const float* __restrict__ gamma_ptr,
+                                                         const uint4* __restrict__ x, float* __restrict__ alpha,
+                                                         int8_t* __restrict__ xq_out, int m, int n, int k,
+                                                         int32_t* __restrict__ acc_out, uint16_t* __restrict__ y_out) {
+  static_assert(kW == 8 || kW == 16, "one wave per token of the block");
+  constexpr int kJ = (2 * kXC + kW - 1) / kW;  // groups per wave and row tile (ceil(k / 256) <= 2 kXC)
+  extern __shared__ uint4 xs_raw[];            // [kW][k + kLdsRowPad] codes, then [kRT][kW][64] partial sums
+  __shared__ int tok_sum[16];
+  __shared__ int tok_amax[16];
+  int8_t* xs = reinterpret_cast<int8_t*>(xs_raw);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int sub = lane >> 4;
+  const int col = lane & 15;
+  const int tile0 = (int)blockIdx.x * kRT;
+  const int row_tiles = (n + kTileRows - 1) / kTileRows;
+  const int tiles_here = min(kRT, row_tiles - tile0);
+  const int tok0 = (int)blockIdx.y * kW;
+  const int rows = min(kW, m - tok0);
+  const int kt_count = k / kTileCols;
+  const int groups = (kt_count + 3) / 4;
+  const int k8 = k / 8;
+  const int ldx = k + kLdsRowPad;
+  const bool first_block = blockIdx.x == 0;
+
+  // ---- token row `wave`: chunks lane, lane + 64, ...; reads past the row,
+  // or by a wave without a token, return zero
+  const __amdgpu_buffer_rsrc_t xrsrc =
+      buffer_rsrc(x + (int64_t)(tok0 + min(wave, rows - 1)) * k8, wave < rows ? (uint32_t)k * 2u : 0u);
+  uint4 xr[kXC];
+#pragma unroll
+  for (int i = 0; i < kXC; ++i) xr[i] = buffer_load16(xrsrc, (uint32_t)(lane + 64 * i) * 16u);
+  // ---- weights: lane (col, sub) of group g holds row col of tile 4g + sub;
+  // tiles past k, and row tiles past n, read as zero codes
+  const __amdgpu_buffer_rsrc_t wrsrc = buffer_rsrc(packed + (int64_t)tile0 * kt_count * (kTileBytes / 16),
+                                                   (uint32_t)(tiles_here * kt_count * kTileBytes));
+  uint4 a[kJ][kRT];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const int kt = 4 * (wave + kW * j) + sub;
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt)
+      a[j][rt] = buffer_load16_stream(
+          wrsrc, kt < kt_count ? (uint32_t)((rt * kt_count + kt) * kTileBytes + col * 16) : kOutOfRange);
+  }
+  const float gamma = buffer_load_f32(buffer_rsrc(gamma_ptr, 4), 0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- quantize token `wave` into LDS row `wave` (and xq, alpha once)
+  u16x2 m2 = {0, 0};
+#pragma unroll
+  for (int i = 0; i < kXC; ++i) m2 = absmax_step(m2, xr[i]);
+  const int amax_bits = wave_reduce<true>((int)max(m2.x, m2.y));
+  const float amax = __uint_as_float((uint32_t)amax_bits << 16);
+  const float s = 127.0f / fmaxf(amax, 1e-5f);  // IEEE division, as in bl_quant_act
+  int sum = 0;
+  if (wave < rows) {
+    uint2* dst = reinterpret_cast<uint2*>(xs + wave * ldx);
+    uint2* gdst = first_block && xq_out ? reinterpret_cast<uint2*>(xq_out + (int64_t)(tok0 + wave) * k) : nullptr;
+#pragma unroll
+    for (int i = 0; i < kXC; ++i) {
+      const int c = lane + 64 * i;
+      if (c < k8) {
+        const uint2 q = act_codes8(xr[i], s, sum);
+        dst[c] = q;
+        if (gdst) gdst[c] = q;
+      }
+    }
+    if (first_block && alpha && lane == 0) alpha[tok0 + wave] = amax;
+  }
+  sum = wave_reduce<false>(sum);
+  if (lane == 0) {
+    tok_sum[wave] = sum;
+    tok_amax[wave] = amax_bits;
+  }
+  __syncthreads();
+
+  // ---- products: token col's 16 bytes of field f of tile 4g + sub
+  const int8_t* xrow = xs + min(col, kW - 1) * ldx;  // B columns past the block: any row (not stored)
+  v4i acc[kRT][4];
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) acc[rt][f] = v4i{0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const int g = wave + kW * j;
+    if (g >= groups) break;  // wave-uniform
+    // tiles past k carry zero codes, so any in-bounds activation bytes will do
+    const int kt = min(4 * g + sub, kt_count - 1);
+    const uint4* xt = reinterpret_cast<const uint4*>(xrow + kt * kTileCols);
+    uint4 b[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) b[f] = xt[f];
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) {
+      acc[rt][0] = mfma_16x16x64(mask4(a[j][rt], 0x03030303u, 0), as_v4i(b[0]), acc[rt][0]);
+      acc[rt][1] = mfma_16x16x64(mask4(a[j][rt], 0x0C0C0C0Cu, 0), as_v4i(b[1]), acc[rt][1]);
+      acc[rt][2] = mfma_16x16x64(mask4(a[j][rt], 0x30303030u, 0), as_v4i(b[2]), acc[rt][2]);
+      acc[rt][3] = mfma_16x16x64(mask4(a[j][rt], 0x30303030u, 2), as_v4i(b[3]), acc[rt][3]);
+    }
+  }
+  // the waves with groups (all of them once groups >= 16) leave their partial
+  // sums where the codes were
+  const int nw = min(kW, groups);
+  __syncthreads();
+  v4i* partial = reinterpret_cast<v4i*>(xs_raw);  // [kRT][kW][64]
+  if (wave < nw) {
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) {
+      // exact: acc[1] holds 4x, acc[2] and acc[3] 16x the code sums
+      v4i part = acc[rt][0];
+      part.x += (acc[rt][1].x >> 2) + ((acc[rt][2].x + acc[rt][3].x) >> 4);
+      part.y += (acc[rt][1].y >> 2) + ((acc[rt][2].y + acc[rt][3].y) >> 4);
+      part.z += (acc[rt][1].z >> 2) + ((acc[rt][2].z + acc[rt][3].z) >> 4);
+      part.w += (acc[rt][1].w >> 2) + ((acc[rt][2].w + acc[rt][3].w) >> 4);
+      partial[(rt * kW + wave) * 64 + lane] = part;
+    }
+  }
+  __syncthreads();
+  if (col >= rows) return;
+  const int xsum = tok_sum[col];  // sum q*x = sum c*x - sum x
+  const float scale = (gamma * __uint_as_float((uint32_t)tok_amax[col] << 16)) / 127.0f;
+  auto tile_sum = [&](int rt) {
+    v4i t = partial[(rt * kW) * 64 + lane];
+    for (int w = 1; w < nw; ++w) add4(t, partial[(rt * kW + w) * 64 + lane]);
+    t.x -= xsum;
+    t.y -= xsum;
+    t.z -= xsum;
+    t.w -= xsum;
+    return t;
+  };
+  if constexpr (kGlu) {
+    static_assert(kRT % 2 == 0, "gate/up tiles come in pairs");
+#pragma unroll
+    for (int p = 0; p < kRT / 2; ++p) {
+      if (p != wave || 2 * p >= tiles_here) continue;
+      store_glu_tile(tile_sum(2 * p), tile_sum(2 * p + 1), (int64_t)(tile0 / 2 + p) * kTileRows + 4 * sub, tok0 + col,
+                     n / 2, scale, y_out);
+    }
+    return;
+  }
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    if (rt != wave || rt >= tiles_here) continue;
+    store_tile(tile_sum(rt), (int64_t)(tile0 + rt) * kTileRows + 4 * sub, tok0 + col, n, scale, acc_out, y_out);
+  }
+}
+
 constexpr int kM1MaxSlots = 7;  // 16-byte bf16 chunks per lane at 8 waves (own groups only: rows up to k = 28672)
 
-// BitLinear for one token, or a few (m <= kM = 4) with short rows,
-// quantization fused.  Wave w of the kWv (4, or 8 for long rows) multiplies
+// BitLinear for one token (kM = 1), quantization fused.  The kernel also
+// takes up to kM = 4 tokens of short rows, a form no longer launched (the
+// token-block kernel is faster there); the source keeps it because the
+// one-token instance compiles to faster code from it (measured 3.77
+// against 3.90 us per launch on the 2B-shaped stack).  Wave w of the kWv (4, or 8 for long rows) multiplies
 // the 256-column groups w, w + kWv, ... and quantizes exactly those, for every token, into its own
 // LDS region, which only it reads.  The tokens' absmaxes come from per-wave
 // maxima of the own groups exchanged through LDS (one barrier).  Slot i of
@@ -981,23 +1152,20 @@ namespace {
 // LDS of k_bitlinear_fused<kRT, kW> besides the token block
 constexpr size_t fused_static_lds(int rt, int w) { return (size_t)rt * w * 1024 + 2 * (size_t)(w * 4) * 4; }
 
-struct FusedPlan {
-  int rt = 0, waves = 0;
-};
+constexpr int kFusedWaves = 8;
 
-FusedPlan fused_plan(int64_t m, int64_t n, int64_t k) {
+// Row tiles per workgroup of k_bitlinear_fused (0: the token block does not
+// fit in LDS).  It takes the rows the other fused kernels do not hold (one
+// token of more than 28672 columns, 2-3 tokens of more than 8192), with
+// eight waves; two row tiles per workgroup once there are ~4 per CU (one
+// token) or ~2 (several).
+int fused_plan(int64_t m, int64_t n, int64_t k) {
   const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
-  // Several tokens: eight waves per workgroup (the block quantization is
-  // shared by more weight streams) except for short rows with many row
-  // tiles; two row tiles per workgroup once there are ~2 per CU.  A single
-  // token (rows too long for the single-token kernel): eight waves for long
-  // rows, two row tiles once there are ~4 per CU.
-  int w = m == 1 ? (k >= 16384 ? 8 : 4) : (row_tiles >= 512 && k <= 4096 ? 4 : 8);
   int rt = m == 1 ? (row_tiles >= 1024 ? 2 : 1) : (row_tiles >= 512 ? 2 : 1);
   const size_t dyn = gemv_lds_bytes(m, k);
-  while (rt > 1 && dyn + fused_static_lds(rt, w) > (size_t)kLdsBudget) rt /= 2;
-  if (dyn + fused_static_lds(rt, w) > (size_t)kLdsBudget) return FusedPlan{};
-  return FusedPlan{rt, w};
+  while (rt > 1 && dyn + fused_static_lds(rt, kFusedWaves) > (size_t)kLdsBudget) rt /= 2;
+  if (dyn + fused_static_lds(rt, kFusedWaves) > (size_t)kLdsBudget) return 0;
+  return rt;
 }
 
 }  // namespace
@@ -1084,175 +1252,187 @@ typedef void (*M1Kernel)(const uint4*, const float*, const uint4*, float*, int8_
 struct M1Config {
   int rt = 0;
   int waves = kWaves;
-  M1Kernel kernel = nullptr;  // none when the rows need more slots per lane than the token count allows
+  M1Kernel kernel = nullptr;  // none for several tokens, or rows needing more slots per lane than it has
 };
 
-template <int kRT>
-M1Kernel m1_pick(int64_t m, int64_t groups, int& waves) {
+template <int kRT, bool kGlu>
+M1Kernel m1_pick(int64_t groups, int& waves) {
   const int64_t slots = ((groups + kWaves - 1) / kWaves + 1) / 2;
   waves = kWaves;
-  if (m == 1) {
-    if (slots <= 2) return k_bitlinear_m1<kRT, 2, 1>;
-    if (slots <= 5) return k_bitlinear_m1<kRT, 5, 1>;
-    // long rows: eight waves, so each streams half as many groups (measured
-    // 4.9 TB/s against 4.3 with four on rows of 28672)
-    if (((groups + 7) / 8 + 1) / 2 <= kM1MaxSlots) {
-      waves = 8;
-      return k_bitlinear_m1<kRT, kM1MaxSlots, 1, false, 8>;
-    }
-  } else if (m <= 4 && slots <= 2) {
-    return k_bitlinear_m1<kRT, 2, 4>;
-  }
-  return nullptr;
-}
-
-template <int kRT>
-M1Kernel m1_pick_glu(int64_t m, int64_t groups, int& waves) {
-  const int64_t slots = ((groups + kWaves - 1) / kWaves + 1) / 2;
-  waves = kWaves;
-  if (m == 1) {
-    if (slots <= 2) return k_bitlinear_m1<kRT, 2, 1, true>;
-    if (slots <= 5) return k_bitlinear_m1<kRT, 5, 1, true>;
-    // long rows: eight waves, so each streams half as many groups (measured
-    // 4.9 TB/s against 4.3 with four on rows of 28672)
-    if (((groups + 7) / 8 + 1) / 2 <= kM1MaxSlots) {
-      waves = 8;
-      return k_bitlinear_m1<kRT, kM1MaxSlots, 1, true, 8>;
-    }
-  } else if (m <= 4 && slots <= 2) {
-    return k_bitlinear_m1<kRT, 2, 4, true>;
+  if (slots <= 2) return k_bitlinear_m1<kRT, 2, 1, kGlu>;
+  if (slots <= 5) return k_bitlinear_m1<kRT, 5, 1, kGlu>;
+  // long rows: eight waves, so each streams half as many groups (measured
+  // 4.9 TB/s against 4.3 with four on rows of 28672)
+  if (((groups + 7) / 8 + 1) / 2 <= kM1MaxSlots) {
+    waves = 8;
+    return k_bitlinear_m1<kRT, kM1MaxSlots, 1, kGlu, 8>;
   }
   return nullptr;
 }
 
 // The gated form always takes two row tiles (a gate tile and its up tile)
-// per workgroup; the token rules are those of m1_config.
-M1Config m1_config_glu(int64_t m, int64_t groups, int64_t row_tiles) {
-  if (m > 1 && (m > 4 || row_tiles >= 512)) return M1Config{};
+// per workgroup.
+M1Config m1_config_glu(int64_t m, int64_t groups) {
+  if (m != 1) return M1Config{};
   M1Config c;
   c.rt = 2;
-  c.kernel = m1_pick_glu<2>(m, groups, c.waves);
+  c.kernel = m1_pick<2, true>(groups, c.waves);
   return c;
 }
 
 M1Config m1_config(int64_t m, int64_t groups, int64_t row_tiles) {
-  // Several tokens: every workgroup quantizes all of them, which pays off
-  // for short rows (measured: rows of 2560 with 160 or 240 row tiles, and
-  // with 864 row tiles at 3-4 tokens, 7.3 -> 6.8 us; not at 2 tokens, where
-  // the block-quantizing kernel is faster, nor on 6912-column rows).
-  if (m > 1 && (m > 4 || (row_tiles >= 512 && m < 3))) return M1Config{};
+  if (m != 1) return M1Config{};
   // two row tiles per workgroup (the quantized tokens are reused) for short
   // rows once there are more than ~2 tiles per CU, for longer rows once there
   // are ~4 (measured on 8192-column rows: 5.6 TB/s against 5.1 with one)
   const int rt = (row_tiles >= 512 && groups <= 16) || row_tiles >= 1024 ? 2 : 1;
   M1Config c;
   c.rt = rt;
-  c.kernel = rt == 2 ? m1_pick<2>(m, groups, c.waves) : m1_pick<1>(m, groups, c.waves);
+  c.kernel = rt == 2 ? m1_pick<2, false>(groups, c.waves) : m1_pick<1, false>(groups, c.waves);
   return c;
 }
 
 }  // namespace
 
-// Every workgroup of k_bitlinear_fused quantizes its whole token block, so
-// it pays off while m * k is small (up to 8 tokens of 2560, 4 of 6912) and
-// the matrix has few row tiles; larger blocks go through the quantizer and
-// k_gemv_lds.  k_bitlinear_m1
-// takes one token, and up to 4 on small matrices, whenever it applies.
+// One launch per BitLinear where the quantization is cheap enough to fuse:
+// k_bitlinear_m1 for one token (rows up to 28672), k_bitlinear_tok for 2-16
+// tokens with m * k <= 65536 and rows up to 8192, k_bitlinear_fused for the
+// rest with m * k <= 32767 (one token of longer rows, 2-3 tokens of rows
+// past 8192).  Larger blocks go through the quantizer and the GEMV kernels.
+namespace {
+
+constexpr int64_t kTokMaxK = 8192;  // rows k_bitlinear_tok holds (16 tokens x k codes in LDS, k / 512 chunks per lane)
+
+// Every workgroup of k_bitlinear_tok quantizes its whole token block (about
+// 4.5 VALU operations per activation), so it pays off while m * k is small;
+// past 65536 the quantizer + product launch pair is faster (measured on the
+// 2B-shaped matrices: 16 tokens of 2560 columns 5.2 against 6.0 us, of 6912
+// columns 8.5 against 7.7 us; 32 tokens of 2560 no faster).
+bool tok_applies(int64_t m, int64_t k) { return m >= 2 && m <= 16 && k <= kTokMaxK && m * k <= 65536; }
+
+template <bool kGlu>
+hipError_t launch_tok(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t n, int64_t k,
+                      int8_t* xq, float* alpha, int32_t* acc, uint16_t* y, hipStream_t s) {
+  const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
+  // four row tiles per workgroup on matrices of 512+ (the block's
+  // quantization shared by more weights: 16 tokens on 864 row tiles of 2560
+  // columns, 6.9 against 8.2 us with two), else one (two for gate+up pairs);
+  // eight waves (one per token) for up to 8 tokens (3.7 against 4.1 us at 2)
+  const int rt = row_tiles >= 512 ? 4 : kGlu ? 2 : 1;
+  const dim3 grid((unsigned)((row_tiles + rt - 1) / rt));
+  const uint4* p = reinterpret_cast<const uint4*>(packed);
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  const int mi = (int)m, ni = (int)n, ki = (int)k;
+  const int64_t c = (k + 511) / 512;
+  auto go = [&](auto kern, int w) {
+    const size_t lds = std::max((size_t)w * (size_t)(k + kLdsRowPad), (size_t)rt * w * 1024);
+    hipLaunchKernelGGL(kern, grid, dim3(w * 64), lds, s, p, gamma, xv, alpha, xq, mi, ni, ki, acc, y);
+    return hipGetLastError();
+  };
+  auto pick = [&](auto xc) {
+    constexpr int kXC = decltype(xc)::value;
+    if (m <= 8) {
+      if (rt == 4) return go(k_bitlinear_tok<4, kXC, 8, kGlu>, 8);
+      if (rt == 2) return go(k_bitlinear_tok<2, kXC, 8, kGlu>, 8);
+      if constexpr (!kGlu) return go(k_bitlinear_tok<1, kXC, 8>, 8);
+    } else {
+      if (rt == 4) return go(k_bitlinear_tok<4, kXC, 16, kGlu>, 16);
+      if (rt == 2) return go(k_bitlinear_tok<2, kXC, 16, kGlu>, 16);
+      if constexpr (!kGlu) return go(k_bitlinear_tok<1, kXC, 16>, 16);
+    }
+    return hipErrorInvalidValue;
+  };
+#define BL_TOK_CASE(XC) \
+  if (c <= XC) return pick(std::integral_constant<int, XC>{});
+  BL_TOK_CASE(2)
+  BL_TOK_CASE(4)
+  BL_TOK_CASE(6)
+  BL_TOK_CASE(8)
+  BL_TOK_CASE(12)
+  BL_TOK_CASE(16)
+#undef BL_TOK_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
 bool gemv_fused_applies(int64_t m, int64_t n, int64_t k) {
+  if (tok_applies(m, k)) return true;
   if (m < 1 || m > 16) return false;
   const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
   if (m1_config(m, (k / kTileCols + 3) / 4, row_tiles).kernel) return true;
   if (m > 1 && m * k > kFusedMaxTokenColumns) return false;
-  // the quantizer + product launch pair is faster for more than 8 tokens
-  // (rows of 2560, 160-240 row tiles: 5.7 against 7.9 us at 10-12 tokens;
-  // at 16 tokens, with every workgroup quantizing the block, 9.6 against
-  // 6.7 us), and from 5 tokens on matrices of 512+ row tiles (7.5 against 8.8 us)
-  if (m > 8 || (m > 4 && row_tiles >= 512)) return false;
-  return fused_plan(m, 1, k).rt > 0;
+  return fused_plan(m, 1, k) > 0;
 }
 
 namespace {
 
 // Block-quantizing kernel for the gated form: two row tiles (a gate tile and
-// its up tile) per workgroup, waves as in fused_plan.
-FusedPlan fused_plan_glu(int64_t m, int64_t n, int64_t k) {
-  FusedPlan p = fused_plan(m, n, k);
-  if (p.rt == 0) return p;
-  p.rt = 2;
-  if (gemv_lds_bytes(m, k) + fused_static_lds(2, p.waves) > (size_t)kLdsBudget) return FusedPlan{};
-  return p;
+// its up tile) per workgroup, if the token block leaves room for them.
+bool fused_glu_fits(int64_t m, int64_t k) {
+  return gemv_lds_bytes(m, k) + fused_static_lds(2, kFusedWaves) <= (size_t)kLdsBudget;
 }
 
 }  // namespace
 
 bool gemv_fused_glu_applies(int64_t m, int64_t f, int64_t k) {
+  if (f >= 16 && f % 16 == 0 && tok_applies(m, k)) return true;
   if (m < 1 || m > 16 || f < 16 || f % 16 != 0) return false;
-  if (m1_config_glu(m, (k / kTileCols + 3) / 4, 2 * f / kTileRows).kernel) return true;
+  if (m1_config_glu(m, (k / kTileCols + 3) / 4).kernel) return true;
   if (m > 1 && m * k > kFusedMaxTokenColumns) return false;
-  return fused_plan_glu(m, 2 * f, k).rt == 2;
+  return fused_glu_fits(m, k);
 }
 
 hipError_t launch_gemv_fused_glu(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t f,
                                  int64_t k, int8_t* xq, float* alpha, uint16_t* h, hipStream_t s) {
   if (!gemv_fused_glu_applies(m, f, k)) return hipErrorInvalidValue;
+  if (tok_applies(m, k)) return launch_tok<true>(packed, gamma, x, m, 2 * f, k, xq, alpha, nullptr, h, s);
   const int64_t groups = (k / kTileCols + 3) / 4;
   const int64_t row_tiles = 2 * f / kTileRows;
-  const M1Config c = m1_config_glu(m, groups, row_tiles);
+  const M1Config c = m1_config_glu(m, groups);
   const uint4* p = reinterpret_cast<const uint4*>(packed);
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   if (c.kernel) {
-    const int64_t tokens = m == 1 ? 1 : 4;
-    const size_t lds = (size_t)c.waves * (size_t)((groups + c.waves - 1) / c.waves) * (size_t)tokens * 256;
+    const size_t lds = (size_t)c.waves * (size_t)((groups + c.waves - 1) / c.waves) * 256;
     const dim3 grid((unsigned)(row_tiles / 2));
     hipLaunchKernelGGL(c.kernel, grid, dim3(64 * c.waves), lds, s, p, gamma, xv, alpha, xq, (int)m, (int)(2 * f),
                        (int)k, nullptr, h);
     return hipGetLastError();
   }
-  const FusedPlan fp = fused_plan_glu(m, 2 * f, k);
   const dim3 grid((unsigned)(row_tiles / 2), (unsigned)((m + 15) / 16));
   const size_t lds = gemv_lds_bytes(m, k);
   const int64_t n = 2 * f;
-  if (fp.waves == 8)
-    hipLaunchKernelGGL((k_bitlinear_fused<2, 8, true>), grid, dim3(512), lds, s, p, gamma, xv, alpha, xq, m, n, k,
-                       nullptr, h);
-  else
-    hipLaunchKernelGGL((k_bitlinear_fused<2, 4, true>), grid, dim3(256), lds, s, p, gamma, xv, alpha, xq, m, n, k,
-                       nullptr, h);
+  hipLaunchKernelGGL((k_bitlinear_fused<2, kFusedWaves, true>), grid, dim3(64 * kFusedWaves), lds, s, p, gamma, xv,
+                     alpha, xq, m, n, k, nullptr, h);
   return hipGetLastError();
 }
 
 hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t n,
                              int64_t k, int8_t* xq, float* alpha, int32_t* acc, uint16_t* y, hipStream_t s) {
-  if (m > 16 || !gemv_fused_applies(m, n, k)) return hipErrorInvalidValue;
+  if (!gemv_fused_applies(m, n, k)) return hipErrorInvalidValue;
+  if (tok_applies(m, k)) return launch_tok<false>(packed, gamma, x, m, n, k, xq, alpha, acc, y, s);
   const M1Config c = m1_config(m, (k / kTileCols + 3) / 4, (n + kTileRows - 1) / kTileRows);
   if (c.kernel) {
     const int64_t groups = (k / kTileCols + 3) / 4;
     const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
-    const int64_t tokens = m == 1 ? 1 : 4;
-    const size_t lds = (size_t)c.waves * (size_t)((groups + c.waves - 1) / c.waves) * (size_t)tokens * 256;
+    const size_t lds = (size_t)c.waves * (size_t)((groups + c.waves - 1) / c.waves) * 256;
     const dim3 grid((unsigned)((row_tiles + c.rt - 1) / c.rt));
     hipLaunchKernelGGL(c.kernel, grid, dim3(64 * c.waves), lds, s, reinterpret_cast<const uint4*>(packed), gamma,
                        reinterpret_cast<const uint4*>(x), alpha, xq, (int)m, (int)n, (int)k, acc, y);
     return hipGetLastError();
   }
-  const FusedPlan f = fused_plan(m, n, k);
+  const int rt = fused_plan(m, n, k);
   const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
-  const dim3 grid((unsigned)((row_tiles + f.rt - 1) / f.rt), (unsigned)((m + 15) / 16));
+  const dim3 grid((unsigned)((row_tiles + rt - 1) / rt), (unsigned)((m + 15) / 16));
   const uint4* p = reinterpret_cast<const uint4*>(packed);
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   const size_t lds = gemv_lds_bytes(m, k);
-  if (f.waves == 8) {
-    if (f.rt == 2)
-      hipLaunchKernelGGL((k_bitlinear_fused<2, 8>), grid, dim3(512), lds, s, p, gamma, xv, alpha, xq, m, n, k, acc, y);
-    else
-      hipLaunchKernelGGL((k_bitlinear_fused<1, 8>), grid, dim3(512), lds, s, p, gamma, xv, alpha, xq, m, n, k, acc, y);
-  } else if (f.rt == 2) {
-    hipLaunchKernelGGL((k_bitlinear_fused<2, 4>), grid, dim3(256), lds, s, p, gamma, xv, alpha, xq, m, n, k, acc, y);
-  } else if (f.rt == 1) {
-    hipLaunchKernelGGL((k_bitlinear_fused<1, 4>), grid, dim3(256), lds, s, p, gamma, xv, alpha, xq, m, n, k, acc, y);
-  } else {
-    return hipErrorInvalidValue;
-  }
+  if (rt == 2)
+    hipLaunchKernelGGL((k_bitlinear_fused<2, kFusedWaves>), grid, dim3(64 * kFusedWaves), lds, s, p, gamma, xv, alpha,
+                       xq, m, n, k, acc, y);
+  else
+    hipLaunchKernelGGL((k_bitlinear_fused<1, kFusedWaves>), grid, dim3(64 * kFusedWaves), lds, s, p, gamma, xv, alpha,
+                       xq, m, n, k, acc, y);
   return hipGetLastError();
 }
 

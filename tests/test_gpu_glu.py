@@ -53,12 +53,13 @@ def test_pack_glu_matches_oracle(f, k):
 @pytest.mark.parametrize("m,f,k", [
     # single-token kernel: short rows, long rows (up to the kernel's 28672), K tails
     (1, 16, 64), (1, 48, 320), (1, 160, 2560), (1, 1280, 6912), (1, 16, 28672), (1, 80, 2624),
-    # few-token kernel (short rows, few tiles)
-    (2, 48, 320), (3, 160, 2560), (4, 32, 4096),
-    # block-quantizing kernel (two tiles per workgroup, four and eight waves)
-    (3, 4096, 2560), (5, 48, 320), (8, 160, 2560), (16, 48, 1024),
-    # quantizer + LDS-staged product (16- and 64-token blocks; eight waves from k = 8192)
-    (9, 96, 6912), (17, 160, 640), (40, 96, 640), (64, 1040, 320), (3, 48, 6912), (5, 48, 8256),
+    # token-block kernel (gate/up tile pairs, four row tiles on 512+; eight and sixteen waves)
+    (2, 48, 320), (3, 160, 2560), (4, 32, 4096), (3, 4096, 2560), (5, 48, 320), (8, 160, 2560),
+    (16, 48, 1024), (9, 96, 6912), (3, 48, 6912),
+    # block-quantizing kernel: one token past 28672 columns, two tokens past 8192
+    (1, 16, 32832), (2, 48, 12352),
+    # quantizer + LDS-staged product (16- and 64-token blocks) and LDS-ring product (k >= 8192)
+    (17, 160, 640), (40, 96, 640), (64, 1040, 320), (5, 48, 8256),
     # 64-token workgroups (512 row tiles of the gate+up matrix, more than 32 tokens)
     (40, 4096, 320),
     # quantizer + GEMM path: past the product's token limits, ragged token blocks

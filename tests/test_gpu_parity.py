@@ -373,35 +373,27 @@ def test_linear_is_deterministic():
 # ---------------------------------------------------------------- whole layer in one call
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 33, 64), (1, 2560, 2560), (1, 2560, 6912), (1, 100, 28672),
-                                   # single-token kernel with 1 and 2 row tiles per workgroup, ragged last workgroup
-                                   (1, 8200, 320), (1, 16400, 2560), (1, 16400, 6912), (1, 17000, 7168),
-                                   # single-token kernel: partial last column group, both slot counts
-                                   (1, 40, 192), (1, 1000, 2624), (1, 9000, 4160), (1, 8200, 28672),
-                                   # single-token kernel, two row tiles per workgroup (1025 row tiles);
-                                   # its 4-token form with two row tiles (513) and with one; 16 tokens
-                                   # on 1025 row tiles: quantizer + LDS-staged product, two tiles per workgroup
-                                   (1, 16400, 8192), (3, 8200, 2560), (2, 17, 320), (16, 16400, 1024),
-                                   # block-quantizing kernel with two row tiles and four waves (2 tokens on
-                                   # 513 row tiles, k <= 4096); its activation path that re-reads the rows
-                                   # instead of holding them in registers: 1 token on rows too long for
-                                   # the single-token kernel, 3 tokens of 10240 and 5 of 5120 columns
-                                   (2, 8200, 2560), (1, 40, 32832), (3, 48, 10240), (5, 48, 5120),
-                                   # several tokens: quantizer + product with shared activation loads
-                                   (8, 16400, 2560), (16, 32800, 320), (5, 2000, 6912),
-                                   # block-quantizing kernel with eight waves, one and two row tiles
-                                   (4, 600, 6912), (3, 9000, 8000),
-                                   # few-token kernel (4 token slots), partial last column group; and
-                                   # shapes just past its limits
-                                   (2, 70, 2624), (4, 1000, 4096), (4, 8000, 2560), (4, 8200, 2560),
-                                   (7, 530, 2112), (6, 16400, 320), (4, 33, 10240),
-                                   # eight-wave kernels for long rows: block-quantizing (k >= 16384) and
-                                   # single-token (k > 10240) with two row tiles, ragged last workgroup and group
-                                   (1, 530, 16384), (7, 70, 16448), (16, 40, 32768), (1, 16400, 10304),
-                                   (3, 48, 2560), (4, 3840, 2560), (5, 40, 6912), (16, 64, 1024), (16, 31, 2560),
-                                   (17, 40, 2560), (64, 100, 2560), (4, 16, 28672),
-                                   # block-quantizing kernel up to 8 tokens on few row tiles; past it
-                                   (6, 240, 2560), (8, 160, 2560), (10, 240, 2560), (6, 1040, 2560)])
+@pytest.mark.parametrize("m,n,k", [
+    # single-token kernel: both slot counts and eight waves (rows up to 28672), one and two row
+    # tiles per workgroup (1025 row tiles), ragged last workgroup, partial last column group
+    (1, 33, 64), (1, 2560, 2560), (1, 2560, 6912), (1, 100, 28672), (1, 8200, 320), (1, 16400, 2560),
+    (1, 16400, 6912), (1, 17000, 7168), (1, 40, 192), (1, 1000, 2624), (1, 9000, 4160), (1, 8200, 28672),
+    (1, 16400, 8192), (1, 530, 16384), (1, 16400, 10304),
+    # block-quantizing kernel (rows the others do not hold): one token past 28672 columns, whose
+    # activations are read twice instead of held in registers; 2-3 tokens past 8192 columns
+    (1, 40, 32832), (3, 48, 10240), (2, 70, 12352),
+    # token-block kernel: eight waves (up to 8 tokens) and sixteen, one and four row tiles (512+),
+    # every chunk count per lane up to 16, ragged last workgroup and column group, m * k at its limit
+    (2, 17, 320), (3, 8200, 2560), (2, 8200, 2560), (16, 16400, 1024), (5, 48, 5120), (8, 16400, 2560),
+    (16, 32800, 320), (5, 2000, 6912), (4, 600, 6912), (3, 9000, 8000), (2, 70, 2624), (4, 1000, 4096),
+    (4, 8000, 2560), (4, 8200, 2560), (7, 530, 2112), (6, 16400, 320), (3, 48, 2560), (4, 3840, 2560),
+    (5, 40, 6912), (16, 64, 1024), (16, 31, 2560), (6, 240, 2560), (8, 160, 2560), (10, 240, 2560),
+    (6, 1040, 2560), (2, 8200, 8192), (9, 100, 7232), (16, 8200, 4096), (16, 40, 4096), (12, 530, 5440),
+    (5, 33, 64), (3, 20, 1088),
+    # past its limits: quantizer + LDS-staged product (m * k > 65536, or more than 16 tokens) and
+    # quantizer + LDS-ring product (rows of 8192 and more)
+    (16, 200, 4160), (17, 40, 2560), (64, 100, 2560), (4, 33, 10240), (7, 70, 16448), (16, 40, 32768),
+    (4, 16, 28672)])
 def test_bitlinear_matches_oracle(m, n, k):
     """bl_bitlinear (fused quantize + product where it fits, two kernels
     otherwise) against the oracle's quantizer, product and rescale."""
