@@ -148,10 +148,10 @@ bl_status bl_linear(const uint8_t* packed, const float* gamma, const int8_t* xq,
 /* The whole layer in one call [P1, P2, P3]: per-token absmax int8
  * quantization of x followed by the ternary product and rescale, with exactly
  * the results of bl_quant_act followed by bl_linear.  For one token, and for
- * up to 8 tokens with short rows (m * k below 32768), a single kernel does
- * both steps (each workgroup quantizes the tokens it multiplies); otherwise
- * the two kernels run back to back on `stream`.  Results do not depend on
- * the choice.
+ * up to 16 tokens while m * k is at most 65536 (rows up to 8192; 32767
+ * beyond), a single kernel does both steps (each workgroup quantizes the
+ * tokens it multiplies); otherwise the two kernels run back to back on
+ * `stream`.  Results do not depend on the choice.
  *   x      [m][k] bf16 (raw 16-bit patterns), read only.
  *   xq     out [m][k] int8 (the quantized activations; also used as staging).
  *   alpha  out [m] fp32 (per-token absmax).
@@ -241,8 +241,8 @@ bl_status bl_linear_glu(const uint8_t* packed, const float* gamma, const int8_t*
 
 /* The gated front half in one call: per-token quantization of x (xq and
  * alpha written exactly as bl_quant_act would) and the gated product, with
- * exactly the results of bl_quant_act followed by bl_linear_glu.  One token
- * (and up to 4 with short rows) takes a single kernel.
+ * exactly the results of bl_quant_act followed by bl_linear_glu.  The token
+ * counts that bl_bitlinear serves with a single kernel take one here too.
  *   x      [m][k] bf16; xq out [m][k] int8; alpha out [m] fp32;
  *   h      out [m][f] bf16 bit patterns.
  * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_HIP. */
