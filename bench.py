@@ -298,6 +298,7 @@ STACK_WORKLOAD = "bitnet-b1.58-2B-shaped decode stack, M=1"
 STACK_KERNEL = "k_bitlinear_m1"
 # kernel base name -> source file whose hash marks the stored counter figures as current
 KERNEL_SOURCES = {"k_bitlinear_m1": "gemv.hip", "k_bitlinear_fused": "gemv.hip", "k_gemv_direct": "gemv.hip",
+                  "k_bitlinear_tok": "gemv.hip", "k_bitlinear_b3": "b3.hip", "k_bitlinear_b3_band": "b3.hip",
                   "k_gemv_lds": "gemv.hip", "k_gemv_ring": "gemv.hip", "k_gemm": "gemm.hip", "k_quant_act": "quant.hip",
                   "k_bwd_x": "backward.hip", "k_bwd_w": "backward.hip", "k_bwd_w_prep": "backward.hip"}
 # operations per MFMA instruction: int8 16 x 16 x 64 (the forward kernels),
@@ -723,7 +724,53 @@ def _profile_training_2b(args):
     return 0
 
 
+def _profile_b3(args):
+    """Five-trits-per-byte weights at one token: the 70B-shaped layer's gate+up
+    and down (two copies each, 2 x 143 MB for gate+up), then the first 16
+    layers of the 2B-shaped stack; bl_bitlinear_b3, --reps passes each."""
+    import numpy as np
+    import torch
+    import datagen
+    import ternary_weight_absmean_amd as bl
+
+    dev = torch.device("cuda", 0)
+    wl = datagen.WORKLOAD_70B
+    for pi, (name, k, n) in enumerate(datagen.LAYER_70B_PROJ):
+        w = torch.from_numpy(datagen.weights(datagen.stream_id(wl, 0, pi, datagen.TENSOR_W), n, k)).to(dev)
+        p3, g3 = bl.bl_ternarize_pack_b3(w)
+        del w
+        copies = [p3, p3.clone()]
+        cols = datagen.outlier_columns(wl, k, datagen.n_outliers_70b(k))
+        x = datagen.activations_bf16(datagen.stream_id(wl, 0, pi, datagen.TENSOR_X) + 1, 1, k, cols,
+                                     datagen.LAYER_70B_OUTLIER_MULT)
+        xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        for r in range(args.reps):
+            bl.bl_bitlinear_b3(copies[r % 2], g3, xd, n, acc=False)
+        torch.cuda.synchronize()
+        print(f"[profile] b3 70b {name} K={k} N={n} x{args.reps}", flush=True)
+        del copies, p3
+    wl = datagen.WORKLOAD_STACK_2B
+    linears = []
+    for layer in range(16):
+        for pi, (name, k, n) in enumerate(datagen.STACK_2B_PROJ):
+            w = torch.from_numpy(datagen.weights(datagen.stream_id(wl, layer, pi, datagen.TENSOR_W), n, k)).to(dev)
+            p3, g3 = bl.bl_ternarize_pack_b3(w)
+            del w
+            cols = datagen.outlier_columns(wl, k, datagen.STACK_2B_OUTLIERS)
+            x = datagen.activations_bf16(datagen.stream_id(wl, layer, pi, datagen.TENSOR_X), 1, k, cols,
+                                         datagen.STACK_2B_OUTLIER_MULT)
+            linears.append((p3, g3, torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16), n))
+    torch.cuda.synchronize()
+    for r in range(args.reps):
+        for p3, g3, xd, n in linears:
+            bl.bl_bitlinear_b3(p3, g3, xd, n, acc=False)
+        torch.cuda.synchronize()
+        print(f"[profile] b3 2B stack pass {r + 1}/{args.reps}", flush=True)
+    return 0
+
+
 PROFILE_CASES = {
+    "decode_b3": _profile_b3,
     "stack_2b_m1": _profile_stack_2b_m1,
     "prefill_2b": _profile_prefill_2b,
     "training_2b": _profile_training_2b,
