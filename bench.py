@@ -1352,6 +1352,23 @@ def stream_reference(torch):
         torch.cuda.synchronize()
         out[name] = round(moved * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
     out["read_kernel"] = "blmeasure_stream_read (non-temporal 16-byte loads, 1 GiB)"
+    # the same read at the sizes of the 70B-shaped layer's packed matrices
+    # (down 58.7 MB, gate+up 117.4 MB): consecutive windows of the 1 GiB
+    # buffer, one launch each, in a graph (every pass touches the whole GiB,
+    # past the Infinity Cache)
+    sink_ptr = ctypes.c_void_p(sink.data_ptr())
+    for label, size in (("read_GBps_58.7MB", 58720256), ("read_GBps_117.4MB", 117440512)):
+        wins = nbytes // size
+
+        def windows(size=size, wins=wins):
+            s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            for w in range(wins):
+                rc = mlib.blmeasure_stream_read(ctypes.c_void_p(src.data_ptr() + w * size), size, sink_ptr, s)
+                if rc:
+                    raise RuntimeError(f"blmeasure_stream_read failed ({rc})")
+
+        ms = _graph_time_ms(torch, windows, 5)
+        out[label] = round(size * wins / (ms * 1e-3) / 1e9, 1)
     del src, dst, sink
     torch.cuda.empty_cache()
     return out
