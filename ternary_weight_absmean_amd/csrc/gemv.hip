@@ -1197,10 +1197,13 @@ hipError_t launch_gemv_impl(const uint8_t* packed, const float* gamma, const int
   }
   if (m >= 2) {
     // one workgroup per 16-token block; two row tiles per workgroup once
-    // there are ~2 per CU; rows of 8192 and
-    // more stream through the LDS ring (measured 10-25% faster on 70B-shaped
+    // there are ~2 per CU, or once one tile per workgroup would make 256
+    // workgroups or more (2B-shaped rows at 17-64 tokens: 9.8 -> 7.7 us for
+    // 64 tokens on 240 row tiles, 9.2 -> 8.7 for 17 on 160; a single block
+    // of 160 row tiles measured slower with two); rows of 8192 and more
+    // stream through the LDS ring (measured 10-25% faster on 70B-shaped
     // matrices at 4-16 tokens; no gain on 2560- and 6912-column rows)
-    const int rt = kGlu || row_tiles >= 512 ? 2 : 1;
+    const int rt = kGlu || row_tiles >= 512 || (k < kRingMinK && row_tiles * ((m + 15) / 16) >= 256) ? 2 : 1;
     const dim3 grid((unsigned)((row_tiles + rt - 1) / rt), (unsigned)((m + 15) / 16));
     if (k >= kRingMinK) {
       // four row tiles (sixteen waves) per workgroup once there are ~8 per CU:
