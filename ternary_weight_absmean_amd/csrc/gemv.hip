@@ -1190,9 +1190,11 @@ hipError_t launch_gemv_impl(const uint8_t* packed, const float* gamma, const int
     // up to 64 tokens per workgroup: the unpacked weights serve 4 token blocks
     // (pays on matrices of many row tiles; elsewhere the token blocks go to
     // separate workgroups below, whose activation bytes per CU are 4x fewer:
-    // measured 17.4 -> 12.1 us for 64 tokens on a 2560 x 6912 matrix)
-    const dim3 grid((unsigned)((row_tiles + 1) / 2), (unsigned)((m + 63) / 64));
-    hipLaunchKernelGGL((k_gemv_lds<2, 4, 1, 4, kGlu>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
+    // measured 17.4 -> 12.1 us for 64 tokens on a 2560 x 6912 matrix); four
+    // row tiles per workgroup (2B-shaped gate+up, 64 tokens: 12.1 against
+    // 13.6 us with two)
+    const dim3 grid((unsigned)((row_tiles + 3) / 4), (unsigned)((m + 63) / 64));
+    hipLaunchKernelGGL((k_gemv_lds<4, 4, 1, 4, kGlu>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
     return hipGetLastError();
   }
   if (m >= 2) {

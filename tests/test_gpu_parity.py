@@ -240,8 +240,10 @@ def test_linear_brute_force_shapes(m, n, k):
 
 
 @pytest.mark.parametrize("m,n,k", [(16, 16400, 1024), (5, 32800, 320), (9, 16416, 2112),
-                                   # 17..64 tokens in one workgroup (four token blocks), ragged chunk
-                                   (40, 1000, 4160), (64, 8200, 320),
+                                   # 17..64 tokens in one workgroup (four token blocks) with four row
+                                   # tiles, ragged last workgroup and chunk; 16-token workgroups with
+                                   # one row tile, and with two once that would make 256 workgroups
+                                   (64, 8200, 320), (40, 8208, 4160), (40, 1000, 4160), (33, 2000, 2560),
                                    # the same token counts on a matrix with many row tiles: the GEMM
                                    (20, 32784, 128),
                                    # 2..16 tokens on rows of 8192 and more: the LDS ring with 1, 2 and 4
