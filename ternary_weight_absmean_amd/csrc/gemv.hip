@@ -1186,15 +1186,22 @@ hipError_t launch_gemv_impl(const uint8_t* packed, const float* gamma, const int
   // at most one workgroup of up to 1024 threads per row tile, at most 4 token blocks
   if (!grid_fits(row_tiles, 1024) || (m + 15) / 16 > 65535) return kErrGridTooLarge;
   const uint4* p = reinterpret_cast<const uint4*>(packed);
-  if (m > 32 && row_tiles >= 512) {
-    // up to 64 tokens per workgroup: the unpacked weights serve 4 token blocks
-    // (pays on matrices of many row tiles; elsewhere the token blocks go to
-    // separate workgroups below, whose activation bytes per CU are 4x fewer:
-    // measured 17.4 -> 12.1 us for 64 tokens on a 2560 x 6912 matrix); four
-    // row tiles per workgroup (2B-shaped gate+up, 64 tokens: 12.1 against
-    // 13.6 us with two)
-    const dim3 grid((unsigned)((row_tiles + 3) / 4), (unsigned)((m + 63) / 64));
-    hipLaunchKernelGGL((k_gemv_lds<4, 4, 1, 4, kGlu>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
+  if ((m > 32 || (m > 16 && k < kRingMinK)) && row_tiles >= 512) {
+    // 32 or 64 tokens per workgroup: the unpacked weights serve 2 or 4 token
+    // blocks (pays on matrices of many row tiles; elsewhere the token blocks
+    // go to separate workgroups below, whose activation bytes per CU are
+    // fewer: measured 17.4 -> 12.1 us for 64 tokens on a 2560 x 6912
+    // matrix).  Up to 32 tokens: two row tiles per workgroup (2B-shaped
+    // gate+up at 17-32 tokens: 8.8-9.4 against 11.3-11.4 us in 16-token
+    // workgroups; rows of 8192 and more keep the LDS ring there); 64: four
+    // (12.1 against 13.6 us with two)
+    if (m <= 32) {
+      const dim3 grid((unsigned)((row_tiles + 1) / 2), (unsigned)((m + 31) / 32));
+      hipLaunchKernelGGL((k_gemv_lds<2, 4, 1, 2, kGlu>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
+    } else {
+      const dim3 grid((unsigned)((row_tiles + 3) / 4), (unsigned)((m + 63) / 64));
+      hipLaunchKernelGGL((k_gemv_lds<4, 4, 1, 4, kGlu>), grid, dim3(256), 0, s, p, gamma, xq, alpha, m, n, k, acc, y);
+    }
     return hipGetLastError();
   }
   if (m >= 2) {

@@ -244,6 +244,8 @@ def test_linear_brute_force_shapes(m, n, k):
                                    # tiles, ragged last workgroup and chunk; 16-token workgroups with
                                    # one row tile, and with two once that would make 256 workgroups
                                    (64, 8200, 320), (40, 8208, 4160), (40, 1000, 4160), (33, 2000, 2560),
+                                   # 17..32 tokens in one workgroup (two token blocks, two row tiles)
+                                   (20, 8200, 2560), (32, 8208, 1088),
                                    # the same token counts on a matrix with many row tiles: the GEMM
                                    (20, 32784, 128),
                                    # 2..16 tokens on rows of 8192 and more: the LDS ring with 1, 2 and 4
