@@ -315,18 +315,18 @@ __global__ __launch_bounds__(kW * 64) void k_bitlinear_fused(const uint4* __rest
   }
 }
 
-// Whole BitLinear for a block of up to 16 tokens on rows of up to 8192
-// columns, in one launch of sixteen waves.  Wave r quantizes token r of the
+// Whole BitLinear for a block of up to kW (8 or 16) tokens on rows of up to
+// 8192 columns, in one launch of kW waves.  Wave r quantizes token r of the
 // block from registers (kXC 16-byte bf16 chunks per lane: the row's absmax
 // and activation sum are whole-wave reductions, no LDS round) and writes its
 // int8 codes into LDS row r.  Every weight load of the workgroup (kRT row
-// tiles x the 1 KiB groups w, w + 16, ... of wave w) is issued right after
+// tiles x the 1 KiB groups w, w + kW, ... of wave w) is issued right after
 // the activation loads, so the HBM latency of the weights overlaps the
 // quantization.  After one barrier each wave multiplies its groups with B
 // operands read from LDS (four scaled accumulators per row tile, as in
-// k_bitlinear_fused); the sixteen partial sums of a row tile then meet in
-// LDS.  kGlu (kRT even): gate+up matrix with alternating gate/up row tiles,
-// y_out is h ([m][n / 2]).
+// k_bitlinear_fused); the waves' partial sums of a row tile then meet in
+// LDS.  Waves past the block's tokens only multiply.  kGlu (kRT even):
+// gate+up matrix with alternating gate/up row tiles, y_out is h ([m][n / 2]).
 template <int kRT, int kXC, int kW, bool kGlu = false>
 __global__ __launch_bounds__(kW * 64) void k_bitlinear_tok(const uint4* __restrict__ packed,
                                                          const float* __restrict__ gamma_ptr,
