@@ -1308,29 +1308,44 @@ M1Config m1_config(int64_t m, int64_t groups, int64_t row_tiles) {
 
 // One launch per BitLinear where the quantization is cheap enough to fuse:
 // k_bitlinear_m1 for one token (rows up to 28672), k_bitlinear_tok for 2-16
-// tokens with m * k <= 65536 and rows up to 8192, k_bitlinear_fused for the
-// rest with m * k <= 32767 (one token of longer rows, 2-3 tokens of rows
-// past 8192).  Larger blocks go through the quantizer and the GEMV kernels.
+// tokens with m * k <= 65536, rows up to 8192 and few workgroups (below),
+// k_bitlinear_fused for the rest with m * k <= 32767 (one token of longer
+// rows, 2-3 tokens of longer rows or of many row tiles).  Larger blocks go
+// through the quantizer and the GEMV kernels.
 namespace {
 
 constexpr int64_t kTokMaxK = 8192;  // rows k_bitlinear_tok holds (16 tokens x k codes in LDS, k / 512 chunks per lane)
 
-// Every workgroup of k_bitlinear_tok quantizes its whole token block (about
-// 4.5 VALU operations per activation), so it pays off while m * k is small;
-// past 65536 the quantizer + product launch pair is faster (measured on the
-// 2B-shaped matrices: 16 tokens of 2560 columns 5.2 against 6.0 us, of 6912
-// columns 8.5 against 7.7 us; 32 tokens of 2560 no faster).
-bool tok_applies(int64_t m, int64_t k) { return m >= 2 && m <= 16 && k <= kTokMaxK && m * k <= 65536; }
+// Row tiles per workgroup of k_bitlinear_tok: four on matrices of 512+ (the
+// block's quantization shared by more weights: 16 tokens on 864 row tiles of
+// 2560 columns, 6.9 against 8.2 us with two), else one (two for gate+up pairs).
+int tok_row_tiles(int64_t row_tiles, bool glu) { return row_tiles >= 512 ? 4 : glu ? 2 : 1; }
+
+// Every workgroup of k_bitlinear_tok (and of k_bitlinear_fused) quantizes its
+// whole token block (about 4.5 VALU operations per activation), so one launch
+// pays off while that repeated work is small: m * k up to 65536 (2B-shaped
+// matrices: 16 tokens of 2560 columns 5.2 against 6.0 us for the quantizer +
+// product pair, of 6912 columns 8.5 against 7.7 us; 32 tokens of 2560 no
+// faster), and a bound on the activations quantized over all workgroups:
+// 2^24, or 2^23 for rows of 8192 and more, whose quantizer + LDS-ring pair is
+// faster (70B-shaped gate+up, 8192-column rows: 26.5 against 30.2 us at 2
+// tokens, 26.3 against 29.8 at 4, 26.8 against 36.7 at 8; the block-quantizing
+// kernel at 3 tokens 31.4 against 26.0).
+int64_t max_repeated_quantization(int64_t k) { return k >= kRingMinK ? (int64_t)1 << 23 : (int64_t)1 << 24; }
+
+bool tok_applies(int64_t m, int64_t n, int64_t k, bool glu) {
+  if (m < 2 || m > 16 || k > kTokMaxK || m * k > 65536) return false;
+  const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
+  const int rt = tok_row_tiles(row_tiles, glu);
+  return (row_tiles + rt - 1) / rt * m * k <= max_repeated_quantization(k);
+}
 
 template <bool kGlu>
 hipError_t launch_tok(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t n, int64_t k,
                       int8_t* xq, float* alpha, int32_t* acc, uint16_t* y, hipStream_t s) {
   const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
-  // four row tiles per workgroup on matrices of 512+ (the block's
-  // quantization shared by more weights: 16 tokens on 864 row tiles of 2560
-  // columns, 6.9 against 8.2 us with two), else one (two for gate+up pairs);
   // eight waves (one per token) for up to 8 tokens (3.7 against 4.1 us at 2)
-  const int rt = row_tiles >= 512 ? 4 : kGlu ? 2 : 1;
+  const int rt = tok_row_tiles(row_tiles, kGlu);
   const dim3 grid((unsigned)((row_tiles + rt - 1) / rt));
   const uint4* p = reinterpret_cast<const uint4*>(packed);
   const uint4* xv = reinterpret_cast<const uint4*>(x);
@@ -1369,12 +1384,15 @@ hipError_t launch_tok(const uint8_t* packed, const float* gamma, const uint16_t*
 }  // namespace
 
 bool gemv_fused_applies(int64_t m, int64_t n, int64_t k) {
-  if (tok_applies(m, k)) return true;
+  if (tok_applies(m, n, k, false)) return true;
   if (m < 1 || m > 16) return false;
   const int64_t row_tiles = (n + kTileRows - 1) / kTileRows;
   if (m1_config(m, (k / kTileCols + 3) / 4, row_tiles).kernel) return true;
   if (m > 1 && m * k > kFusedMaxTokenColumns) return false;
-  return fused_plan(m, 1, k) > 0;
+  const int rt = fused_plan(m, n, k);
+  // several tokens: the same bound on repeated quantization as k_bitlinear_tok
+  if (m > 1 && rt > 0 && (row_tiles + rt - 1) / rt * m * k > max_repeated_quantization(k)) return false;
+  return rt > 0;
 }
 
 namespace {
@@ -1388,17 +1406,18 @@ bool fused_glu_fits(int64_t m, int64_t k) {
 }  // namespace
 
 bool gemv_fused_glu_applies(int64_t m, int64_t f, int64_t k) {
-  if (f >= 16 && f % 16 == 0 && tok_applies(m, k)) return true;
+  if (f >= 16 && f % 16 == 0 && tok_applies(m, 2 * f, k, true)) return true;
   if (m < 1 || m > 16 || f < 16 || f % 16 != 0) return false;
   if (m1_config_glu(m, (k / kTileCols + 3) / 4).kernel) return true;
   if (m > 1 && m * k > kFusedMaxTokenColumns) return false;
+  if (m > 1 && f / kTileRows * m * k > max_repeated_quantization(k)) return false;  // two row tiles per workgroup
   return fused_glu_fits(m, k);
 }
 
 hipError_t launch_gemv_fused_glu(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t f,
                                  int64_t k, int8_t* xq, float* alpha, uint16_t* h, hipStream_t s) {
   if (!gemv_fused_glu_applies(m, f, k)) return hipErrorInvalidValue;
-  if (tok_applies(m, k)) return launch_tok<true>(packed, gamma, x, m, 2 * f, k, xq, alpha, nullptr, h, s);
+  if (tok_applies(m, 2 * f, k, true)) return launch_tok<true>(packed, gamma, x, m, 2 * f, k, xq, alpha, nullptr, h, s);
   const int64_t groups = (k / kTileCols + 3) / 4;
   const int64_t row_tiles = 2 * f / kTileRows;
   const M1Config c = m1_config_glu(m, groups);
@@ -1422,7 +1441,7 @@ hipError_t launch_gemv_fused_glu(const uint8_t* packed, const float* gamma, cons
 hipError_t launch_gemv_fused(const uint8_t* packed, const float* gamma, const uint16_t* x, int64_t m, int64_t n,
                              int64_t k, int8_t* xq, float* alpha, int32_t* acc, uint16_t* y, hipStream_t s) {
   if (!gemv_fused_applies(m, n, k)) return hipErrorInvalidValue;
-  if (tok_applies(m, k)) return launch_tok<false>(packed, gamma, x, m, n, k, xq, alpha, acc, y, s);
+  if (tok_applies(m, n, k, false)) return launch_tok<false>(packed, gamma, x, m, n, k, xq, alpha, acc, y, s);
   const M1Config c = m1_config(m, (k / kTileCols + 3) / 4, (n + kTileRows - 1) / kTileRows);
   if (c.kernel) {
     const int64_t groups = (k / kTileCols + 3) / 4;

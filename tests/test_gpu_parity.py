@@ -386,6 +386,9 @@ def test_linear_is_deterministic():
     # block-quantizing kernel (rows the others do not hold): one token past 28672 columns, whose
     # activations are read twice instead of held in registers; 2-3 tokens past 8192 columns
     (1, 40, 32832), (3, 48, 10240), (2, 70, 12352),
+    # 3 tokens of 8192 columns on a matrix where both fused kernels would repeat too much
+    # quantization: quantizer + LDS-ring product
+    (3, 43712, 8192),
     # token-block kernel: eight waves (up to 8 tokens) and sixteen, one and four row tiles (512+),
     # every chunk count per lane up to 16, ragged last workgroup and column group, m * k at its limit
     (2, 17, 320), (3, 8200, 2560), (2, 8200, 2560), (16, 16400, 1024), (5, 48, 5120), (8, 16400, 2560),
