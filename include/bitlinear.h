@@ -149,9 +149,10 @@ bl_status bl_linear(const uint8_t* packed, const float* gamma, const int8_t* xq,
  * quantization of x followed by the ternary product and rescale, with exactly
  * the results of bl_quant_act followed by bl_linear.  For one token, and for
  * up to 16 tokens while m * k is at most 65536 (rows up to 8192; 32767
- * beyond), a single kernel does both steps (each workgroup quantizes the
- * tokens it multiplies); otherwise the two kernels run back to back on
- * `stream`.  Results do not depend on the choice.
+ * beyond) and the activations quantized over all workgroups stay below 2^24
+ * (2^23 for rows of 8192 and more), a single kernel does both steps (each
+ * workgroup quantizes the tokens it multiplies); otherwise the two kernels
+ * run back to back on `stream`.  Results do not depend on the choice.
  *   x      [m][k] bf16 (raw 16-bit patterns), read only.
  *   xq     out [m][k] int8 (the quantized activations; also used as staging).
  *   alpha  out [m] fp32 (per-token absmax).
