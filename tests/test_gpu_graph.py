@@ -25,18 +25,20 @@ def test_graph_replays_match_eager():
     w = f32((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
     w_glu = f32((rng.standard_normal((2 * f, k)) * 0.02).astype(np.float32))
     cols = rng.choice(k, size=8, replace=False)
-    x = {m: bf16(datagen.activations_bf16(int(rng.integers(1 << 40)), m, k, cols, 20.0)) for m in (1, 16, 300)}
+    x = {m: bf16(datagen.activations_bf16(int(rng.integers(1 << 40)), m, k, cols, 20.0)) for m in (1, 4, 16, 300)}
     dy = bf16(datagen.f32_to_bf16((rng.standard_normal((300, n)) * 0.01).astype(np.float32)))
 
     def run(outs):
-        """Packer, the single-token / ring / GEMM products, the gated product and
-        both gradients, writing into the tensors of `outs`."""
+        """Packer, the single-token / token-block / ring / GEMM products, the gated
+        product (token-block and ring) and both gradients, writing into the
+        tensors of `outs`."""
         bl.bl_ternarize_pack(w, packed=outs["packed"], gamma=outs["gamma"], workspace=outs["ws"])
-        for m in (1, 16, 300):
+        for m in (1, 4, 16, 300):
             bl.bl_bitlinear(outs["packed"], outs["gamma"], x[m], n, xq=outs[f"xq{m}"], alpha=outs[f"a{m}"],
                             acc=outs[f"acc{m}"], y=outs[f"y{m}"])
         bl.bl_ternarize_pack_glu(w_glu, packed=outs["pglu"], gamma=outs["gglu"], workspace=outs["ws"])
         bl.bl_bitlinear_glu(outs["pglu"], outs["gglu"], x[16], f, xq=outs["xqg"], alpha=outs["ag"], h=outs["h"])
+        bl.bl_bitlinear_glu(outs["pglu"], outs["gglu"], x[4], f, xq=outs["xqg4"], alpha=outs["ag4"], h=outs["h4"])
         bl.bl_pack_transposed(outs["packed"], n, k, packed_t=outs["packed_t"])
         bl.bl_bitlinear_backward_x(outs["packed_t"], outs["gamma"], dy, k, dx=outs["dx"])
         bl.bl_bitlinear_backward_w(dy, outs["xq300"], outs["a300"], dw=outs["dw"], workspace=outs["wsw"])
@@ -51,11 +53,14 @@ def test_graph_replays_match_eager():
              "xqg": torch.empty((16, k), dtype=torch.int8, device=d),
              "ag": torch.empty(16, dtype=torch.float32, device=d),
              "h": torch.empty((16, f), dtype=torch.bfloat16, device=d),
+             "xqg4": torch.empty((4, k), dtype=torch.int8, device=d),
+             "ag4": torch.empty(4, dtype=torch.float32, device=d),
+             "h4": torch.empty((4, f), dtype=torch.bfloat16, device=d),
              "packed_t": torch.empty(bl.bl_packed_bytes(k, n), dtype=torch.uint8, device=d),
              "dx": torch.empty((300, k), dtype=torch.float32, device=d),
              "dw": torch.empty((n, k), dtype=torch.float32, device=d),
              "wsw": torch.empty(bl.bl_backward_w_workspace_bytes(300, n, k), dtype=torch.uint8, device=d)}
-        for m in (1, 16, 300):
+        for m in (1, 4, 16, 300):
             o[f"xq{m}"] = torch.empty((m, k), dtype=torch.int8, device=d)
             o[f"a{m}"] = torch.empty(m, dtype=torch.float32, device=d)
             o[f"acc{m}"] = torch.empty((m, n), dtype=torch.int32, device=d)
